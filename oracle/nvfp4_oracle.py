@@ -1,0 +1,294 @@
+"""CPU oracle for the NVFP4 routed-expert MoE projection.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
+this module: only the tests, the smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code with the HIP library; both sides consume the same
+seeded arrays from `workloads`.
+
+Everything is plain numpy in float64. Dequantization is exact in float64 (an
+E2M1 value has 2 significant bits, an E4M3 value 4, an FP32 global scale 24,
+so a product has at most 30), so the dense float64 computation *is* the
+definition of the method up to summation order. Library primitives used as
+steps: numpy matrix products and numpy's float64->float32/float16 casts; torch
+only for float32->bf16 rounding of outputs.
+
+Sources (the pages, by title and section):
+  [S-NVFP4]  "Strata NVFP4" README, section "How it differs from upstream
+             Strata": NVFP4 keeps experts at 4.5 bits with calibrated scales;
+             per-expert FP32 scales are kept and applied to each projection's
+             output; W4A8 prompt path keeps 8-bit activations; a scale fold
+             that left hidden activations in FP16 subnormals caused 2-12%
+             expert error; the shared expert's fused SwiGLU quantizer.
+  [TF-906]   TensorFold pull 906 (rank-local NVFP4 slice reader): plain E4M3
+             scale bytes, input cuts preserve groups of 16, the FP32 tensor
+             scale is unchanged by slicing; row and input partitions
+             reassemble to the original bytes.
+  [FP4-L]    #2727 "tools: add opt-in FP4-Local CSF checkpoint conversion",
+             Validation list: expert tensors stack 512 experts; three-expert
+             CUDA parity on relative output error.
+Element formats are the public OCP Microscaling definitions that NVFP4 uses:
+E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit, no inf/NaN) and
+FP8 E4M3 "FN" (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no inf,
+S.1111.111 is NaN, largest finite 448).
+
+Readings where the pages are silent (each listed in the design notes):
+  * element 2j of a row sits in the low nibble of byte j, 2j+1 in the high;
+  * weights are [outputs][inputs]; the 16-groups run along the inputs;
+  * the global scale multiplies the projection output; the gate's scale is
+    applied before SiLU;
+  * SwiGLU is SiLU(gate) * up with SiLU(z) = z / (1 + exp(-z)), no clamp;
+  * router weights are used as given; duplicate ids are summed; ids outside
+    [0, E) are dropped;
+  * W4A8: per row s = fp32(absmax / 127) by an fp32 division, q = clamp(
+    rint_even(fp32(x / s)), -127, 127), s = q = 0 for an all-zero row; the
+    down projection's input h is quantized per (token, slot) row the same
+    way, from h rounded to fp32.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+GROUP = 16
+
+
+# ----------------------------------------------------------------- element codecs
+def e2m1_value(code):
+    """E2M1 code (0..15) -> value. Bit fields s.ee.m; e == 0 is subnormal (m * 0.5),
+    otherwise 2^(e-1) * (1 + m/2). Codes 0 and 8 are +0 and -0. [S-NVFP4]"""
+    c = np.asarray(code, dtype=np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m * 0.5, np.exp2(e - 1.0) * (1.0 + m / 2.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def e4m3fn_value(byte):
+    """FP8 E4M3 (FN variant) byte -> value. Bit fields s.eeee.mmm; e == 0 is
+    subnormal (m * 2^-9), otherwise 2^(e-7) * (1 + m/8); e == 15 with m == 7 is
+    NaN; there is no infinity. [TF-906] ("plain E4M3" scale bytes)"""
+    b = np.asarray(byte, dtype=np.int64)
+    s = (b >> 7) & 1
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, np.exp2(e - 7.0) * (1.0 + m / 8.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+E2M1_TABLE = e2m1_value(np.arange(16))
+E4M3_TABLE = e4m3fn_value(np.arange(256))
+
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    """Packed bytes [..., K/2] -> codes [..., K]; element 2j = low nibble of byte j."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = codes & 0x0F
+    out[..., 1::2] = codes >> 4
+    return out
+
+
+def pack_codes(nibbles: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_codes."""
+    n = np.asarray(nibbles, dtype=np.uint8)
+    if n.shape[-1] % 2:
+        raise ValueError("odd number of codes")
+    return (n[..., 0::2] & 0x0F) | ((n[..., 1::2] & 0x0F) << 4)
+
+
+# ----------------------------------------------------------------- dequantization
+def dequant(codes: np.ndarray, scales: np.ndarray, gamma: Optional[float] = None) -> np.ndarray:
+    """W[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k // 16]) [* gamma], float64, exact.
+    [S-NVFP4] 4.5-bit experts; [TF-906] groups of 16 inputs and the FP32 tensor scale."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    K = codes.shape[-1] * 2
+    if scales.shape[-1] * GROUP != K:
+        raise ValueError("scale plane does not cover K in groups of 16")
+    vals = E2M1_TABLE[unpack_codes(codes)]
+    sc = E4M3_TABLE[scales]
+    W = vals * np.repeat(sc, GROUP, axis=-1)
+    if gamma is not None:
+        W = W * float(np.float32(gamma))
+    return W
+
+
+def dequant_f32(codes, scales, gamma=None) -> np.ndarray:
+    """One round-to-nearest-even rounding of the exact product to float32."""
+    with np.errstate(invalid="ignore"):
+        return dequant(codes, scales, gamma).astype(np.float32)
+
+
+def bf16_bits(a32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (torch's conversion)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def dequant_bf16(codes, scales, gamma=None) -> np.ndarray:
+    """bf16 output: the exact product rounded to float32, then to bf16 (both
+    nearest-even). Without gamma the product is exact in bf16 and both
+    roundings are the identity."""
+    return bf16_bits(dequant_f32(codes, scales, gamma))
+
+
+def dequant_f16(codes, scales, gamma=None) -> np.ndarray:
+    with np.errstate(invalid="ignore", over="ignore"):
+        return dequant_f32(codes, scales, gamma).astype(np.float16)
+
+
+# ----------------------------------------------------------------- linear algebra
+def linear(x: np.ndarray, codes, scales, gamma) -> np.ndarray:
+    """y[t][n] = gamma * sum_k x[t][k] * W[n][k]: rows of W are outputs, the
+    global scale multiplies the output. [S-NVFP4] [TF-906]"""
+    W = dequant(codes, scales)
+    y = np.asarray(x, dtype=np.float64) @ W.T
+    return y * float(np.float32(gamma))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z / (1 + exp(-z)), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def _expert(layer, e: int):
+    s = layer.slot(e)
+    return (
+        dequant(layer.gate.codes[s], layer.gate.scales[s]), float(layer.gate.gamma[s]),
+        dequant(layer.up.codes[s], layer.up.scales[s]), float(layer.up.gamma[s]),
+        dequant(layer.down.codes[s], layer.down.scales[s]), float(layer.down.gamma[s]),
+    )
+
+
+def expert_ffn(x: np.ndarray, Wg, gg, Wu, gu, Wd, gd) -> np.ndarray:
+    """One routed expert on rows x [n][H]: y = gd * (SiLU(gg * x Wg^T) * (gu * x Wu^T)) Wd^T."""
+    g = (x @ Wg.T) * gg
+    u = (x @ Wu.T) * gu
+    h = silu(g) * u
+    return (h @ Wd.T) * gd
+
+
+def moe_pairwise(x: np.ndarray, layer, ids: np.ndarray, w: np.ndarray,
+                 rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """out[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]), one (token, slot) at a time,
+    dequantizing the expert afresh for each pair. x is float64 [T][H]."""
+    T, k = ids.shape
+    rows = range(T) if rows is None else rows
+    out = np.zeros((len(rows), layer.H), dtype=np.float64)
+    for r, t in enumerate(rows):
+        for j in range(k):
+            e = int(ids[t, j])
+            if e < 0 or e >= layer.E:
+                continue
+            y = expert_ffn(x[t:t + 1], *_expert(layer, e))[0]
+            out[r] += float(w[t, j]) * y
+    return out
+
+
+def route(ids: np.ndarray, E: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Counting sort of the pairs p = t*k + j by expert id.
+
+    Returns offsets int32 [E+1] (exclusive prefix sum of per-expert counts,
+    offsets[E] = number of valid pairs) and sorted_pairs int32 [T*k] listing
+    the valid pairs ordered by (expert, p) ascending, padded with -1."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        if 0 <= e < E:
+            counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:-1].copy()
+    sorted_pairs = np.full(flat.shape[0], -1, dtype=np.int64)
+    for p, e in enumerate(flat):
+        if 0 <= e < E:
+            sorted_pairs[cursor[e]] = p
+            cursor[e] += 1
+    return offsets.astype(np.int32), sorted_pairs.astype(np.int32)
+
+
+def moe_grouped(x: np.ndarray, layer, ids: np.ndarray, w: np.ndarray,
+                rows: Optional[Sequence[int]] = None, ffn=None) -> np.ndarray:
+    """Same result as moe_pairwise, computed expert by expert: each expert is
+    dequantized once and applied to all of its routed pairs."""
+    T, k = ids.shape
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    sel = ids[rows]
+    offsets, sp = route(sel, layer.E)
+    out = np.zeros((len(rows), layer.H), dtype=np.float64)
+    ffn = expert_ffn if ffn is None else ffn
+    for e in range(layer.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        pairs = sp[a:b]
+        r_idx = pairs // k
+        Y = ffn(x[rows[r_idx]], *_expert(layer, e))
+        for i, p in enumerate(pairs):
+            out[p // k] += float(w[rows[p // k], p % k]) * Y[i]
+    return out
+
+
+# ----------------------------------------------------------------- W4A8
+def quant_rows_i8(x32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row symmetric int8: s = fp32(absmax / 127) (float32 division),
+    q = clamp(round_half_even(fp32(x / s)), -127, 127); an all-zero row gives
+    s = 0, q = 0. [S-NVFP4] W4A8 prompt path with 8-bit activations."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    absmax = np.max(np.abs(x32), axis=-1)
+    s = (absmax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = np.rint((x32 / safe[..., None]).astype(np.float32))
+    q = np.clip(r, -127, 127)
+    q = np.where(s[..., None] > 0, q, 0).astype(np.int8)
+    return q, s
+
+
+def w4a8_expert_ffn(xq: np.ndarray, Wg, gg, Wu, gu, Wd, gd) -> np.ndarray:
+    """Expert FFN on already-dequantized int8 activations x_hat = q * s (float64);
+    h is rounded to fp32, quantized per row to int8, and the down projection
+    consumes h_hat = q_h * s_h."""
+    g = (xq @ Wg.T) * gg
+    u = (xq @ Wu.T) * gu
+    h = silu(g) * u
+    qh, sh = quant_rows_i8(h.astype(np.float32))
+    hh = qh.astype(np.float64) * sh.astype(np.float64)[:, None]
+    return (hh @ Wd.T) * gd
+
+
+def w4a8_activations(x_bf16_bits: np.ndarray) -> np.ndarray:
+    """x (bf16) -> per-row int8 quantization -> x_hat = q * s in float64."""
+    x32 = bf16_to_f64(x_bf16_bits).astype(np.float32)
+    q, s = quant_rows_i8(x32)
+    return q.astype(np.float64) * s.astype(np.float64)[:, None]
+
+
+def moe_w4a8(x_bf16_bits: np.ndarray, layer, ids, w, rows=None) -> np.ndarray:
+    """W4A8 MoE: both expert GEMMs take per-row int8 activations."""
+    xh = w4a8_activations(x_bf16_bits)
+    return moe_grouped(xh, layer, ids, w, rows=rows, ffn=w4a8_expert_ffn)
+
+
+# ----------------------------------------------------------------- comparison
+def rel_l2_rows(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row relative L2 error ||y - ref|| / ||ref|| (rows with ||ref|| = 0
+    report ||y||)."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.sqrt(np.sum((y - ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(ref ** 2, axis=-1))
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+

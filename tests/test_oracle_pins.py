@@ -1,0 +1,429 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something it does not itself compute: value
+tables of the element formats, a library decoder (torch.float8_e4m3fn), exact
+rational brute force, closed forms, hand-derived fixtures under tests/golden/
+and invariants of the method. A negative-control section plants plausible
+mistakes in copies of oracle functions and checks that a pin catches each.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from conftest import read_golden
+
+
+# ------------------------------------------------------------------ element formats
+def _e2m1_golden():
+    tab = {}
+    for ln in read_golden("e2m1_values.txt"):
+        c, v = ln.split()
+        tab[int(c)] = float(v)
+    return tab
+
+
+def test_e2m1_table_matches_golden():
+    tab = _e2m1_golden()
+    assert sorted(tab) == list(range(16))
+    got = O.e2m1_value(np.arange(16))
+    for c in range(16):
+        assert got[c] == tab[c]
+        assert math.copysign(1.0, got[c]) == math.copysign(1.0, tab[c])  # -0 for code 8
+
+
+def test_e4m3_all_bytes_match_torch_fn():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3fn_value(np.arange(256))
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def test_e4m3_spot_values_and_not_fnuz():
+    for ln in read_golden("e4m3_spot_values.txt"):
+        b, v = ln.split()
+        got = float(O.e4m3fn_value(int(b, 16)))
+        if v == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(v), (b, got, v)
+    fnuz = torch.tensor([0x38], dtype=torch.uint8).view(torch.float8_e4m3fnuz).to(torch.float64).item()
+    assert fnuz == 0.5 and float(O.e4m3fn_value(0x38)) == 1.0
+
+
+def test_pack_unpack_roundtrip_all_bytes():
+    b = np.arange(256, dtype=np.uint8)
+    n = O.unpack_codes(b[None, :])[0]
+    assert np.array_equal(n[0::2], b & 0xF) and np.array_equal(n[1::2], b >> 4)
+    assert np.array_equal(O.pack_codes(n[None, :])[0], b)
+    rng = np.random.default_rng(1)
+    nib = rng.integers(0, 16, size=(7, 96), dtype=np.uint8)
+    assert np.array_equal(O.unpack_codes(O.pack_codes(nib)), nib)
+
+
+# ------------------------------------------------------------------ hand products
+def _hand_cases():
+    for ln in read_golden("hand_products.txt"):
+        name, codes, scale, gamma, x, y = [f.strip() for f in ln.split("|")]
+        cb = np.frombuffer(bytes.fromhex(codes), dtype=np.uint8)[None, :]
+        sb = np.array([[int(scale, 16)]], dtype=np.uint8)
+        xs = np.array([float(v) for v in x.split(",")])[None, :]
+        yield name, cb, sb, float(gamma), xs, float(y)
+
+
+@pytest.mark.parametrize("case", list(_hand_cases()), ids=lambda c: c[0])
+def test_hand_products(case):
+    name, cb, sb, gamma, xs, y = case
+    assert O.linear(xs, cb, sb, gamma)[0, 0] == y
+
+
+def test_global_scale_rounding_example():
+    # code 7 (6.0) x scale 0x7E (448) x fp32(1/2688): exact product 1.0000000186264515,
+    # which rounds to 1.0f in fp32 (one rounding).
+    cb = np.array([[0x07] + [0] * 7], dtype=np.uint8)
+    sb = np.array([[0x7E]], dtype=np.uint8)
+    g = np.float32(1.0 / 2688.0)
+    w64 = O.dequant(cb, sb, g)[0, 0]
+    assert w64 == 6.0 * 448.0 * float(g)
+    assert w64 == 1.0000000186264515
+    assert O.dequant_f32(cb, sb, g)[0, 0] == np.float32(1.0)
+
+
+def test_products_exact_in_bf16_and_f16():
+    codes = np.arange(16)
+    finite = [b for b in range(256) if (b & 0x7F) != 0x7F]
+    v = O.e2m1_value(codes)[:, None] * O.e4m3fn_value(np.array(finite))[None, :]
+    v32 = v.astype(np.float32)
+    assert np.array_equal(v32.astype(np.float64), v)
+    bf = O.bf16_to_f64(O.bf16_bits(v32))
+    assert np.array_equal(bf, v)
+    assert np.array_equal(v32.astype(np.float16).astype(np.float64), v)
+
+
+# ------------------------------------------------------------------ brute force linear
+def _frac_tables():
+    e2 = {c: Fraction(v) for c, v in _e2m1_golden().items()}
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    e4 = {b: Fraction(float(t[b])) for b in range(256) if not math.isnan(t[b])}
+    return e2, e4
+
+
+def _bruteforce_linear(x, codes, scales, gamma):
+    """Exact rational y[t][n] = gamma * sum_k x[t][k] * e2m1(code) * e4m3(scale),
+    reading nibbles and groups straight from the bytes."""
+    e2, e4 = _frac_tables()
+    T, K = x.shape
+    N = codes.shape[0]
+    y = np.zeros((T, N))
+    g = Fraction(float(np.float32(gamma)))
+    for t in range(T):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                byte = int(codes[n, k // 2])
+                c = (byte >> 4) if (k % 2) else (byte & 0xF)
+                acc += Fraction(float(x[t, k])) * e2[c] * e4[int(scales[n, k // 16])]
+            y[t, n] = float(acc * g)
+    return y
+
+
+def test_linear_bruteforce_exact():
+    rng = np.random.default_rng(7)
+    T, N, K = 3, 5, 48  # N != K and three groups: a transposed operand or a wrong group index fails
+    x = rng.standard_normal((T, K)).astype(np.float32).astype(np.float64)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x18, 0x59, size=(N, K // 16), dtype=np.uint8)
+    gamma = np.float32(0.37)
+    ref = _bruteforce_linear(x, codes, scales, gamma)
+    got = O.linear(x, codes, scales, gamma)
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-14 * np.abs(ref).max())
+
+
+def test_linear_small_config_against_bruteforce():
+    x, codes, scales, gamma = W.draw_linear_case(0)
+    x = x.astype(np.float64)
+    ref = _bruteforce_linear(x[:2], codes[:6], scales[:6], gamma[0])
+    got = O.linear(x[:2], codes[:6], scales[:6], gamma[0])
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-13)
+
+
+# ------------------------------------------------------------------ SiLU closed forms
+def test_silu_closed_forms():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-16
+    assert abs(O.silu(np.array([-1.0]))[0] + 0.2689414213699951) < 1e-16
+    z = np.linspace(-30, 30, 121)
+    # z*sigma(z) - (-z)*sigma(-z) = z for every z: a sign error in the exponent breaks it
+    assert np.allclose(O.silu(z) - O.silu(-z), z, rtol=0, atol=1e-12)
+    assert O.silu(np.array([800.0]))[0] == 800.0
+    assert O.silu(np.array([-800.0]))[0] == 0.0
+
+
+# ------------------------------------------------------------------ MoE
+def _const_proj(E, N, K, code_byte, scale_byte, gammas):
+    return W.Proj(np.full((E, N, K // 2), code_byte, np.uint8),
+                  np.full((E, N, K // 16), scale_byte, np.uint8),
+                  np.asarray(gammas, np.float32))
+
+
+def test_moe_hand_closed_form():
+    """E=2, H=I=16. Expert 0: gate codes 1.0, gamma 1/16 -> g = 1 for x = ones;
+    up codes 2.0, gamma 1/4 -> u = 8; h = SiLU(1) * 8; down codes 1.0, gamma 1/32 ->
+    y_n = 16 * h / 32. Expert 1: gate codes -1.0 (byte 0xAA), gamma 1/16 -> g = -1;
+    up codes 0.5 (0x11), gamma 1 -> u = 8; down codes -2.0 (0xCC), gamma 1/64 ->
+    y_n = -2 * 16 * SiLU(-1) * 8 / 64. Slot weights 0.75 and 0.25."""
+    H = I = 16
+    gate = W.Proj(np.stack([np.full((I, H // 2), 0x22, np.uint8), np.full((I, H // 2), 0xAA, np.uint8)]),
+                  np.full((2, I, 1), 0x38, np.uint8), np.array([1 / 16, 1 / 16], np.float32))
+    up = W.Proj(np.stack([np.full((I, H // 2), 0x44, np.uint8), np.full((I, H // 2), 0x11, np.uint8)]),
+                np.full((2, I, 1), 0x38, np.uint8), np.array([1 / 4, 1.0], np.float32))
+    down = W.Proj(np.stack([np.full((H, I // 2), 0x22, np.uint8), np.full((H, I // 2), 0xCC, np.uint8)]),
+                  np.full((2, H, 1), 0x38, np.uint8), np.array([1 / 32, 1 / 64], np.float32))
+    lay = W.Layer(gate, up, down, E=2, H=H, I=I)
+    x = np.ones((1, H))
+    ids = np.array([[0, 1]], np.int32)
+    w = np.array([[0.75, 0.25]], np.float32)
+    s1 = 1.0 / (1.0 + math.exp(-1.0))
+    sm1 = -1.0 / (1.0 + math.exp(1.0))
+    y0 = 16 * (s1 * 8) / 32
+    y1 = -2 * 16 * (sm1 * 8) / 64
+    expect = 0.75 * y0 + 0.25 * y1
+    for fn in (O.moe_pairwise, O.moe_grouped):
+        out = fn(x, lay, ids, w)
+        assert out.shape == (1, H)
+        assert np.allclose(out, expect, rtol=1e-15, atol=0)
+
+
+def _small_layer(seed=3, E=6, H=32, I=48):
+    return W.draw_layer(seed, E=E, H=H, I=I)
+
+
+def _compose_ffn(x, lay, e):
+    """FFN built from the separately pinned pieces (linear, silu)."""
+    g = O.linear(x, lay.gate.codes[e], lay.gate.scales[e], lay.gate.gamma[e])
+    u = O.linear(x, lay.up.codes[e], lay.up.scales[e], lay.up.gamma[e])
+    h = O.silu(g) * u
+    return O.linear(h, lay.down.codes[e], lay.down.scales[e], lay.down.gamma[e])
+
+
+def test_moe_single_expert_reduces_to_ffn():
+    lay = _small_layer()
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, lay.H))
+    for e in range(lay.E):
+        ids = np.full((5, 1), e, np.int32)
+        w = np.ones((5, 1), np.float32)
+        ref = _compose_ffn(x, lay, e)
+        assert np.allclose(O.moe_pairwise(x, lay, ids, w), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_pairwise_matches_grouped_and_invariants():
+    lay = _small_layer()
+    rng = np.random.default_rng(5)
+    T, k = 9, 4
+    x = rng.standard_normal((T, lay.H))
+    ids = rng.integers(0, lay.E, size=(T, k)).astype(np.int32)
+    ids[2, 1] = ids[2, 0]          # duplicate expert within a token
+    ids[4, 3] = -1                 # dropped
+    ids[6, 0] = lay.E + 3          # dropped
+    w = rng.random((T, k)).astype(np.float32)
+    a = O.moe_pairwise(x, lay, ids, w)
+    b = O.moe_grouped(x, lay, ids, w)
+    scale = np.abs(a).max()
+    assert np.abs(a - b).max() <= 1e-12 * scale
+    # slot permutation invariance
+    perm = rng.permutation(k)
+    c = O.moe_grouped(x, lay, ids[:, perm], w[:, perm])
+    assert np.abs(a - c).max() <= 1e-12 * scale
+    # linear in the router weights
+    d = O.moe_grouped(x, lay, ids, (2 * w).astype(np.float32))
+    assert np.abs(d - 2 * a).max() <= 1e-12 * scale
+    # zero weights give zero
+    assert not np.any(O.moe_grouped(x, lay, ids, np.zeros_like(w)))
+    # dropped ids equal a zero weight on a valid id
+    ids2, w2 = ids.copy(), w.copy()
+    ids2[4, 3], w2[4, 3] = 0, 0.0
+    ids2[6, 0], w2[6, 0] = 0, 0.0
+    assert np.abs(O.moe_grouped(x, lay, ids2, w2) - a).max() <= 1e-12 * scale
+    # duplicate ids sum: merging the two slots' weights into one gives the same
+    ids3, w3 = ids.copy(), w.copy()
+    w3[2, 0] = np.float32(w[2, 0] + w[2, 1])
+    ids3[2, 1], w3[2, 1] = 0, 0.0
+    row = O.moe_pairwise(x, lay, ids3, w3)[2]
+    assert np.allclose(row, a[2], rtol=1e-6, atol=1e-9 * scale)
+
+
+def test_moe_rows_subset():
+    lay = _small_layer()
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((7, lay.H))
+    ids = rng.integers(0, lay.E, size=(7, 3)).astype(np.int32)
+    w = rng.random((7, 3)).astype(np.float32)
+    full = O.moe_grouped(x, lay, ids, w)
+    rows = [5, 1, 6]
+    assert np.array_equal(O.moe_grouped(x, lay, ids, w, rows=rows), full[rows]) or \
+        np.allclose(O.moe_grouped(x, lay, ids, w, rows=rows), full[rows], rtol=1e-14, atol=0)
+    assert np.allclose(O.moe_pairwise(x, lay, ids, w, rows=rows), full[rows], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ routing
+def test_route_matches_stable_sort():
+    rng = np.random.default_rng(11)
+    for T, k, E in [(1, 8, 512), (5, 3, 4), (37, 8, 16), (200, 2, 7)]:
+        ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+        off, sp = O.route(ids, E)
+        flat = ids.reshape(-1)
+        valid = [p for p in range(T * k) if 0 <= flat[p] < E]
+        expect = sorted(valid, key=lambda p: flat[p])  # Python's sort is stable
+        n = len(expect)
+        assert off[0] == 0 and off[E] == n and np.all(np.diff(off) >= 0)
+        assert list(sp[:n]) == expect and np.all(sp[n:] == -1)
+        for e in range(E):
+            assert np.all(flat[sp[off[e]:off[e + 1]]] == e)
+
+
+# ------------------------------------------------------------------ W4A8 quantizer
+def test_quant_i8_fixture():
+    for ln in read_golden("quant_i8_cases.txt"):
+        xs, s, q = [f.strip() for f in ln.split("|")]
+        x = np.array([[float(v) for v in xs.split(",")]], dtype=np.float32)
+        qq, ss = O.quant_rows_i8(x)
+        assert ss[0] == np.float32(float(s)), (xs, ss[0])
+        assert list(qq[0]) == [int(v) for v in q.split(",")], (xs, qq[0])
+
+
+def test_quant_i8_properties():
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((64, 768)) * rng.uniform(1e-3, 1e3, size=(64, 1))).astype(np.float32)
+    q, s = O.quant_rows_i8(x)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(q[np.arange(64), am].astype(int)) == 127)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= 0.5 * s[:, None].astype(np.float64) * (1 + 1e-6))
+
+
+def test_w4a8_ffn_composition():
+    """W4A8 FFN = pinned pieces: quantize x, linear, silu, fp32 h, quantize h, linear."""
+    lay = _small_layer(E=2)
+    rng = np.random.default_rng(17)
+    xb = W.f32_to_bf16_bits(rng.standard_normal((4, lay.H)).astype(np.float32))
+    ids = np.array([[0], [1], [1], [0]], np.int32)
+    w = np.ones((4, 1), np.float32)
+    got = O.moe_w4a8(xb, lay, ids, w)
+    x32 = O.bf16_to_f64(xb).astype(np.float32)
+    qx, sx = O.quant_rows_i8(x32)
+    xh = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    for t in range(4):
+        e = ids[t, 0]
+        g = O.linear(xh[t:t + 1], lay.gate.codes[e], lay.gate.scales[e], lay.gate.gamma[e])
+        u = O.linear(xh[t:t + 1], lay.up.codes[e], lay.up.scales[e], lay.up.gamma[e])
+        h = (O.silu(g) * u).astype(np.float32)
+        qh, sh = O.quant_rows_i8(h)
+        hh = qh.astype(np.float64) * float(sh[0])
+        y = O.linear(hh, lay.down.codes[e], lay.down.scales[e], lay.down.gamma[e])
+        assert np.allclose(got[t], y[0], rtol=1e-13, atol=1e-13 * np.abs(y).max())
+
+
+def test_w4a8_exact_int8_inputs():
+    """Activations that are exactly q * 2^-4 with |q| <= 127 and a 127 present
+    quantize losslessly: the first GEMM equals the unquantized one."""
+    rng = np.random.default_rng(19)
+    q = rng.integers(-127, 128, size=(3, 32))
+    q[:, 0] = 127
+    x32 = (q * 0.0625).astype(np.float32)
+    qq, s = O.quant_rows_i8(x32)
+    assert np.all(s == np.float32(0.0625)) and np.array_equal(qq.astype(int), q)
+
+
+# ------------------------------------------------------------------ slicing (TF-906)
+def test_row_and_input_partitions_reassemble():
+    """TensorFold pull 906: row cuts and input cuts at multiples of 16 keep codes,
+    scale bytes and the global scale; reassembly recovers the original bytes, and
+    the partial products over input cuts sum to the full product."""
+    lay = _small_layer(E=1, H=64, I=48)
+    codes, scales, g = lay.gate.codes[0], lay.gate.scales[0], lay.gate.gamma[0]
+    N, K = 48, 64
+    rows = [(0, 16), (16, 40), (40, 48)]
+    cols = [(0, 16), (16, 48), (48, 64)]
+    full = O.dequant(codes, scales, g)
+    assert np.array_equal(np.concatenate([O.dequant(codes[a:b], scales[a:b], g) for a, b in rows]), full)
+    parts = [(codes[:, a // 2:b // 2], scales[:, a // 16:b // 16]) for a, b in cols]
+    assert np.array_equal(np.concatenate([p[0] for p in parts], axis=1), codes)
+    assert np.array_equal(np.concatenate([p[1] for p in parts], axis=1), scales)
+    assert np.array_equal(np.concatenate([O.dequant(c, s, g) for c, s in parts], axis=1), full)
+    x = np.random.default_rng(2).standard_normal((3, K))
+    y = O.linear(x, codes, scales, g)
+    ysum = sum(O.linear(x[:, a:b], c, s, g) for (a, b), (c, s) in zip(cols, parts))
+    assert np.allclose(ysum, y, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ negative controls
+def test_negative_controls_are_caught(monkeypatch):
+    """Plant mistakes in the oracle (on the CPU) and check a pin fails for each."""
+    cases = list(_hand_cases())
+    nib = [c for c in cases if c[0] == "nibble_low"][0]
+
+    # 1) swapped nibble order
+    def unpack_swapped(codes):
+        codes = np.asarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+        out[..., 0::2] = codes >> 4
+        out[..., 1::2] = codes & 0x0F
+        return out
+    monkeypatch.setattr(O.nvfp4_oracle, "unpack_codes", unpack_swapped)
+    assert O.nvfp4_oracle.linear(nib[4], nib[1], nib[2], nib[3])[0, 0] != nib[5]
+    monkeypatch.undo()
+
+    # 2) group size 32 instead of 16: the brute force over three groups disagrees
+    def dequant_g32(codes, scales, gamma=None):
+        vals = O.E2M1_TABLE[O.unpack_codes(codes)]
+        sc = O.E4M3_TABLE[np.asarray(scales)]
+        sc = np.repeat(sc, 32, axis=-1)[..., :vals.shape[-1]]
+        return vals * sc
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, 48))
+    codes = rng.integers(0, 256, size=(3, 24), dtype=np.uint8)
+    scales = rng.integers(0x18, 0x59, size=(3, 3), dtype=np.uint8)
+    ref = _bruteforce_linear(x, codes, scales, 1.0)
+    bad = x @ dequant_g32(codes, scales).T
+    assert not np.allclose(bad, ref, rtol=1e-6)
+
+    # 3) gate's global scale applied after SiLU: the hand closed form disagrees
+    def ffn_gamma_after(x, Wg, gg, Wu, gu, Wd, gd):
+        h = O.silu(x @ Wg.T) * gg * ((x @ Wu.T) * gu)
+        return (h @ Wd.T) * gd
+    monkeypatch.setattr(O.nvfp4_oracle, "expert_ffn", ffn_gamma_after)
+    with pytest.raises(AssertionError):
+        test_moe_hand_closed_form()
+    monkeypatch.undo()
+
+    # 4) gate and up swapped
+    def ffn_swapped(x, Wg, gg, Wu, gu, Wd, gd):
+        return expert_ref(x, Wu, gu, Wg, gg, Wd, gd)
+    expert_ref = O.nvfp4_oracle.expert_ffn
+    monkeypatch.setattr(O.nvfp4_oracle, "expert_ffn", ffn_swapped)
+    with pytest.raises(AssertionError):
+        test_moe_hand_closed_form()
+    monkeypatch.undo()
+
+    # 5) an unstable routing order fails the stable-sort pin
+    ids = np.array([[3, 1], [3, 0], [1, 3]], np.int32)
+    off, sp = O.route(ids, 4)
+    unstable = list(sp[:6])
+    i3 = [i for i in range(6) if ids.reshape(-1)[unstable[i]] == 3]
+    unstable[i3[0]], unstable[i3[-1]] = unstable[i3[-1]], unstable[i3[0]]
+    expect = sorted(range(6), key=lambda p: ids.reshape(-1)[p])
+    assert list(sp[:6]) == expect and unstable != expect
+
+    # 6) rounding the quantizer's quotient in float64 (not fp32) fails the fixture
+    x = np.array([[12.7, -6.35, 0.05, 0, 0, 0, 0, 0]], np.float32)
+    s = np.float32(12.7) / np.float32(127)
+    q64 = np.rint(x.astype(np.float64) / float(s))
+    assert q64[0, 1] == -63 and O.quant_rows_i8(x)[0][0, 1] == -64
