@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 routed-expert MoE layer on one MI355X.
+
+Headline (`value`): prefill tokens/s of one MoE layer at 8192 tokens (top-8 Zipf(1.1)
+routing over 512 experts, hidden 2048, expert intermediate 768, bf16 in and out); a
+step is one nvfp4_moe_prefill call (route, activation staging, gate/up + SwiGLU, down +
+weighted combine, final rounding). Steps rotate over 48 distinct device copies of the
+layer (65 GB), so no step finds its weights in the 256 MB Infinity Cache.
+
+Also reported on the same line: per-kernel times from HIP events on the launch stream
+and the roofline of the dominant kernel (the gate/up grouped GEMM against the dense
+fp16 matrix-core peak), decode HBM bandwidth at 1 and 4 tokens (hipGraph of 48
+layer calls, replayed), the W4A8 prefill at 32768 tokens, and the CPU oracle timed on
+a bounded sample of the prefill workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+PEAK_INT8_TOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+N_LAYERS = 48
+BYTES_PER_EXPERT = 3 * 2048 * 768 * 9 // 16  # codes + scales of gate, up, down
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=N_LAYERS)
+    ap.add_argument("--decode-rounds", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8"], default="all")
+    return ap.parse_args()
+
+
+def replicate(layer, n):
+    """n distinct device copies of one layer (same bytes, different addresses)."""
+    import nvfp4_quantized_moe_02_amd as nv
+    out = [layer]
+    for _ in range(n - 1):
+        out.append(nv.Layer(*[nv.Proj(p.codes.clone(), p.scales.clone(), p.gamma.clone())
+                              for p in (layer.gate, layer.up, layer.down)]))
+    return out
+
+
+def stage_times(calls, steps, nstages):
+    """Mean ms per stage over `steps` calls, from events on the launch stream."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nstages + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        c = calls[i % len(calls)]
+        for s in range(nstages):
+            ev[i][s].record()
+            c.stage(s)
+        ev[i][nstages].record()
+    torch.cuda.synchronize()
+    return [sum(ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(steps)) / steps for s in range(nstages)]
+
+
+def timed_steps(calls, steps, warmup):
+    import torch
+    for i in range(warmup):
+        calls[i % len(calls)].run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        calls[i % len(calls)].run()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bench_prefill(layers, index, act, steps, warmup):
+    import numpy as np
+    import torch
+    import nvfp4_quantized_moe_02_amd as nv
+    import workloads as W
+    wl = W.draw_workload(index)
+    dev = "cuda"
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(wl.ids).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    L0 = layers[0]
+    out = torch.empty((wl.T, L0.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nv.prefill_workspace_size(wl.T, L0.H, L0.I, L0.E, 8, act), dtype=torch.uint8, device=dev)
+    calls = [nv.PreparedCall("prefill", x, L, ids, w, out, ws, act=act) for L in layers]
+    ms = timed_steps(calls, steps, warmup)
+    st = stage_times(calls, steps, 4)
+    P = wl.T * 8
+    H, I = L0.H, L0.I
+    gu_flops = 2.0 * P * (2 * I) * H
+    dn_flops = 2.0 * P * H * I
+    counts = np.bincount(wl.ids.reshape(-1), minlength=L0.E)
+    tiles = int(np.sum((counts + 127) // 128))
+    return dict(T=wl.T, ms=ms, stages_ms=st, gu_flops=gu_flops, dn_flops=dn_flops,
+                padded_frac=P / (tiles * 128.0), tokens_per_s=wl.T / (ms / 1e3))
+
+
+def bench_decode(layers, index, rounds):
+    """hipGraph of one call per layer (48 layers), replayed `rounds` times."""
+    import numpy as np
+    import torch
+    import nvfp4_quantized_moe_02_amd as nv
+    import workloads as W
+    wl = W.draw_workload(index)
+    dev = "cuda"
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.from_numpy(wl.ids).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    L0 = layers[0]
+    out = torch.empty((wl.T, L0.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(nv.decode_workspace_size(wl.T, L0.H, L0.I, L0.E, 8), dtype=torch.uint8, device=dev)
+    calls = [nv.PreparedCall("decode", x, L, ids, w, out, ws) for L in layers]
+    res = {}
+    for name, fn in (("call", lambda c: c.run()), ("gateup", lambda c: c.stage(0)), ("down", lambda c: c.stage(1))):
+        for c in calls[:4]:
+            fn(c)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                fn(c)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(rounds):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) * 1e3 / (rounds * len(calls))  # us per launch
+        del g
+    U = len(np.unique(wl.ids))
+    byt = U * BYTES_PER_EXPERT
+    return dict(T=wl.T, unique_experts=U, bytes=byt, us=res["call"], us_gateup=res["gateup"],
+                us_down=res["down"], gbs=byt / (res["call"] * 1e-6) / 1e9,
+                gbs_gateup=U * 2 * 768 * 2048 * 9 / 16 / (res["gateup"] * 1e-6) / 1e9,
+                gbs_down=U * 768 * 2048 * 9 / 16 / (res["down"] * 1e-6) / 1e9)
+
+
+def cpu_baseline(n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle as O
+    import workloads as W
+    lay = W.draw_layer(W.config_seed(3))
+    wl = W.draw_workload(3)
+    x = O.bf16_to_f64(wl.x)
+    rows = np.arange(n_tokens)
+    t = time.perf_counter()
+    O.moe_grouped(x, lay, wl.ids, wl.w, rows=rows)
+    dt = time.perf_counter() - t
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the 8192-token prefill workload (all {len(np.unique(wl.ids[:n_tokens]))} "
+                      f"experts they route to), float64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_quantized_moe_02_amd as nv
+    import workloads as W
+    nv.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    t = time.time()
+    lay = W.draw_layer(W.config_seed(3))
+    base = nv.Layer.from_numpy(lay, "cuda")
+    del lay
+    layers = replicate(base, args.layers)
+    torch.cuda.synchronize()
+    log(f"{args.layers} layers on device in {time.time() - t:.1f} s")
+
+    result = {}
+    pre = None
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(layers, 3, "bf16", args.steps, args.warmup)
+        log(f"prefill 8192: {pre['ms']:.3f} ms/step, {pre['tokens_per_s']:.0f} tok/s, stages {pre['stages_ms']}")
+    dec = {}
+    if args.only in ("all", "decode"):
+        for idx in (1, 2):
+            d = bench_decode(layers, idx, args.decode_rounds)
+            dec[f"t{d['T']}"] = d
+            log(f"decode T={d['T']}: {d['us']:.2f} us/layer, {d['gbs']:.0f} GB/s (U={d['unique_experts']}), "
+                f"gate/up {d['us_gateup']:.2f} us, down {d['us_down']:.2f} us")
+    w4 = None
+    if args.only in ("all", "w4a8"):
+        w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2)
+        log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_sample_tokens)
+        log(f"cpu oracle: {cpu}")
+
+    if pre is not None:
+        gu_ms = pre["stages_ms"][1]
+        dn_ms = pre["stages_ms"][2]
+        achieved = pre["gu_flops"] / (gu_ms * 1e-3) / 1e12
+        result = {
+            "metric": "NVFP4 MoE layer: prefill tokens/s (% MFMA peak); decode HBM GB/s (% peak)",
+            "value": round(pre["tokens_per_s"], 1),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(pre["ms"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f16",
+            "data": "synthetic: seeded NVFP4 layer (512 experts, H=2048, I=768) copied to 48 device layers; "
+                    "seeded bf16 activations and Zipf(1.1) top-8 routing",
+            "config": {"workload": "prefill_t8192_zipf: one MoE layer, 8192 tokens, top-8 Zipf(1.1) over 512 "
+                                   "experts, hidden 2048, intermediate 768, NVFP4 gate/up/down, bf16 in/out, "
+                                   "fp16 matrix cores with fp32 accumulation",
+                       "tokens": pre["T"], "experts": 512, "topk": 8, "hidden": 2048, "intermediate": 768,
+                       "layers_rotated": args.layers},
+            "roofline": {"bound": "mfma", "kernel": "moe_gemm_f16_kernel (gate/up + SwiGLU)",
+                         "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+            "prefill_detail": {
+                "stage_ms": {"route_stage": round(pre["stages_ms"][0], 4), "gateup": round(gu_ms, 4),
+                             "down": round(dn_ms, 4), "finalize": round(pre["stages_ms"][3], 4)},
+                "down_tflops": round(pre["dn_flops"] / (dn_ms * 1e-3) / 1e12, 1),
+                "useful_tflops_step": round((pre["gu_flops"] + pre["dn_flops"]) / (pre["ms"] * 1e-3) / 1e12, 1),
+                "frac_of_fp16_peak_step": round((pre["gu_flops"] + pre["dn_flops"]) / (pre["ms"] * 1e-3) / 1e12
+                                                / PEAK_FP16_TFLOPS, 4),
+                "row_tile_fill": round(pre["padded_frac"], 4),
+            },
+        }
+    if dec:
+        result["decode"] = {k: {"us_per_layer": round(v["us"], 3), "GB/s": round(v["gbs"], 1),
+                                "frac_hbm_peak": round(v["gbs"] / PEAK_HBM_GBS, 4),
+                                "unique_experts": v["unique_experts"], "weight_bytes": v["bytes"],
+                                "us_gateup": round(v["us_gateup"], 3), "us_down": round(v["us_down"], 3),
+                                "GB/s_gateup": round(v["gbs_gateup"], 1), "GB/s_down": round(v["gbs_down"], 1),
+                                "timing": "hipGraph of 48 layer calls, replayed"}
+                            for k, v in dec.items()}
+    if w4 is not None:
+        result["w4a8"] = {"workload": "32768 tokens, int8 activations (x and h per row), fp16 matrix cores",
+                          "tokens/s": round(w4["tokens_per_s"], 1), "ms_per_step": round(w4["ms"], 4),
+                          "stage_ms": [round(v, 4) for v in w4["stages_ms"]],
+                          "frac_of_fp16_peak_step": round((w4["gu_flops"] + w4["dn_flops"]) / (w4["ms"] * 1e-3)
+                                                          / 1e12 / PEAK_FP16_TFLOPS, 4),
+                          "frac_of_int8_peak_step": round((w4["gu_flops"] + w4["dn_flops"]) / (w4["ms"] * 1e-3)
+                                                          / 1e12 / PEAK_INT8_TOPS, 4)}
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * nvfp4moe.h - C ABI of the NVFP4 routed-expert MoE projection for AMD MI355X (gfx950).
+ *
+ * The operation (sources are the pages this library is written from, cited by title
+ * and section):
+ *   - NVFP4 weights: 4-bit E2M1 codes, two per byte, one FP8 E4M3 scale byte per 16
+ *     consecutive inputs, and one FP32 global scale per expert tensor that multiplies
+ *     the projection's output ("Strata NVFP4" README, "How it differs from upstream
+ *     Strata": 4.5-bit experts with calibrated scales, per-expert FP32 scales kept and
+ *     applied to each projection's output; TensorFold pull 906: plain E4M3 scale bytes,
+ *     input cuts preserve groups of 16, the FP32 tensor scale).
+ *   - Routed experts: for token t and slot j with expert e = topk_ids[t][j],
+ *       g = gamma_gate[e] * (x_t . Wgate_e^T),  u = gamma_up[e] * (x_t . Wup_e^T)
+ *       h = SiLU(g) * u,  SiLU(z) = z / (1 + exp(-z))
+ *       y = gamma_down[e] * (h . Wdown_e^T)
+ *       out[t] = sum_j topk_weights[t][j] * y        (FP32 accumulation, one final rounding)
+ *     ("Strata NVFP4" README: routed experts kept in RAM and computed per token; the
+ *     shared expert's fused SwiGLU quantizer names the SwiGLU activation.)
+ *   - W4A8 prompt path: activations quantized per row to int8 with an FP32 scale
+ *     absmax / 127 before each expert GEMM ("Strata NVFP4" README, "How it differs from
+ *     upstream Strata": an int8 (W4A8) prompt path that keeps 8-bit activations).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor's
+ *     data_ptr()) owned by the caller. The library never allocates, frees or retains
+ *     them, and keeps no state between calls: it is safe to call from several host
+ *     threads on different streams, provided their workspaces and outputs differ.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. All
+ *     work is enqueued on it asynchronously; no call synchronizes the host.
+ *   - Arguments are validated completely before anything is enqueued: a call that
+ *     returns an error has enqueued nothing and written nothing. A failed kernel
+ *     launch returns NVFP4_EHIP.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Weight layout (one projection of E experts; rows are outputs):
+ *       codes  uint8 [E][N][K/2]   element 2j of a row in the LOW nibble of byte j,
+ *                                  element 2j+1 in the high nibble;
+ *       scales uint8 [E][N][K/16]  scale byte g covers inputs 16g .. 16g+15;
+ *       global float [E]           one FP32 scale per expert tensor.
+ *     K must be a multiple of 32. Code and scale planes must be 16-byte aligned.
+ *   - topk_ids int32 [T][topk], topk_weights float [T][topk]. Ids outside [0, E) are
+ *     dropped (they contribute nothing); the number dropped is written as an int32 to
+ *     the first 4 bytes of the workspace. Duplicate ids within a token are legal and
+ *     are summed. Router weights are used as given (no renormalization).
+ *   - NaN/Inf in activations or weights propagate to the outputs they touch.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = -1,       /* a null or misaligned pointer, a size out of range */
+  NVFP4_EUNSUPPORTED = -2, /* a valid request this build does not implement */
+  NVFP4_EWORKSPACE = -3,   /* ws_bytes smaller than the matching *_workspace_size() */
+  NVFP4_EHIP = -4          /* a HIP runtime error while enqueueing */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
+
+/* Activation handling of the prefill path.
+ *   NVFP4_ACT_BF16      bf16 activations; both expert GEMMs run on fp16 matrix cores
+ *                       (x is converted to fp16, h is kept in fp16).
+ *   NVFP4_ACT_W4A8      x and h quantized per row to int8 (scale absmax/127); the GEMMs
+ *                       run on int8 matrix cores with an FP32 rescale per 16-input group.
+ *   NVFP4_ACT_W4A8_F16  the same int8 activations and the same result, computed on fp16
+ *                       matrix cores (int8 values are exact in fp16). */
+typedef enum { NVFP4_ACT_BF16 = 0, NVFP4_ACT_W4A8 = 1, NVFP4_ACT_W4A8_F16 = 2 } nvfp4_act;
+
+/* One projection (gate, up or down) of all E experts of a layer. Device pointers. */
+typedef struct {
+  const uint8_t* codes;  /* [E][N][K/2] */
+  const uint8_t* scales; /* [E][N][K/16] */
+  const float* global;   /* [E] */
+  int32_t N;             /* outputs per expert (rows) */
+  int32_t K;             /* inputs per expert, multiple of 32 */
+} nvfp4_weight;
+
+/* Dequantize `rows` NVFP4 rows of K inputs: out[r][k] = e2m1 * e4m3 [* global[0]].
+ * codes [rows][K/2], scales [rows][K/16]; global is a device pointer to ONE float, or
+ * NULL for no global scale. out_dtype F32: the exact product rounded once to fp32.
+ * BF16: that fp32 value rounded to bf16 (round to nearest even). F16: the same to fp16.
+ * Without a global scale every product is exact in all three types. (Source: the NVFP4
+ * element formats above; #2727 "tools: add opt-in FP4-Local CSF checkpoint conversion"
+ * streams an NVFP4 table to BF16 in bounded row chunks, which is this call over row
+ * ranges.) Errors: EINVAL for null pointers, rows < 0, K <= 0 or K % 32 != 0. */
+int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* global, int64_t rows,
+                  int32_t K, int32_t out_dtype, void* out, void* stream);
+
+/* Single-expert NVFP4 linear: out[t][n] = w->global[expert] * sum_k x[t][k] * W_e[n][k].
+ * x [T][w->K] in x_dtype (F32 or BF16), out float [T][w->N]. (Same sources as above.)
+ * Errors: EINVAL for null pointers, T < 0, expert outside [0, E) (E is not known here:
+ * the caller guarantees the arrays hold expert+1 experts), bad K. */
+int nvfp4_linear(const void* x, int32_t x_dtype, int32_t T, const nvfp4_weight* w, int32_t expert,
+                 float* out, void* stream);
+
+/* Routing sort. Pairs p = t*topk + j are counting-sorted by expert id:
+ * expert_offsets int32 [E+1] is the exclusive prefix sum of per-expert pair counts
+ * (expert_offsets[E] = number of valid pairs); sorted_pairs int32 [T*topk] lists the
+ * valid pairs ordered by (expert, p) ascending, followed by -1 for each dropped pair.
+ * The order is deterministic and equals a stable sort. ws must hold
+ * nvfp4_route_workspace_size() bytes; its first 4 bytes receive the dropped count.
+ * ("Strata NVFP4" README: an MMQ group's experts gathered in one launch after one wait,
+ * instead of one wait per streamed expert.) Errors: EINVAL for null pointers, T < 0,
+ * topk < 1, E < 1 or E > 8192; EWORKSPACE. */
+size_t nvfp4_route_workspace_size(int32_t T, int32_t topk, int32_t E);
+int nvfp4_moe_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
+                    int32_t* expert_offsets, int32_t* sorted_pairs, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Per-row int8 quantization (the W4A8 activation rule): s[r] = fp32(absmax_r / 127) by
+ * an fp32 division, q[r][c] = clamp(round_half_even(fp32(x[r][c] / s[r])), -127, 127);
+ * an all-zero row gives s = 0 and q = 0. x [rows][cols] in x_dtype (F32 or BF16).
+ * ("Strata NVFP4" README: the W4A8 prompt path keeps 8-bit activations.)
+ * Errors: EINVAL for null pointers, rows < 0, cols < 1. */
+int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, int8_t* q,
+                        float* scale, void* stream);
+
+/* Decode (small token batches): the full routed-expert projection above for
+ * 1 <= T <= 8 tokens, with FP32 arithmetic throughout and h kept in fp32 ("#1858
+ * strata-safetensors": the quality profile keeps canonical FP32 expert decode).
+ * x [T][H] bf16; gate/up: N = I, K = H; down: N = H, K = I; out [T][H] in out_dtype
+ * (F32 or BF16). ws needs nvfp4_moe_decode_workspace_size() bytes. The result does not
+ * depend on scheduling: every output element is summed in a fixed order.
+ * Errors: EINVAL (null pointers, shapes that disagree, H or I not a multiple of 32,
+ * topk < 1, E < 1); EUNSUPPORTED for x not bf16, T > 8, topk * T > 64, H or I above
+ * 8192; EWORKSPACE. T == 0 is a no-op and may pass null tensors. */
+size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk);
+int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                     const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                     const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
+                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill (any T >= 0): the same projection as grouped GEMMs on matrix cores, one
+ * launch per stage for all experts. x [T][H] bf16; out [T][H] bf16 or f32 (accumulated
+ * in fp32, rounded once). `act` selects the activation handling (nvfp4_act).
+ * ws needs nvfp4_moe_prefill_workspace_size() bytes. ("Strata NVFP4" README: prompt
+ * chunks up to 32K tokens, where every chunk streams every layer's experts once.)
+ * The down projection adds each pair's contribution into the fp32 accumulator with
+ * atomic adds, so the summation order of the (at most topk) terms of an output element
+ * can differ between runs. T == 0 is a no-op and may pass null tensors.
+ * Errors: EINVAL (null pointers, shapes that disagree, unknown act, out_dtype F16);
+ * EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128, E > 8192, x_dtype
+ * other than BF16; EWORKSPACE. */
+size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                        int32_t act);
+int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                      const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                      const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act,
+                      void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* One stage of the same sequence, for callers that interleave or time the stages.
+ * Arguments, validation and workspace are those of the full call; running the stages
+ * in order on one stream with the same arguments and workspace is the full call.
+ * Decode stages: 0 gate/up + SwiGLU (h into the workspace), 1 down + combine.
+ * Prefill stages: 0 zero the accumulator, route, stage the activations (fp16, or int8
+ * codes and row scales for W4A8); 1 gate/up + SwiGLU (W4A8: then requantize h);
+ * 2 down + weighted combine; 3 final rounding to the output dtype.
+ * Errors: those of the full call, and EINVAL for a stage outside that range. */
+int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                           const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down,
+                           int32_t E, const int32_t* topk_ids, const float* topk_weights, int32_t topk,
+                           void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                            const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down,
+                            int32_t E, const int32_t* topk_ids, const float* topk_weights, int32_t topk,
+                            int32_t act, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

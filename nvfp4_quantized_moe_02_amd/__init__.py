@@ -1,0 +1,26 @@
+"""NVFP4 routed-expert MoE projection on AMD MI355X (gfx950).
+
+A thin ctypes binding over libnvfp4moe.so (C ABI in include/nvfp4moe.h). This module
+only marshals arguments: every step of the computation runs in the library's HIP
+kernels. torch supplies device memory and the current stream. There is no fallback:
+if the library is missing the import of the binding fails loudly.
+"""
+from .binding import (  # noqa: F401
+    ACT,
+    DTYPE,
+    NVFP4Error,
+    PreparedCall,
+    Proj,
+    Layer,
+    dequant,
+    lib_path,
+    linear,
+    load_library,
+    moe_decode,
+    moe_prefill,
+    quant_rows_i8,
+    route,
+    decode_workspace_size,
+    prefill_workspace_size,
+    route_workspace_size,
+)

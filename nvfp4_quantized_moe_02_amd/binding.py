@@ -1,0 +1,292 @@
+"""ctypes binding of libnvfp4moe.so: the same entry points as include/nvfp4moe.h.
+
+Argument marshalling only: tensors become device pointers, dtypes become the C enums,
+and the current torch stream is passed through. No arithmetic of the method is done
+here; a non-zero status raises NVFP4Error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libnvfp4moe.so"
+
+DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+ACT = {"bf16": 0, "w4a8": 1, "w4a8_f16": 2}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("global_", ctypes.c_void_p),
+        ("N", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+    ]
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+_SIGS = {
+    "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4_dequant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "nvfp4_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Weight),
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "nvfp4_route_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "nvfp4_moe_route": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]),
+    "nvfp4_quant_rows_i8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "nvfp4_moe_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 5),
+    "nvfp4_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
+    "nvfp4_moe_decode_stage": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                              ctypes.POINTER(_Weight), ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "nvfp4_moe_prefill_stage": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                               ctypes.POINTER(_Weight), ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "nvfp4_moe_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 6),
+    "nvfp4_moe_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().nvfp4_status_string(status).decode()
+        raise NVFP4Error(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class Proj:
+    """One NVFP4 projection of E experts on the device: codes uint8 [E][N][K/2],
+    scales uint8 [E][N][K/16], gamma float32 [E]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    gamma: torch.Tensor
+
+    @property
+    def N(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def K(self) -> int:
+        return int(self.codes.shape[2]) * 2
+
+    def cstruct(self) -> _Weight:
+        return _Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.gamma), self.N, self.K)
+
+    @staticmethod
+    def from_numpy(p, device) -> "Proj":
+        return Proj(torch.from_numpy(p.codes).to(device), torch.from_numpy(p.scales).to(device),
+                    torch.from_numpy(p.gamma).to(device))
+
+
+@dataclass
+class Layer:
+    gate: Proj
+    up: Proj
+    down: Proj
+
+    @property
+    def E(self) -> int:
+        return int(self.gate.codes.shape[0])
+
+    @property
+    def H(self) -> int:
+        return self.gate.K
+
+    @property
+    def I(self) -> int:
+        return self.gate.N
+
+    @staticmethod
+    def from_numpy(layer, device="cuda") -> "Layer":
+        return Layer(Proj.from_numpy(layer.gate, device), Proj.from_numpy(layer.up, device),
+                     Proj.from_numpy(layer.down, device))
+
+
+def dequant(codes: torch.Tensor, scales: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+            out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """codes [rows][K/2], scales [rows][K/16], gamma: one float32 or None."""
+    lib = load_library()
+    K = int(codes.shape[-1]) * 2
+    rows = codes.numel() // (K // 2)
+    if out is None:
+        out = torch.empty(codes.shape[:-1] + (K,), dtype=out_dtype, device=codes.device)
+    _check("nvfp4_dequant", lib.nvfp4_dequant(_ptr(codes), _ptr(scales), _ptr(gamma), rows, K, DTYPE[out.dtype],
+                                              _ptr(out), _stream(codes.device)))
+    return out
+
+
+def linear(x: torch.Tensor, proj: Proj, expert: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load_library()
+    T = int(x.shape[0])
+    if out is None:
+        out = torch.empty((T, proj.N), dtype=torch.float32, device=x.device)
+    w = proj.cstruct()
+    _check("nvfp4_linear", lib.nvfp4_linear(_ptr(x), DTYPE[x.dtype], T, ctypes.byref(w), expert, _ptr(out),
+                                            _stream(x.device)))
+    return out
+
+
+def route_workspace_size(T: int, topk: int, E: int) -> int:
+    return int(load_library().nvfp4_route_workspace_size(T, topk, E))
+
+
+def route(ids: torch.Tensor, E: int, ws: Optional[torch.Tensor] = None):
+    """Returns (expert_offsets int32 [E+1], sorted_pairs int32 [T*topk], ws)."""
+    lib = load_library()
+    T, k = int(ids.shape[0]), int(ids.shape[1])
+    dev = ids.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    need = route_workspace_size(T, k, E)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("nvfp4_moe_route", lib.nvfp4_moe_route(_ptr(ids), T, k, E, _ptr(off), _ptr(sp), _ptr(ws), ws.numel(),
+                                                  _stream(dev)))
+    return off, sp[:T * k], ws
+
+
+def quant_rows_i8(x: torch.Tensor):
+    lib = load_library()
+    rows, cols = int(x.shape[0]), int(x.shape[1])
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check("nvfp4_quant_rows_i8", lib.nvfp4_quant_rows_i8(_ptr(x), DTYPE[x.dtype], rows, cols, _ptr(q), _ptr(s),
+                                                          _stream(x.device)))
+    return q, s
+
+
+def decode_workspace_size(T: int, H: int, I: int, E: int, topk: int) -> int:
+    return int(load_library().nvfp4_moe_decode_workspace_size(T, H, I, E, topk))
+
+
+def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str = "bf16") -> int:
+    return int(load_library().nvfp4_moe_prefill_workspace_size(T, H, I, E, topk, ACT[act]))
+
+
+def _ws(ws: Optional[torch.Tensor], need: int, dev) -> torch.Tensor:
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def moe_decode(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor,
+               out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    k = int(ids.shape[1])
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    ws = _ws(ws, decode_workspace_size(T, H, layer.I, layer.E, k), x.device)
+    g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
+    _check("nvfp4_moe_decode", lib.nvfp4_moe_decode(
+        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+        _ptr(w), k, _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def moe_prefill(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor, act: str = "bf16",
+                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    k = int(ids.shape[1])
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    ws = _ws(ws, prefill_workspace_size(T, H, layer.I, layer.E, k, act), x.device)
+    g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
+    _check("nvfp4_moe_prefill", lib.nvfp4_moe_prefill(
+        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+        _ptr(w), k, ACT[act], _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+class PreparedCall:
+    """A decode or prefill call with its arguments marshalled once, for launch loops
+    (benchmarks, graph capture): run() enqueues the whole call, stage(i) one stage."""
+
+    def __init__(self, kind: str, x, layer: Layer, ids, w, out, ws, act: str = "bf16"):
+        self.lib = load_library()
+        self.kind = kind
+        self.keep = (x, layer, ids, w, out, ws)
+        self._w = (layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct())
+        g, u, d = (ctypes.byref(v) for v in self._w)
+        T, H = int(x.shape[0]), int(x.shape[1])
+        k = int(ids.shape[1])
+        common = [_ptr(x), DTYPE[x.dtype], T, H, g, u, d, layer.E, _ptr(ids), _ptr(w), k]
+        tail = [_ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel()]
+        self.device = x.device
+        if kind == "decode":
+            self.args = common + tail
+            self.full, self.staged, self.nstages = self.lib.nvfp4_moe_decode, self.lib.nvfp4_moe_decode_stage, 2
+        else:
+            self.args = common + [ACT[act]] + tail
+            self.full, self.staged, self.nstages = self.lib.nvfp4_moe_prefill, self.lib.nvfp4_moe_prefill_stage, 4
+
+    def run(self) -> None:
+        # the stream is looked up per call, so graph capture sees its capture stream
+        _check(self.kind, self.full(*self.args, _stream(self.device)))
+
+    def stage(self, i: int) -> None:
+        _check(self.kind + "_stage", self.staged(i, *self.args, _stream(self.device)))

@@ -1,0 +1,295 @@
+// The C ABI (include/nvfp4moe.h): argument validation, workspace layout and launch
+// order. Every entry point validates all of its arguments before enqueueing anything.
+#include "../../include/nvfp4moe.h"
+#include "kernels.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+bool weight_ok(const nvfp4_weight* w) {
+  return w && w->codes && w->scales && w->global && w->N > 0 && w->K > 0 && (w->K % 32) == 0 &&
+         aligned(w->codes, 16) && aligned(w->scales, 16);
+}
+
+WeightArgs to_args(const nvfp4_weight* w) { return WeightArgs{w->codes, w->scales, w->global, w->N, w->K}; }
+
+// Workspace carving: offsets are computed identically by the size query and the call.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  }
+};
+
+struct RouteLayout {
+  size_t hdr, counts, dropped, offsets, sorted, tiles, end;
+  int nblk, max_tiles;
+};
+
+RouteLayout route_layout(int64_t P, int E, bool with_tiles, Carver& c) {
+  RouteLayout l;
+  l.nblk = route_blocks(P);
+  l.max_tiles = with_tiles ? (int)((P + kTileM - 1) / kTileM + (P < E ? P : E)) : 0;
+  l.hdr = c.take(64);
+  l.counts = c.take((size_t)E * l.nblk * 4);
+  l.dropped = c.take((size_t)l.nblk * 4);
+  l.offsets = c.take((size_t)(E + 1) * 4);
+  l.sorted = c.take((size_t)P * 4);
+  l.tiles = c.take((size_t)l.max_tiles * sizeof(TileDesc));
+  l.end = c.off;
+  return l;
+}
+
+struct PrefillLayout {
+  RouteLayout r;
+  size_t a16, sx, h, qh16, sh, acc, end;
+};
+
+PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
+  Carver c;
+  PrefillLayout l;
+  const int64_t P = (int64_t)T * topk;
+  l.r = route_layout(P, E, true, c);
+  const bool w4a8 = act != NVFP4_ACT_BF16;
+  l.a16 = c.take((size_t)T * H * 2);
+  l.sx = c.take(w4a8 ? (size_t)T * 4 : 0);
+  l.h = c.take((size_t)P * I * (w4a8 ? 4 : 2));
+  l.qh16 = c.take(w4a8 ? (size_t)P * I * 2 : 0);
+  l.sh = c.take(w4a8 ? (size_t)P * 4 : 0);
+  l.acc = c.take((size_t)T * H * 4);
+  l.end = c.off;
+  return l;
+}
+
+struct DecodeLayout {
+  size_t hdr, h, end;
+};
+
+DecodeLayout decode_layout(int T, int I, int topk) {
+  Carver c;
+  DecodeLayout l;
+  l.hdr = c.take(64);
+  l.h = c.take((size_t)T * topk * I * 4);
+  l.end = c.off;
+  return l;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_EUNSUPPORTED: return "unsupported configuration";
+    case NVFP4_EWORKSPACE: return "workspace too small";
+    case NVFP4_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* global, int64_t rows, int32_t K,
+                  int32_t out_dtype, void* out, void* stream) {
+  if (!codes || !scales || !out || rows < 0 || K <= 0 || (K % 32) != 0) return NVFP4_EINVAL;
+  if (out_dtype < NVFP4_F32 || out_dtype > NVFP4_F16) return NVFP4_EINVAL;
+  if (!aligned(codes, 16) || !aligned(out, 16)) return NVFP4_EINVAL;
+  (void)hipGetLastError();
+  return hip_status(launch_dequant(codes, scales, global, rows, K, out_dtype, out, as_stream(stream)));
+}
+
+int nvfp4_linear(const void* x, int32_t x_dtype, int32_t T, const nvfp4_weight* w, int32_t expert, float* out,
+                 void* stream) {
+  if (!x || !out || T < 0 || expert < 0 || !weight_ok(w)) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (!aligned(x, 4)) return NVFP4_EINVAL;
+  (void)hipGetLastError();
+  const size_t er = (size_t)expert * w->N;
+  return hip_status(launch_linear(x, x_dtype, T, w->codes + er * (w->K / 2), w->scales + er * (w->K / 16),
+                                  w->global + expert, w->N, w->K, out, as_stream(stream)));
+}
+
+size_t nvfp4_route_workspace_size(int32_t T, int32_t topk, int32_t E) {
+  if (T < 0 || topk < 1 || E < 1) return 0;
+  Carver c;
+  return route_layout((int64_t)T * topk, E, false, c).end;
+}
+
+int nvfp4_moe_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E, int32_t* expert_offsets,
+                    int32_t* sorted_pairs, void* ws, size_t ws_bytes, void* stream) {
+  if (!expert_offsets || !ws || T < 0 || topk < 1 || E < 1 || E > kMaxExperts) return NVFP4_EINVAL;
+  if (T > 0 && (!topk_ids || !sorted_pairs)) return NVFP4_EINVAL;
+  if ((int64_t)T * topk > (int64_t)1 << 30) return NVFP4_EUNSUPPORTED;
+  if (!aligned(ws, 16)) return NVFP4_EINVAL;
+  Carver c;
+  const RouteLayout l = route_layout((int64_t)T * topk, E, false, c);
+  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
+  RouteWs rw{at<int32_t>(ws, l.counts), at<int32_t>(ws, l.dropped), at<int32_t>(ws, l.hdr), nullptr};
+  (void)hipGetLastError();
+  return hip_status(
+      launch_route(topk_ids, (int64_t)T * topk, E, expert_offsets, sorted_pairs, rw, kTileM, as_stream(stream)));
+}
+
+int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, int8_t* q, float* scale,
+                        void* stream) {
+  if (!x || !q || !scale || rows < 0 || cols < 1) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (rows > 0x7fffffff) return NVFP4_EUNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, 0, scale, as_stream(stream)));
+}
+
+size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk) {
+  (void)H;
+  (void)E;
+  if (T < 0 || I < 1 || topk < 1) return 0;
+  return decode_layout(T, I, topk).end;
+}
+
+static int check_moe_common(const void* x, int32_t T, int32_t H, const nvfp4_weight* gate, const nvfp4_weight* up,
+                            const nvfp4_weight* down, int32_t E, const int32_t* ids, const float* w, int32_t topk,
+                            void* out, void* ws) {
+  if (!ws || T < 0 || H < 1 || E < 1 || topk < 1) return NVFP4_EINVAL;
+  if (T > 0 && (!x || !ids || !w || !out)) return NVFP4_EINVAL;  // T == 0 may pass empty (null) tensors
+  if (!weight_ok(gate) || !weight_ok(up) || !weight_ok(down)) return NVFP4_EINVAL;
+  const int I = gate->N;
+  if (gate->K != H || up->K != H || up->N != I || down->N != H || down->K != I) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 16)) return NVFP4_EINVAL;
+  return NVFP4_OK;
+}
+
+static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                       const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                       const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
+                       int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_moe_common(x, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, ws);
+  if (st != NVFP4_OK) return st;
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
+  const int I = gate->N;
+  if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > 8192 || I > 8192) return NVFP4_EUNSUPPORTED;
+  const DecodeLayout l = decode_layout(T, I, topk);
+  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
+  if (T == 0) return NVFP4_OK;
+  (void)hipGetLastError();
+  for (int stage = first; stage <= last; ++stage) {
+    hipError_t e = launch_decode(stage, x, T, H, I, to_args(gate), to_args(up), to_args(down), E, topk_ids,
+                                 topk_weights, topk, out, out_dtype, at<float>(ws, l.h), at<int32_t>(ws, l.hdr),
+                                 as_stream(stream));
+    if (e != hipSuccess) return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
+}
+
+int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                     const nvfp4_weight* up, const nvfp4_weight* down, int32_t E, const int32_t* topk_ids,
+                     const float* topk_weights, int32_t topk, void* out, int32_t out_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return decode_impl(0, 1, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, out_dtype, ws,
+                     ws_bytes, stream);
+}
+
+int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                           const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                           const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
+                           int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (stage < 0 || stage > 1) return NVFP4_EINVAL;
+  return decode_impl(stage, stage, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out,
+                     out_dtype, ws, ws_bytes, stream);
+}
+
+size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return 0;
+  return prefill_layout(T, H, I, E, topk, act).end;
+}
+
+static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                        const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                        const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act, void* out,
+                        int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_moe_common(x, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, ws);
+  if (st != NVFP4_OK) return st;
+  if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
+  if (act == NVFP4_ACT_W4A8) return NVFP4_EUNSUPPORTED;
+  const int I = gate->N;
+  if ((H % 256) != 0 || (I % 128) != 0 || E > kMaxExperts) return NVFP4_EUNSUPPORTED;
+  if ((int64_t)T * topk > (int64_t)1 << 30) return NVFP4_EUNSUPPORTED;
+  const PrefillLayout l = prefill_layout(T, H, I, E, topk, act);
+  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
+  if (T == 0) return NVFP4_OK;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const int64_t P = (int64_t)T * topk;
+  float* acc = out_dtype == NVFP4_F32 ? reinterpret_cast<float*>(out) : at<float>(ws, l.acc);
+  int32_t* offsets = at<int32_t>(ws, l.r.offsets);
+  int32_t* sorted = at<int32_t>(ws, l.r.sorted);
+  int32_t* hdr = at<int32_t>(ws, l.r.hdr);
+  TileDesc* tiles = at<TileDesc>(ws, l.r.tiles);
+  void* a16 = at<void>(ws, l.a16);
+  float* sx = at<float>(ws, l.sx);
+  float* sh = at<float>(ws, l.sh);
+  const int mode = act == NVFP4_ACT_BF16 ? 0 : 1;
+  for (int stage = first; stage <= last; ++stage) {
+    hipError_t e = hipSuccess;
+    if (stage == 0) {  // zero the accumulator, route, stage the activations
+      e = launch_zero(acc, (int64_t)T * H * 4, s);
+      if (e == hipSuccess) {
+        RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles};
+        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
+      }
+      if (e == hipSuccess) {
+        if (act == NVFP4_ACT_BF16) e = launch_bf16_to_f16(x, a16, (int64_t)T * H, s);
+        else e = launch_quant_rows(x, NVFP4_BF16, T, H, a16, 1, sx, s);
+      }
+    } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
+      e = launch_gemm_gateup(mode, a16, sx, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+                             to_args(gate), to_args(up), at<void>(ws, l.h), s);
+      if (e == hipSuccess && mode == 1)
+        e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<void>(ws, l.qh16), 1, sh, s);
+    } else if (stage == 2) {  // down + weighted combine into the fp32 accumulator
+      const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh16);
+      e = launch_gemm_down(mode, hA, sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+                           to_args(down), topk_weights, acc, s);
+    } else if (out_dtype == NVFP4_BF16) {  // one rounding of the accumulator
+      e = launch_finalize_bf16(acc, out, (int64_t)T * H, s);
+    }
+    if (e != hipSuccess) return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
+}
+
+int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                      const nvfp4_weight* up, const nvfp4_weight* down, int32_t E, const int32_t* topk_ids,
+                      const float* topk_weights, int32_t topk, int32_t act, void* out, int32_t out_dtype, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return prefill_impl(0, 3, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, act, out, out_dtype,
+                      ws, ws_bytes, stream);
+}
+
+int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,
+                            const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                            const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act, void* out,
+                            int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (stage < 0 || stage > 3) return NVFP4_EINVAL;
+  return prefill_impl(stage, stage, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, act, out,
+                      out_dtype, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Shared device helpers for the NVFP4 MoE kernels (gfx950 / CDNA4 only).
+//
+// Element decoding follows the NVFP4 format: E2M1 codes (two per byte, element 2j in
+// the low nibble), one FP8 E4M3 (OCP "FN") scale per 16 inputs, one FP32 global scale
+// per expert tensor ("Strata NVFP4" README, "How it differs from upstream Strata";
+// TensorFold pull 906 for the E4M3 scale bytes and the 16-input groups).
+//
+// gfx950 facts these helpers rely on (each checked against the CPU oracle by the
+// bit-exact dequantization tests):
+//   * v_cvt_scalef32_pk_{f32,f16,bf16}_fp4 decode the two E2M1 codes of one byte, low
+//     nibble first, and multiply by 2^exponent(scale): only the scale's exponent is
+//     used (an E8M0 scale), never its mantissa.
+//   * v_cvt_f32_fp8 decodes the OCP E4M3 "FN" format (0x7F/0xFF NaN, max 448).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+namespace nvfp4 {
+
+constexpr int kGroup = 16;
+
+// ---------------------------------------------------------------- scalar codecs
+// E4M3 byte SEL of `word` -> fp32 (exact).
+template <int SEL>
+__device__ __forceinline__ float e4m3_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
+}
+
+// The two E2M1 codes of byte SEL of `word` as exact fp32 values (low nibble -> [0]).
+template <int SEL>
+__device__ __forceinline__ f32x2_t e2m1x2_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+// The two E2M1 codes of byte SEL as exact bf16 values.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t e2m1x2_bf16(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+}
+
+// A scale split for the fp16 unpack: the E2M1 convert applies 2^exponent(s); the
+// remaining factor sign(s) * 1.mmm (at most 4 significant bits, exact in fp16) is
+// applied with one packed fp16 multiply. e2m1 * e4m3 is exact in fp16 (at most 5
+// significant bits, magnitudes 2^-10 .. 2688), so the product of the two steps is
+// the exact dequantized weight. A NaN scale gives a NaN factor, so NaN propagates.
+struct F16Scale {
+  float expo;     // passed to the convert; only its exponent field matters
+  f16x2_t mant;   // (m, m)
+};
+
+__device__ __forceinline__ F16Scale f16_scale(float s) {
+  uint32_t b = __float_as_uint(s);
+  float m = __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+  if ((b & 0x7F800000u) == 0x7F800000u) m = __uint_as_float(0x7FC00000u);
+  F16Scale r;
+  r.expo = s;
+  _Float16 mh = (_Float16)m;
+  r.mant = f16x2_t{mh, mh};
+  return r;
+}
+
+// Byte SEL of `word` -> two exact fp16 weights e2m1 * scale.
+template <int SEL>
+__device__ __forceinline__ f16x2_t e2m1x2_f16_scaled(uint32_t word, const F16Scale& sc) {
+  f16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc.expo, SEL);
+  return v * sc.mant;
+}
+
+// Four bytes (8 codes) -> 8 exact fp16 weights, element order = k order.
+__device__ __forceinline__ void unpack8_f16(uint32_t word, const F16Scale& sc, f16x2_t out[4]) {
+  out[0] = e2m1x2_f16_scaled<0>(word, sc);
+  out[1] = e2m1x2_f16_scaled<1>(word, sc);
+  out[2] = e2m1x2_f16_scaled<2>(word, sc);
+  out[3] = e2m1x2_f16_scaled<3>(word, sc);
+}
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- wave reductions
+// Sum over groups of 16 consecutive lanes (every lane of the group gets the total).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace nvfp4

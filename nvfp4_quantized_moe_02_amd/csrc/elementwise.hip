@@ -1,0 +1,239 @@
+// Element-wise kernels: NVFP4 dequantization, the single-expert linear, per-row int8
+// quantization (the W4A8 activation rule) and activation staging for the prefill GEMMs.
+#include "kernels.h"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------------ dequantization
+// One thread per 16-input group: 8 code bytes + 1 scale byte -> 16 outputs.
+// F32: e2m1 (exact) * e4m3 (exact product) * global: one rounding.
+// BF16 / F16 with a global: that fp32 value rounded once more. F16 without a global:
+// the same unpack the prefill GEMMs feed to the matrix cores (exponent-scaled convert
+// times the scale's mantissa factor), so this output checks that unpack bit for bit.
+template <int OUT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ global,
+                                                      int64_t ngroups, void* __restrict__ out) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= ngroups) return;
+  const uint2 cw = *reinterpret_cast<const uint2*>(codes + g * 8);
+  const uint32_t sb = scales[g];
+  const float s = e4m3_f32<0>(sb);
+  const bool has_g = global != nullptr;
+  const float gam = has_g ? global[0] : 1.0f;
+  if (OUT == 2 && !has_g) {
+    const F16Scale sc = f16_scale(s);
+    f16x2_t o[8];
+    unpack8_f16(cw.x, sc, o);
+    unpack8_f16(cw.y, sc, o + 4);
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + g * 16);
+    dst[0] = *reinterpret_cast<uint4*>(&o[0]);
+    dst[1] = *reinterpret_cast<uint4*>(&o[4]);
+    return;
+  }
+  float v[16];
+  const uint32_t w[2] = {cw.x, cw.y};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    f32x2_t p0 = e2m1x2_f32<0>(w[q]), p1 = e2m1x2_f32<1>(w[q]);
+    f32x2_t p2 = e2m1x2_f32<2>(w[q]), p3 = e2m1x2_f32<3>(w[q]);
+    v[q * 8 + 0] = p0[0]; v[q * 8 + 1] = p0[1]; v[q * 8 + 2] = p1[0]; v[q * 8 + 3] = p1[1];
+    v[q * 8 + 4] = p2[0]; v[q * 8 + 5] = p2[1]; v[q * 8 + 6] = p3[0]; v[q * 8 + 7] = p3[1];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = v[i] * s;
+    if (has_g) v[i] = v[i] * gam;
+    // The output is defined as the fp32 product rounded again to the output type. The
+    // empty asm pins the fp32 value in a register, so the backend cannot fold the
+    // multiply and the narrowing into one mixed-precision FMA (a single rounding to
+    // fp16 that also turns -0 into +0 by adding +0).
+    asm volatile("" : "+v"(v[i]));
+  }
+  if (OUT == 0) {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + g * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t lo = OUT == 1 ? f32_to_bf16_bits(v[2 * i]) : f32_to_f16_bits(v[2 * i]);
+      uint32_t hi = OUT == 1 ? f32_to_bf16_bits(v[2 * i + 1]) : f32_to_f16_bits(v[2 * i + 1]);
+      pk[i] = lo | (hi << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + g * 16);
+    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* global,
+                          int64_t rows, int K, int out_dtype, void* out, hipStream_t st) {
+  const int64_t ngroups = rows * (K / kGroup);
+  if (ngroups == 0) return hipSuccess;
+  const int64_t blocks = (ngroups + 255) / 256;
+  if (out_dtype == 0)
+    dequant_kernel<0><<<dim3((unsigned)blocks), 256, 0, st>>>(codes, scales, global, ngroups, out);
+  else if (out_dtype == 1)
+    dequant_kernel<1><<<dim3((unsigned)blocks), 256, 0, st>>>(codes, scales, global, ngroups, out);
+  else
+    dequant_kernel<2><<<dim3((unsigned)blocks), 256, 0, st>>>(codes, scales, global, ngroups, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ single-expert linear
+// One wave per (token, output row): lanes stride over the 16-input groups.
+template <bool XBF16>
+__global__ __launch_bounds__(64) void linear_kernel(const void* __restrict__ x, int K,
+                                                    const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales,
+                                                    const float* __restrict__ global, int N,
+                                                    float* __restrict__ out) {
+  const int n = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  const uint8_t* rc = codes + (size_t)n * (K / 2);
+  const uint8_t* rs = scales + (size_t)n * (K / kGroup);
+  float acc = 0.f;
+  for (int g = lane; g < K / kGroup; g += 64) {
+    const uint2 cw = *reinterpret_cast<const uint2*>(rc + g * 8);
+    const float s = e4m3_f32<0>(rs[g]);
+    float part = 0.f;
+    const uint32_t w[2] = {cw.x, cw.y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      f32x2_t p[4] = {e2m1x2_f32<0>(w[q]), e2m1x2_f32<1>(w[q]), e2m1x2_f32<2>(w[q]), e2m1x2_f32<3>(w[q])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = g * 16 + q * 8 + 2 * i;
+        float x0, x1;
+        if (XBF16) {
+          const uint32_t xv = reinterpret_cast<const uint32_t*>(x)[((size_t)t * K + k) / 2];
+          x0 = bf16_lo(xv);
+          x1 = bf16_hi(xv);
+        } else {
+          x0 = reinterpret_cast<const float*>(x)[(size_t)t * K + k];
+          x1 = reinterpret_cast<const float*>(x)[(size_t)t * K + k + 1];
+        }
+        part = fmaf(p[i][0], x0, part);
+        part = fmaf(p[i][1], x1, part);
+      }
+    }
+    acc = fmaf(part, s, acc);
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) out[(size_t)t * N + n] = acc * global[0];
+}
+
+hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes, const uint8_t* scales,
+                         const float* global, int N, int K, float* out, hipStream_t st) {
+  if (T == 0 || N == 0) return hipSuccess;
+  dim3 grid(N, T);
+  if (x_dtype == 1)
+    linear_kernel<true><<<grid, 64, 0, st>>>(x, K, codes, scales, global, N, out);
+  else
+    linear_kernel<false><<<grid, 64, 0, st>>>(x, K, codes, scales, global, N, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ int8 row quantization
+// One block per row. s = absmax / 127 (IEEE fp32 division), q = rint(x / s) clamped to
+// +-127 (IEEE fp32 division, round half to even); all-zero rows give s = 0, q = 0.
+// OUTQ: 0 -> int8 codes, 1 -> the same integers as fp16 (exact), for the fp16 GEMMs.
+template <int XT, int OUTQ>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int cols,
+                                                         void* __restrict__ q, float* __restrict__ scale) {
+  const int64_t r = blockIdx.x;
+  __shared__ float red[4];
+  auto load = [&](int c) -> float {
+    if (XT == 1) return bf16_lo(reinterpret_cast<const uint16_t*>(x)[r * cols + c]);
+    return reinterpret_cast<const float*>(x)[r * cols + c];
+  };
+  float m = 0.f;
+  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(load(c)));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float absmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = absmax / 127.0f;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    float v = 0.f;
+    if (s > 0.f) v = fminf(fmaxf(rintf(load(c) / s), -127.f), 127.f);
+    if (OUTQ == 0)
+      reinterpret_cast<int8_t*>(q)[r * cols + c] = (int8_t)(int)v;
+    else
+      reinterpret_cast<uint16_t*>(q)[r * cols + c] = f32_to_f16_bits(v);
+  }
+  if (threadIdx.x == 0) scale[r] = s;
+}
+
+hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
+                             float* scale, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)rows);
+  if (x_dtype == 1) {
+    if (q_f16) quant_rows_kernel<1, 1><<<grid, 256, 0, st>>>(x, cols, q, scale);
+    else quant_rows_kernel<1, 0><<<grid, 256, 0, st>>>(x, cols, q, scale);
+  } else {
+    if (q_f16) quant_rows_kernel<0, 1><<<grid, 256, 0, st>>>(x, cols, q, scale);
+    else quant_rows_kernel<0, 0><<<grid, 256, 0, st>>>(x, cols, q, scale);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ activation staging
+// bf16 -> fp16 (round to nearest even; exact for |x| in the fp16 normal range).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
+                                                          int64_t n8) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  uint4 v = x[i];
+  uint32_t in[4] = {v.x, v.y, v.z, v.w}, o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)f32_to_f16_bits(bf16_lo(in[j])) | ((uint32_t)f32_to_f16_bits(bf16_hi(in[j])) << 16);
+  y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_bf16_to_f16(const void* x, void* y, int64_t n, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  bf16_to_f16_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, st>>>(
+      reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), n8);
+  return hipGetLastError();
+}
+
+// Zero fill (a kernel rather than a memset node, so the sequence can be graph-captured).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  zero_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+// fp32 accumulator -> output dtype (bf16: round to nearest even).
+__global__ __launch_bounds__(256) void finalize_bf16_kernel(const float4* __restrict__ acc, uint2* __restrict__ out,
+                                                            int64_t n4) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 v = acc[i];
+  out[i] = make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                      (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+}
+
+hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  finalize_bf16_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
+      reinterpret_cast<const float4*>(acc), reinterpret_cast<uint2*>(out), n4);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,64 @@
+// Kernel launchers shared between the translation units of libnvfp4moe.so. Every
+// launcher enqueues on `st` and returns hipGetLastError(); argument validation is the
+// C-ABI layer's job (api.hip).
+#pragma once
+#include "common.h"
+
+namespace nvfp4 {
+
+struct WeightArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global;
+  int N, K;
+};
+
+struct TileDesc {
+  int expert;
+  int m0;
+};
+
+// elementwise.hip
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* global, int64_t rows,
+                          int K, int out_dtype, void* out, hipStream_t st);
+hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes, const uint8_t* scales,
+                         const float* global, int N, int K, float* out, hipStream_t st);
+hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
+                             float* scale, hipStream_t st);
+hipError_t launch_bf16_to_f16(const void* x, void* y, int64_t n, hipStream_t st);
+hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
+hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st);
+
+// route.hip
+constexpr int kRouteChunk = 4096;  // pairs per counting block
+constexpr int kMaxExperts = 8192;
+struct RouteWs {
+  int32_t* counts;    // [E][nblk]
+  int32_t* dropped;   // [nblk]
+  int32_t* hdr;       // hdr[0] = dropped pairs, hdr[1] = tile count
+  TileDesc* tiles;    // [max_tiles] (optional)
+};
+int route_blocks(int64_t P);
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
+                        const RouteWs& ws, int tile_m, hipStream_t st);
+
+// decode.hip
+constexpr int kDecodeMaxT = 8;
+constexpr int kDecodeMaxPairs = 64;
+// stage 0: gate/up + SwiGLU; stage 1: down + combine
+hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
+                         const WeightArgs& down, int E, const int32_t* ids, const float* w, int topk,
+                         void* out, int out_dtype, float* h, int32_t* hdr, hipStream_t st);
+
+// prefill.hip
+constexpr int kTileM = 128;
+hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* sorted_pairs,
+                              const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
+                              int max_tiles, int topk, int H, int I, const WeightArgs& gate,
+                              const WeightArgs& up, void* h, hipStream_t st);
+hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* sorted_pairs,
+                            const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
+                            int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
+                            float* out_acc, hipStream_t st);
+
+}  // namespace nvfp4
