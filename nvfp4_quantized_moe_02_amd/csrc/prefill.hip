@@ -3,38 +3,49 @@
 // Strata": an MMQ group's experts gathered in one launch; prompt chunks up to 32K
 // tokens, each streaming every expert of a layer once).
 //
-// Tile = (expert, 128 routed rows) x one N block; 4 waves. Each wave owns a 128 x 64
-// output block (4 x 2 blocks of v_mfma_f32_32x32x16_f16). The A operand (activations,
-// fp16) is staged through LDS, double-buffered, 64 inputs per K-block; rows are
-// gathered by token for gate/up and contiguous for down. The B operand never touches
-// LDS: each lane loads the 16 code bytes and 2 scale bytes its fragment needs with one
-// 128-bit load and unpacks them exactly to fp16 (exponent-scaled convert, then one
-// packed fp16 multiply by the scale's mantissa factor), so every weight byte is read
-// once per tile and decoded once per wave. Within a K-block the reduction order of the
-// 64 inputs is permuted (lane half 0 takes inputs 0..31, half 1 inputs 32..63); A uses
-// the same permutation, so the dot products are unchanged.
+// Tile = (expert, up to 128 routed rows) x one N block; 4 waves. Each wave owns an
+// NRB*32 x 64 output block (NRB row blocks x 2 column blocks of v_mfma_f32_32x32x16_f16),
+// where NRB = ceil(rows / 32) is a template parameter, so partial tiles skip the empty
+// row blocks without branches in the K loop.
+//
+// A operand (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into
+// registers and stored to a 2-stage LDS ring at the top of the iteration that uses it.
+// Each LDS row holds 64 inputs (8 slots of 16 bytes); slot c of row r holds chunk
+// c ^ (r & 7), so the 32 rows of an MFMA fragment read hit 8 distinct slots (no bank
+// conflicts). Rows are gathered by token for gate/up and contiguous for down.
+//
+// B operand (NVFP4 weights): each lane loads the 16 code bytes and 2 scale bytes its
+// fragment needs (two K-blocks ahead, in registers) and unpacks them exactly to
+// fp16: the E2M1 convert applies 2^exponent(scale), one packed fp16 multiply applies the
+// scale's mantissa factor (e2m1 * e4m3 has at most 5 significant bits). Weight bytes
+// never pass through LDS and are decoded once per wave. Within a K-block the reduction
+// order of the 64 inputs is permuted (lane half 0 takes inputs 0..31, half 1 inputs
+// 32..63); A is read with the same permutation, so the dot products are unchanged.
 //
 // gate/up: wave w computes gate and up for the same 32 intermediate indices, so SwiGLU
 // runs in registers: h = SiLU(gamma_g * g) * (gamma_u * u) (gate scale before SiLU, the
 // "Strata NVFP4" README's per-projection output scale). down: the epilogue multiplies by
 // gamma_d and the router weight and adds into an fp32 [T][H] accumulator.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace nvfp4 {
 
 constexpr int BM = kTileM;
-constexpr int KBLK = 64;
-constexpr int LDS_STRIDE = 72;  // fp16 per LDS row: 64 + 8 padding (144 B, conflict-free 128-bit reads)
+constexpr int KBLK = 64;                        // inputs per K-block
+constexpr int NSTAGE = 2;                       // LDS stages of A
+constexpr int STAGE_BYTES = BM * KBLK * 2;      // 16 KiB per stage
 
 struct BRaw {
   uint4 c;     // 32 codes
-  uint32_t s;  // 2 scale bytes (groups of this lane's 32 inputs)
+  uint32_t s;  // 2 scale bytes (the two groups of this lane's 32 inputs)
 };
 
-__device__ __forceinline__ BRaw load_braw(const uint8_t* rowc, const uint8_t* rows, int kb, int half) {
+__device__ __forceinline__ BRaw load_braw(const uint8_t* pc, const uint8_t* ps) {
   BRaw r;
-  r.c = *reinterpret_cast<const uint4*>(rowc + kb * 32 + half * 16);
-  r.s = *reinterpret_cast<const uint16_t*>(rows + kb * 4 + half * 2);
+  r.c = *reinterpret_cast<const uint4*>(pc);
+  r.s = *reinterpret_cast<const uint16_t*>(ps);
   return r;
 }
 
@@ -52,6 +63,136 @@ __device__ __forceinline__ f16x8_t bfrag(uint32_t word, const F16Scale& sc) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// SiLU for the fp16/fp32 h of the prefill path: exp and reciprocal from the hardware
+// approximations (about 1 ulp each).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+struct TileCtx {
+  int e, m0, rows, base, nb;
+};
+
+template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB>
+__device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
+                                          const uint8_t* const* bc, const uint8_t* const* bs,
+                                          const WeightArgs& w0, const WeightArgs& w1, void* __restrict__ out,
+                                          int ldo, char* lds, const int* s_src, const int* s_tok,
+                                          const float* s_coef) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nkb = K / KBLK;
+
+  // A: thread t copies 16-byte chunk t & 7 of rows (t >> 3) + 32*i, i < NRB, of a
+  // K-block; it stores chunk c of row r into slot c ^ (r & 7) of that LDS row.
+  const int arow = tid >> 3, achunk = tid & 7;
+  const uint16_t* asrc[NRB];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) asrc[i] = A + (size_t)s_src[arow + 32 * i] * K + achunk * 8;
+  const int aslot = ((achunk ^ (arow & 7)) << 4);
+
+  const uint8_t* pc0 = bc[0] + half * 16;
+  const uint8_t* pc1 = bc[1] + half * 16;
+  const uint8_t* ps0 = bs[0] + half * 2;
+  const uint8_t* ps1 = bs[1] + half * 2;
+  auto load_b = [&](int kb, int cb) -> BRaw {
+    const int kc = kb < nkb ? kb : nkb - 1;  // past the end: refetch the last block (never used)
+    return cb == 0 ? load_braw(pc0 + kc * 32, ps0 + kc * 4) : load_braw(pc1 + kc * 32, ps1 + kc * 4);
+  };
+  auto load_a = [&](int kb, int i) -> uint4 {
+    const int kc = kb < nkb ? kb : nkb - 1;
+    return *reinterpret_cast<const uint4*>(asrc[i] + kc * KBLK);
+  };
+
+  f32x16_t acc[NRB][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][cb][i] = 0.f;
+
+  // Two K-blocks of A (registers) and B (registers) in flight. Iteration kb: store
+  // A(kb) into LDS stage kb & 1, barrier, issue A(kb+2) and B(kb+2), compute K-block kb.
+  uint4 aq[2][NRB];
+  BRaw bq[2][2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) aq[d][i] = load_a(d, i);
+    bq[d][0] = load_b(d, 0);
+    bq[d][1] = load_b(d, 1);
+  }
+
+  auto kstep = [&](auto ring, int kb) {
+    constexpr int R = decltype(ring)::value;
+    char* st = lds + R * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) *reinterpret_cast<uint4*>(st + (arow + 32 * i) * 128 + aslot) = aq[R][i];
+    // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
+    // finished those reads before passing the barrier of iteration kb-1.
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) aq[R][i] = load_a(kb + 2, i);
+    const BRaw cur0 = bq[R][0], cur1 = bq[R][1];
+    bq[R][0] = load_b(kb + 2, 0);
+    bq[R][1] = load_b(kb + 2, 1);
+    const F16Scale sc00 = f16_scale(e4m3_f32<0>(cur0.s)), sc01 = f16_scale(e4m3_f32<1>(cur0.s));
+    const F16Scale sc10 = f16_scale(e4m3_f32<0>(cur1.s)), sc11 = f16_scale(e4m3_f32<1>(cur1.s));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8_t b0 = bfrag(word_of(cur0.c, s), s < 2 ? sc00 : sc01);
+      const f16x8_t b1 = bfrag(word_of(cur1.c, s), s < 2 ? sc10 : sc11);
+      const int chunk = half * 4 + s;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int row = rb * 32 + l32;
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(st + row * 128 + ((chunk ^ (row & 7)) << 4));
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[rb][1], 0, 0, 0);
+      }
+    }
+  };
+  // nkb is even (K is a multiple of 128)
+  for (int kb = 0; kb < nkb; kb += 2) {
+    kstep(std::integral_constant<int, 0>{}, kb);
+    kstep(std::integral_constant<int, 1>{}, kb + 1);
+  }
+
+  if (GATEUP) {
+    const float gg = w0.global[tc.e], gu = w1.global[tc.e];
+    const int jcol = tc.nb * 128 + wave * 32 + l32;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        if (r < tc.rows) {
+          const float xs = s_coef[r];
+          const float g = acc[rb][0][i] * (xs * gg);
+          const float u = acc[rb][1][i] * (xs * gu);
+          const float hv = silu_fast(g) * u;
+          const size_t o = (size_t)(tc.base + tc.m0 + r) * ldo + jcol;
+          if (HOUT32) reinterpret_cast<float*>(out)[o] = hv;
+          else reinterpret_cast<uint16_t*>(out)[o] = f32_to_f16_bits(hv);
+        }
+      }
+  } else {
+    const float gd = w0.global[tc.e];
+    float* o = reinterpret_cast<float*>(out);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        if (r < tc.rows) {
+          const float c = s_coef[r] * gd;
+          float* orow = o + (size_t)s_tok[r] * ldo + tc.nb * 256 + wave * 64 + l32;
+          unsafeAtomicAdd(orow, acc[rb][0][i] * c);
+          unsafeAtomicAdd(orow + 32, acc[rb][1][i] * c);
+        }
+      }
+  }
+}
+
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
 // ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
 // HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
@@ -61,31 +202,34 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
     void* __restrict__ out, int ldo) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
   __shared__ int s_src[BM];
   __shared__ int s_tok[BM];
   __shared__ float s_coef[BM];
 
-  // XCD-aware order: consecutive logical tiles (the N blocks of one row tile, which
-  // share their A rows) run on the same XCD and its L2.
+  // XCD-aware order: consecutive logical tiles (the N blocks of one row tile, then the
+  // row tiles of one expert) run on the same XCD and share its L2.
   const int total = *tile_count * NB;
   const int per = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
   if (jj >= per) return;
   const int L = xcd * per + jj;
   if (L >= total) return;
-  const int tile = L / NB, nb = L - tile * NB;
+  TileCtx tc;
+  const int tile = L / NB;
+  tc.nb = L - tile * NB;
   const TileDesc td = tiles[tile];
-  const int e = td.expert, m0 = td.m0;
-  const int base = offsets[e];
-  const int Me = offsets[e + 1] - base;
-  const int rows = Me - m0 < BM ? Me - m0 : BM;
+  tc.e = td.expert;
+  tc.m0 = td.m0;
+  tc.base = offsets[tc.e];
+  const int Me = offsets[tc.e + 1] - tc.base;
+  tc.rows = Me - tc.m0 < BM ? Me - tc.m0 : BM;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int l32 = lane & 31;
   if (tid < BM) {
-    const int r = tid < rows ? tid : rows - 1;  // padding rows repeat the last row
-    const int pos = base + m0 + r;
+    const int r = tid < tc.rows ? tid : tc.rows - 1;  // padding rows repeat the last row
+    const int pos = tc.base + tc.m0 + r;
     const int p = sorted_pairs[pos];
     if (GATEUP) {
       s_src[tid] = p / topk;
@@ -100,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
   const uint8_t* bc[2];
   const uint8_t* bs[2];
   if (GATEUP) {
-    const size_t grow = (size_t)e * w0.N + nb * 128 + wave * 32 + l32;
+    const size_t grow = (size_t)tc.e * w0.N + tc.nb * 128 + wave * 32 + l32;
     bc[0] = w0.codes + grow * (K / 2);
     bs[0] = w0.scales + grow * (K / 16);
     bc[1] = w1.codes + grow * (K / 2);
@@ -108,103 +252,22 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
   } else {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const size_t grow = (size_t)e * w0.N + nb * 256 + wave * 64 + cb * 32 + l32;
+      const size_t grow = (size_t)tc.e * w0.N + tc.nb * 256 + wave * 64 + cb * 32 + l32;
       bc[cb] = w0.codes + grow * (K / 2);
       bs[cb] = w0.scales + grow * (K / 16);
     }
   }
   __syncthreads();
 
-  const int nkb = K / KBLK;
-  const int arow = tid >> 3, achunk = tid & 7;
-  const uint16_t* asrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) asrc[i] = A + (size_t)s_src[arow + 32 * i] * K + achunk * 8;
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][cb][i] = 0.f;
-
-  uint4 areg[4];
-  BRaw braw[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) areg[i] = *reinterpret_cast<const uint4*>(asrc[i]);
-  braw[0] = load_braw(bc[0], bs[0], 0, half);
-  braw[1] = load_braw(bc[1], bs[1], 0, half);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint4*>(&As[0][(arow + 32 * i) * LDS_STRIDE + achunk * 8]) = areg[i];
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    const BRaw cur0 = braw[0], cur1 = braw[1];
-    const bool more = kb + 1 < nkb;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) areg[i] = *reinterpret_cast<const uint4*>(asrc[i] + (kb + 1) * KBLK);
-      braw[0] = load_braw(bc[0], bs[0], kb + 1, half);
-      braw[1] = load_braw(bc[1], bs[1], kb + 1, half);
-    }
-    const F16Scale sc00 = f16_scale(e4m3_f32<0>(cur0.s)), sc01 = f16_scale(e4m3_f32<1>(cur0.s));
-    const F16Scale sc10 = f16_scale(e4m3_f32<0>(cur1.s)), sc11 = f16_scale(e4m3_f32<1>(cur1.s));
-    const uint16_t* Ab = As[kb & 1];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8_t b0 = bfrag(word_of(cur0.c, s), s < 2 ? sc00 : sc01);
-      const f16x8_t b1 = bfrag(word_of(cur1.c, s), s < 2 ? sc10 : sc11);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f16x8_t a =
-            *reinterpret_cast<const f16x8_t*>(Ab + (rb * 32 + l32) * LDS_STRIDE + half * 32 + s * 8);
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[rb][1], 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(&As[(kb + 1) & 1][(arow + 32 * i) * LDS_STRIDE + achunk * 8]) = areg[i];
-    }
-  }
-
-  if (GATEUP) {
-    const float gg = w0.global[e], gu = w1.global[e];
-    const int jcol = nb * 128 + wave * 32 + l32;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        if (r < rows) {
-          const float xs = s_coef[r];
-          const float g = acc[rb][0][i] * xs * gg;
-          const float u = acc[rb][1][i] * xs * gu;
-          const float hv = silu(g) * u;
-          const size_t o = (size_t)(base + m0 + r) * ldo + jcol;
-          if (HOUT32) reinterpret_cast<float*>(out)[o] = hv;
-          else reinterpret_cast<uint16_t*>(out)[o] = f32_to_f16_bits(hv);
-        }
-      }
-  } else {
-    const float gd = w0.global[e];
-    float* o = reinterpret_cast<float*>(out);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        if (r < rows) {
-          const float c = s_coef[r] * gd;
-          float* orow = o + (size_t)s_tok[r] * ldo + nb * 256 + wave * 64 + l32;
-          unsafeAtomicAdd(orow, acc[rb][0][i] * c);
-          unsafeAtomicAdd(orow + 32, acc[rb][1][i] * c);
-        }
-      }
-  }
+  const int nrb = (tc.rows + 31) >> 5;
+  if (nrb == 4)
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+  else if (nrb == 3)
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+  else if (nrb == 2)
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+  else
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
