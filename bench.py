@@ -125,7 +125,7 @@ def bench_decode(layers, index, rounds):
     w = torch.from_numpy(wl.w).to(dev)
     L0 = layers[0]
     out = torch.empty((wl.T, L0.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(nv.decode_workspace_size(wl.T, L0.H, L0.I, L0.E, 8), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nv.decode_workspace_size(wl.T, L0.H, L0.I, L0.E, 8), dtype=torch.uint8, device=dev)
     calls = [nv.PreparedCall("decode", x, L, ids, w, out, ws) for L in layers]
     res = {}
     for name, fn in (("call", lambda c: c.run()), ("gateup", lambda c: c.stage(0)), ("down", lambda c: c.stage(1))):

@@ -225,8 +225,10 @@ def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str =
 
 
 def _ws(ws: Optional[torch.Tensor], need: int, dev) -> torch.Tensor:
+    """A workspace of at least `need` bytes; new ones are zero-filled (the decode
+    workspace holds a grid-barrier counter that must start at zero)."""
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     return ws
 
 

@@ -182,17 +182,17 @@ static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int3
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
   if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > 8192 || I > 8192) return NVFP4_EUNSUPPORTED;
+  if ((int64_t)T * H > kDecodeMaxTH) return NVFP4_EUNSUPPORTED;  // activations are staged in LDS
   const DecodeLayout l = decode_layout(T, I, topk);
   if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
   if (T == 0) return NVFP4_OK;
   (void)hipGetLastError();
-  for (int stage = first; stage <= last; ++stage) {
-    hipError_t e = launch_decode(stage, x, T, H, I, to_args(gate), to_args(up), to_args(down), E, topk_ids,
-                                 topk_weights, topk, out, out_dtype, at<float>(ws, l.h), at<int32_t>(ws, l.hdr),
-                                 as_stream(stream));
-    if (e != hipSuccess) return NVFP4_EHIP;
-  }
-  return NVFP4_OK;
+  // the full call runs as one persistent launch (mode 2); a single stage as mode 0 or 1
+  const int mode = (first == 0 && last == 1) ? 2 : first;
+  hipError_t e = launch_decode(mode, x, T, H, I, to_args(gate), to_args(up), to_args(down), E, topk_ids,
+                               topk_weights, topk, out, out_dtype, at<float>(ws, l.h), at<int32_t>(ws, l.hdr),
+                               as_stream(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
 int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,

@@ -1,50 +1,140 @@
 // Decode path (1..8 tokens): HBM-bound NVFP4 GEMVs with FP32 arithmetic, the pages'
 // quality profile for expert decode ("#1858 strata-safetensors": canonical FP32 expert
-// decode). Two launches per layer:
-//   1. gate/up + SwiGLU: one block per (unique expert, 16 intermediate rows); h in fp32.
-//   2. down + top-k combine: each wave owns 4 output rows and sums every routed pair of
-//      every token into them in a fixed order, so the result is deterministic.
-// Both kernels derive the unique-expert list from topk_ids themselves (no host sync).
+// decode). A decode round is dominated by the expert bytes it moves ("Strata NVFP4"
+// README, "Limits"), so the whole layer runs as ONE persistent launch:
+//
+//   setup    every block derives the unique-expert list from topk_ids and copies the
+//            bf16 activations into LDS.
+//   phase 1  gate/up + SwiGLU: units of (unique expert, 4 intermediate rows) are spread
+//            over all waves of the grid; h (fp32) goes to the workspace.
+//   barrier  one arrival per block on an agent-scope counter (release), a relaxed poll
+//            with a bounded spin, one acquire.
+//   phase 2  down + top-k combine: block b owns output rows 8b .. 8b+7; every block
+//            copies h into LDS once; waves w and w+2, w+4, w+6 share a quad of rows and
+//            split the unique experts, each sums its experts' pairs in a fixed order, and
+//            the partials are added in wave order, so the result is deterministic. Each
+//            wave issues the loads of its first down weights before phase 1, so that
+//            traffic overlaps phase 1 and the wait.
+//
+// The same device code also runs as two ordinary launches (phase 1, then phase 2) for
+// the staged entry point and for shapes whose grid cannot be co-resident; both forms
+// give bit-identical results. Both derive the unique-expert list from topk_ids
+// themselves (no host synchronization).
 //
 // Lane mapping: 16 lanes per weight row, each lane reads 16-byte chunks (32 inputs =
-// two scale groups) with 128-bit loads; four rows per wave-wide load, so each load
-// instruction covers 4 rows x 256 contiguous bytes.
+// two scale groups) with 128-bit loads; a wave covers 4 rows, so each load instruction
+// reads 4 rows x 256 contiguous bytes.
 #include "kernels.h"
 
 namespace nvfp4 {
 
-// Unique experts of the routed pairs, in order of first appearance. Every thread of
-// the block calls this (it holds barriers); wave 0 does the work. s_ids receives each
-// pair's id (or -1 when dropped), s_uniq the unique ids; returns their number.
-__device__ int block_unique_experts(const int32_t* __restrict__ ids, int P, int E, int* s_ids, int* s_uniq,
-                                    int* s_nu, int* s_drop) {
+constexpr int kDecWaves = 8;     // waves per block
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kRowsPerBlock = 8;  // output rows per block in phase 2 (two quads of 4)
+constexpr int kUB = 4;            // down units (one expert x 4 rows) a wave loads at once
+
+struct DecodeSmem {
+  int ids[64];    // each pair's expert id, or -1 when dropped
+  int uniq[64];   // unique experts in order of first appearance
+  int list[64];   // pairs grouped by unique expert, each group in pair order
+  int start[65];  // group boundaries in list
+  float wp[64];   // router weight of each pair
+  int nu, drop, ok;
+  float part[kDecWaves][4][kDecodeMaxT];
+};
+
+// Dynamic LDS: x (bf16, T x H) then, when it fits, h (fp32, P x I). Both are stored in
+// 16-byte-padded chunks (x: 64 B of data per 80 B, h: 128 B per 144 B), so the 16 lanes
+// of a row group, which read chunks l16, l16 + 16, ..., hit distinct banks.
+extern __shared__ __attribute__((aligned(16))) char dec_lds[];
+
+__host__ __device__ inline size_t x_lds_bytes(int T, int H) { return (size_t)T * (H / 32) * 80; }
+__host__ __device__ inline size_t h_lds_bytes(int P, int I) { return (size_t)P * (I / 32) * 144; }
+__device__ inline const uint4* x_lds_chunk(int t, int H, int ch) {
+  return reinterpret_cast<const uint4*>(dec_lds + (size_t)t * (H / 32) * 80 + ch * 80);
+}
+__device__ inline const float* h_lds_chunk(int H_T_bytes, int p, int I, int ch) {
+  return reinterpret_cast<const float*>(dec_lds + H_T_bytes + (size_t)p * (I / 32) * 144 + ch * 144);
+}
+
+struct DecodeArgs {
+  const uint16_t* x;
+  int T, H, I, E, P, topk;
+  WeightArgs gate, up, down;
+  const int32_t* ids;
+  const float* w;
+  float* h;
+  void* out;
+  int out_dtype;
+  int32_t* hdr;                  // [0] dropped pairs, [1] error flags
+  unsigned long long* barrier;   // grid barrier counter
+  int spin_limit;
+  int h_in_lds;                  // phase 2 reads h from LDS (P * I * 4 bytes fit)
+};
+
+
+
+// s_waitcnt immediate: no vector-memory operation of this wave outstanding.
+constexpr int kVmcnt0 = (7 << 4) | (0xF << 8);
+
+// Setup, called by every thread of the block (it holds barriers). The loads of the
+// routing ids, the router weights and the activations are issued together; wave 0 then
+// forms the unique-expert list with cross-lane shuffles (order of first appearance)
+// and the pair list of each unique expert.
+__device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x) {
   const int tid = threadIdx.x;
   int e = -1;
-  bool valid = false;
-  if (tid < 64) {
-    e = tid < P ? ids[tid] : -1;
-    valid = tid < P && (unsigned)e < (unsigned)E;
-    s_ids[tid] = valid ? e : -1;
+  float wv = 0.f;
+  if (tid < 64 && tid < a.P) {
+    e = a.ids[tid];
+    wv = a.w[tid];
   }
-  __syncthreads();
+  if (copy_x) {
+    const int n16 = a.T * a.H / 8;  // 16-byte pieces, 4 per 32-input chunk
+    const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+    for (int i = tid; i < n16; i += kDecThreads)
+      *reinterpret_cast<uint4*>(dec_lds + (i >> 2) * 80 + (i & 3) * 16) = xs[i];
+  }
   if (tid < 64) {
+    const bool valid = tid < a.P && (unsigned)e < (unsigned)a.E;
+    const int ev = valid ? e : -1;
+    sm.ids[tid] = ev;
+    sm.wp[tid] = wv;
     bool first = valid;
-    for (int q = 0; q < tid; ++q)
-      if (s_ids[q] == e) first = false;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+      const int eq = __builtin_amdgcn_readlane(ev, q);  // lane q's id, no LDS round trip
+      if (q < tid && eq == ev) first = false;
+    }
+    const uint64_t lt = (1ull << tid) - 1ull;
     const uint64_t fm = __ballot(first);
-    const uint64_t dm = __ballot(tid < P && !valid);
-    if (first) s_uniq[__popcll(fm & ((1ull << tid) - 1ull))] = e;
+    const uint64_t dm = __ballot(tid < a.P && !valid);
+    const int nu = __popcll(fm);
+    // uniq[rank of my first appearance] = my id; then every lane reads the list back
+    if (first) sm.uniq[__popcll(fm & lt)] = ev;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int start = 0;
+    for (int u = 0; u < nu; ++u) {
+      const int eu = sm.uniq[u];
+      const bool m = ev == eu;
+      const uint64_t mm = __ballot(m);
+      if (m) sm.list[start + __popcll(mm & lt)] = tid;
+      if (tid == 0) sm.start[u] = start;
+      start += __popcll(mm);
+    }
     if (tid == 0) {
-      *s_nu = __popcll(fm);
-      *s_drop = __popcll(dm);
+      sm.start[nu] = start;
+      sm.nu = nu;
+      sm.drop = __popcll(dm);
     }
   }
   __syncthreads();
-  return *s_nu;
 }
 
 // One 16-byte chunk (32 inputs, two scale groups) of a weight row dotted with bf16
-// activations held as 16 packed pairs. Returns the scaled partial sum.
+// activations held as 16 packed pairs; returns the scaled partial sum.
 __device__ __forceinline__ float dot_chunk_bf16(const uint4 c, uint32_t sc, const uint32_t* xv) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float part[2] = {0.f, 0.f};
@@ -60,204 +150,347 @@ __device__ __forceinline__ float dot_chunk_bf16(const uint4 c, uint32_t sc, cons
   return part[0] * e4m3_f32<0>(sc) + part[1] * e4m3_f32<1>(sc);
 }
 
-// ------------------------------------------------------------------ gate/up + SwiGLU
-// CH = chunk iterations per lane = ceil(H / 32 / 16).
-template <int CH>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(const uint16_t* __restrict__ x, int H, int I,
-                                                            WeightArgs gate, WeightArgs up, int E,
-                                                            const int32_t* __restrict__ ids, int P, int topk,
-                                                            float* __restrict__ h, int32_t* __restrict__ hdr) {
-  __shared__ int s_ids[64], s_uniq[64], s_pairs[64];
-  __shared__ int s_nu, s_np, s_drop;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nu = block_unique_experts(ids, P, E, s_ids, s_uniq, &s_nu, &s_drop);
-  if (tid < 64) {
-    if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) hdr[0] = s_drop;
-    const int ex = (int)blockIdx.y < nu ? s_uniq[blockIdx.y] : -2;
-    const bool match = tid < P && s_ids[tid] == ex;
-    const uint64_t mm = __ballot(match);
-    if (match) s_pairs[__popcll(mm & ((1ull << tid) - 1ull))] = tid;
-    if (tid == 0) s_np = __popcll(mm);
+// One 16-byte chunk of a down row dotted with 32 fp32 h values.
+__device__ __forceinline__ float dot_chunk_f32(const uint4 c, uint32_t sc, const float* __restrict__ hp) {
+  const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+  const float4* h4 = reinterpret_cast<const float4*>(hp);
+  float g2[2] = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 ha = h4[2 * q], hb = h4[2 * q + 1];
+    const f32x2_t w0 = e2m1x2_f32<0>(wd[q]), w1 = e2m1x2_f32<1>(wd[q]);
+    const f32x2_t w2 = e2m1x2_f32<2>(wd[q]), w3 = e2m1x2_f32<3>(wd[q]);
+    float s = g2[q >> 1];
+    s = fmaf(w0[0], ha.x, s); s = fmaf(w0[1], ha.y, s);
+    s = fmaf(w1[0], ha.z, s); s = fmaf(w1[1], ha.w, s);
+    s = fmaf(w2[0], hb.x, s); s = fmaf(w2[1], hb.y, s);
+    s = fmaf(w3[0], hb.z, s); s = fmaf(w3[1], hb.w, s);
+    g2[q >> 1] = s;
   }
-  __syncthreads();
-  if ((int)blockIdx.y >= nu) return;
-  const int e = s_uniq[blockIdx.y];
-  const int np = s_np;
-  const int row = blockIdx.x * 16 + wave * 4 + (lane >> 4);
-  const int l16 = lane & 15;
-  const int nch = H >> 5;  // 16-byte chunks per row
-  if (row >= I) return;
-  const size_t grow = (size_t)e * I + row;
-  const uint8_t* gc = gate.codes + grow * (H / 2);
-  const uint8_t* uc = up.codes + grow * (H / 2);
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(gate.scales + grow * (H / 16));
-  const uint16_t* us = reinterpret_cast<const uint16_t*>(up.scales + grow * (H / 16));
-  uint4 gcode[CH], ucode[CH];
-  uint32_t gsc[CH], usc[CH];
+  return g2[0] * e4m3_f32<0>(sc) + g2[1] * e4m3_f32<1>(sc);
+}
+
+// ---- phase 1: a unit is (unique expert slot u, intermediate rows 4q .. 4q+3)
+template <int CH>
+struct GateUpRows {
+  uint4 gc[CH], uc[CH];
+  uint32_t gs[CH], us[CH];
+  float gg, gu;  // the expert's global scales, loaded with its rows
+};
+
+template <int CH>
+__device__ __forceinline__ void gateup_load(const DecodeArgs& a, int e, int row, int l16, GateUpRows<CH>& r) {
+  const int nch = a.H >> 5;
+  const size_t grow = (size_t)e * a.I + row;
+  const uint8_t* gc = a.gate.codes + grow * (a.H / 2);
+  const uint8_t* uc = a.up.codes + grow * (a.H / 2);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(a.gate.scales + grow * (a.H / 16));
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(a.up.scales + grow * (a.H / 16));
+  r.gg = a.gate.global[e];
+  r.gu = a.up.global[e];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int ch = l16 + 16 * c;
     if (ch < nch) {
-      gcode[c] = *reinterpret_cast<const uint4*>(gc + ch * 16);
-      ucode[c] = *reinterpret_cast<const uint4*>(uc + ch * 16);
-      gsc[c] = gs[ch];
-      usc[c] = us[ch];
+      r.gc[c] = *reinterpret_cast<const uint4*>(gc + ch * 16);
+      r.uc[c] = *reinterpret_cast<const uint4*>(uc + ch * 16);
+      r.gs[c] = gs[ch];
+      r.us[c] = us[ch];
     }
   }
-  const float gg = gate.global[e], gu = up.global[e];
-  for (int i = 0; i < np; ++i) {
-    const int p = s_pairs[i];
-    const int t = p / topk;
-    const uint32_t* xr = reinterpret_cast<const uint32_t*>(x + (size_t)t * H);
+}
+
+template <int CH>
+__device__ __forceinline__ void gateup_compute(const DecodeArgs& a, const DecodeSmem& sm, int u, int row, int l16,
+                                               const GateUpRows<CH>& r) {
+  const int nch = a.H >> 5;
+  const float gg = r.gg, gu = r.gu;
+  for (int i = sm.start[u]; i < sm.start[u + 1]; ++i) {
+    const int p = sm.list[i];
+    const int t = p / a.topk;
     float ga = 0.f, ua = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = l16 + 16 * c;
       if (ch < nch) {
         uint32_t xv[16];
-        const uint4* xp = reinterpret_cast<const uint4*>(xr + ch * 16);
+        const uint4* xr = x_lds_chunk(t, a.H, ch);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 v = xp[q];
+          const uint4 v = xr[q];
           xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
         }
-        ga += dot_chunk_bf16(gcode[c], gsc[c], xv);
-        ua += dot_chunk_bf16(ucode[c], usc[c], xv);
+        ga += dot_chunk_bf16(r.gc[c], r.gs[c], xv);
+        ua += dot_chunk_bf16(r.uc[c], r.us[c], xv);
       }
     }
     ga = sum16(ga);
     ua = sum16(ua);
-    if (l16 == 0) h[(size_t)p * I + row] = silu(ga * gg) * (ua * gu);
+    // h goes to memory with an agent-coherent (write-through) store: blocks on other
+    // XCDs read it after the grid barrier without any L2 writeback or invalidation.
+    if (l16 == 0)
+      __hip_atomic_store(a.h + (size_t)p * a.I + row, silu(ga * gg) * (ua * gu), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// ------------------------------------------------------------------ down + combine
-// CH = chunk iterations per lane = ceil(I / 32 / 16). UB experts' rows are loaded
-// before any is used, to keep enough bytes in flight.
-template <int CH, int UB>
-__global__ __launch_bounds__(128) void decode_down_kernel(const float* __restrict__ h, int H, int I,
-                                                          WeightArgs down, int E, const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ w, int P, int topk, int T,
-                                                          void* __restrict__ out, int out_dtype) {
-  __shared__ int s_ids[64], s_uniq[64], s_list[64], s_start[65];
-  __shared__ int s_nu, s_drop;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nu = block_unique_experts(ids, P, E, s_ids, s_uniq, &s_nu, &s_drop);
-  // pairs grouped by unique expert, each group in pair order
-  if (tid < 64) {
-    int start = 0;
-    for (int u = 0; u < nu; ++u) {
-      const bool m = s_ids[tid] == s_uniq[u];
-      const uint64_t mm = __ballot(m);
-      if (m) s_list[start + __popcll(mm & ((1ull << tid) - 1ull))] = tid;
-      if (tid == 0) s_start[u] = start;
-      start += __popcll(mm);
+// All waves of the grid share the phase-1 units, two at a time per wave. The loads of
+// the first two units are issued by the caller (before the gamma loads and the barrier
+// that publishes them).
+template <int CH>
+struct Phase1 {
+  GateUpRows<CH> r0, r1;
+  int j;
+};
+
+template <int CH>
+__device__ __forceinline__ void phase1_issue(const DecodeArgs& a, const DecodeSmem& sm, int j, Phase1<CH>& st) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, rq = lane >> 4;
+  const int quads = a.I >> 2;
+  const int units = sm.nu * quads;
+  const int nw = gridDim.x * kDecWaves;
+  st.j = j;
+  if (j < units) {
+    const int u0 = j / quads;
+    gateup_load<CH>(a, sm.uniq[u0], (j - u0 * quads) * 4 + rq, l16, st.r0);
+  }
+  if (j + nw < units) {
+    const int u1 = (j + nw) / quads;
+    gateup_load<CH>(a, sm.uniq[u1], (j + nw - u1 * quads) * 4 + rq, l16, st.r1);
+  }
+}
+
+template <int CH>
+__device__ void phase1(const DecodeArgs& a, const DecodeSmem& sm, Phase1<CH>& st) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, rq = lane >> 4;
+  const int quads = a.I >> 2;
+  const int units = sm.nu * quads;
+  const int nw = gridDim.x * kDecWaves;
+  for (int j = st.j; j < units; j += 2 * nw) {
+    if (j != st.j) phase1_issue<CH>(a, sm, j, st);
+    const int u0 = j / quads;
+    gateup_compute<CH>(a, sm, u0, (j - u0 * quads) * 4 + rq, l16, st.r0);
+    if (j + nw < units) {
+      const int u1 = (j + nw) / quads;
+      gateup_compute<CH>(a, sm, u1, (j + nw - u1 * quads) * 4 + rq, l16, st.r1);
     }
-    if (tid == 0) s_start[nu] = start;
+  }
+}
+
+// ---- phase 2: wave w owns the row quad (w & 1) of its block and the unique experts
+// (w >> 1) + 4i.
+template <int CH>
+struct DownRows {
+  uint4 c[kUB][CH];
+  uint32_t s[kUB][CH];
+  float gd[kUB];  // global scales of the experts, loaded with their rows
+};
+
+__device__ __forceinline__ int down_expert(int wave, int ub) { return (wave >> 1) + 4 * ub; }
+
+template <int CH>
+__device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
+                                          DownRows<CH>& d) {
+  const int wave = threadIdx.x >> 6;
+  const int nch = a.I >> 5;
+#pragma unroll
+  for (int b = 0; b < kUB; ++b) {
+    const int u = down_expert(wave, ub0 + b);
+    if (u < sm.nu && row < a.H) {
+      d.gd[b] = a.down.global[sm.uniq[u]];
+      const size_t grow = (size_t)sm.uniq[u] * a.H + row;
+      const uint8_t* rc = a.down.codes + grow * (a.I / 2);
+      const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scales + grow * (a.I / 16));
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int ch = l16 + 16 * c;
+        if (ch < nch) {
+          d.c[b][c] = *reinterpret_cast<const uint4*>(rc + ch * 16);
+          d.s[b][c] = rs[ch];
+        }
+      }
+    }
+  }
+}
+
+template <int CH, bool HLDS>
+__device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
+                                           const DownRows<CH>& d, float (&acc)[kDecodeMaxT]) {
+  const int wave = threadIdx.x >> 6;
+  const int nch = a.I >> 5;
+  const int xb = (int)x_lds_bytes(a.T, a.H);
+#pragma unroll
+  for (int b = 0; b < kUB; ++b) {
+    const int u = down_expert(wave, ub0 + b);
+    if (u >= sm.nu) break;
+    const float gd = d.gd[b];
+    for (int i = sm.start[u]; i < sm.start[u + 1]; ++i) {
+      const int p = sm.list[i];
+      const int t = p / a.topk;
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int ch = l16 + 16 * c;
+        if (ch < nch && row < a.H) {
+          const float* hp = HLDS ? h_lds_chunk(xb, p, a.I, ch) : a.h + (size_t)p * a.I + ch * 32;
+          part += dot_chunk_f32(d.c[b][c], d.s[b][c], hp);
+        }
+      }
+      const float coef = sm.wp[p] * gd;
+#pragma unroll
+      for (int tt = 0; tt < kDecodeMaxT; ++tt)
+        if (tt == t) acc[tt] = fmaf(coef, part, acc[tt]);
+    }
+  }
+}
+
+// Grid barrier over gridDim.x co-resident blocks. h was stored write-through (agent
+// scope), so arrival only needs every wave's stores complete (vmcnt 0) before one
+// relaxed atomic per block; readers then load h with agent-coherent loads. The counter
+// only grows: the k-th arrival of a call sees old = base + k with base a multiple of
+// the grid size, so every block of the call waits for base + gridDim.x. Returns false
+// (and sets bit 0 of hdr[1]) if the wait exceeds the spin limit, so every wave exits.
+__device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned long long G = gridDim.x;
+    const unsigned long long old =
+        __hip_atomic_fetch_add(a.barrier, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long target = (old / G + 1) * G;
+    int ok = 1;
+    int n = 0;
+    while (__hip_atomic_load(a.barrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++n > a.spin_limit) {
+        ok = 0;
+        __hip_atomic_fetch_or(a.hdr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    sm.ok = ok;
   }
   __syncthreads();
-  const int row = blockIdx.x * 8 + wave * 4 + (lane >> 4);
+  return sm.ok != 0;
+}
+
+// MODE 0: phase 1 only; MODE 1: phase 2 only; MODE 2: both with the grid barrier.
+template <int MODE, int CHG, int CHD>
+__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem sm;
+  decode_prepare(sm, a, MODE != 1);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && MODE != 1) a.hdr[0] = sm.drop;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15;
-  const int nch = I >> 5;
-  const bool row_ok = row < H;
+  const int row = blockIdx.x * kRowsPerBlock + (wave & 1) * 4 + (lane >> 4);
+  Phase1<CHG> p1;
+  if (MODE != 1) phase1_issue<CHG>(a, sm, blockIdx.x * kDecWaves + wave, p1);
+  DownRows<CHD> d;
+  if (MODE != 0) down_load<CHD>(a, sm, 0, row, l16, d);  // in flight during phase 1 and the wait
+  if (MODE != 1) phase1<CHG>(a, sm, p1);
+  if (MODE == 0) return;
+  if (MODE == 2 && !grid_barrier(a, sm)) return;
+  if (a.h_in_lds) {
+    // agent-coherent 128-bit loads (cache policy sc1) of h into LDS
+    const int n16 = a.P * a.I / 4;  // 16-byte pieces, 8 per 32-value chunk
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc(a.h, 0, (int)((size_t)a.P * a.I * 4), 0x00020000);
+    char* hd = dec_lds + x_lds_bytes(a.T, a.H);
+    for (int i = tid; i < n16; i += kDecThreads)
+      *reinterpret_cast<uint4*>(hd + (i >> 3) * 144 + (i & 7) * 16) =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hr, i * 16, 0, 16));
+    __syncthreads();
+  }
+
   float acc[kDecodeMaxT];
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) acc[t] = 0.f;
-  for (int u0 = 0; u0 < nu; u0 += UB) {
-    uint4 code[UB][CH];
-    uint32_t sc[UB][CH];
-#pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      const int u = u0 + b;
-      if (u < nu && row_ok) {
-        const size_t grow = (size_t)s_uniq[u] * H + row;
-        const uint8_t* rc = down.codes + grow * (I / 2);
-        const uint16_t* rs = reinterpret_cast<const uint16_t*>(down.scales + grow * (I / 16));
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int ch = l16 + 16 * c;
-          if (ch < nch) {
-            code[b][c] = *reinterpret_cast<const uint4*>(rc + ch * 16);
-            sc[b][c] = rs[ch];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      const int u = u0 + b;
-      if (u >= nu) break;
-      const float gd = down.global[s_uniq[u]];
-      for (int i = s_start[u]; i < s_start[u + 1]; ++i) {
-        const int p = s_list[i];
-        const int t = p / topk;
-        const float* hr = h + (size_t)p * I;
-        float part = 0.f;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int ch = l16 + 16 * c;
-          if (ch < nch && row_ok) {
-            const uint32_t wd[4] = {code[b][c].x, code[b][c].y, code[b][c].z, code[b][c].w};
-            const float4* hp = reinterpret_cast<const float4*>(hr + ch * 32);
-            float g2[2] = {0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 ha = hp[2 * q], hb = hp[2 * q + 1];
-              const f32x2_t w0 = e2m1x2_f32<0>(wd[q]), w1 = e2m1x2_f32<1>(wd[q]);
-              const f32x2_t w2 = e2m1x2_f32<2>(wd[q]), w3 = e2m1x2_f32<3>(wd[q]);
-              float s = g2[q >> 1];
-              s = fmaf(w0[0], ha.x, s); s = fmaf(w0[1], ha.y, s);
-              s = fmaf(w1[0], ha.z, s); s = fmaf(w1[1], ha.w, s);
-              s = fmaf(w2[0], hb.x, s); s = fmaf(w2[1], hb.y, s);
-              s = fmaf(w3[0], hb.z, s); s = fmaf(w3[1], hb.w, s);
-              g2[q >> 1] = s;
-            }
-            part += g2[0] * e4m3_f32<0>(sc[b][c]) + g2[1] * e4m3_f32<1>(sc[b][c]);
-          }
-        }
-        const float coef = w[p] * gd;
-#pragma unroll
-        for (int tt = 0; tt < kDecodeMaxT; ++tt)
-          if (tt == t) acc[tt] = fmaf(coef, part, acc[tt]);
-      }
-    }
+  const int per_wave = (sm.nu - (wave >> 1) + 3) / 4;  // experts of this wave
+  for (int ub0 = 0; ub0 < per_wave; ub0 += kUB) {
+    if (ub0 > 0) down_load<CHD>(a, sm, ub0, row, l16, d);
+    if (a.h_in_lds) down_accum<CHD, true>(a, sm, ub0, row, l16, d, acc);
+    else down_accum<CHD, false>(a, sm, ub0, row, l16, d, acc);
   }
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) {
-    if (t >= T) break;
     const float v = sum16(acc[t]);
-    if (l16 == 0 && row_ok) {
-      if (out_dtype == 0) reinterpret_cast<float*>(out)[(size_t)t * H + row] = v;
-      else reinterpret_cast<uint16_t*>(out)[(size_t)t * H + row] = f32_to_bf16_bits(v);
+    if (l16 == 0) sm.part[wave][lane >> 4][t] = v;
+  }
+  __syncthreads();
+  if (tid < kRowsPerBlock * a.T) {
+    const int q8 = tid & 7, t = tid >> 3;  // row within the block, token
+    const int rq = q8 >> 2, q = q8 & 3;
+    const float v = ((sm.part[rq][q][t] + sm.part[rq + 2][q][t]) + sm.part[rq + 4][q][t]) + sm.part[rq + 6][q][t];
+    const int r = blockIdx.x * kRowsPerBlock + q8;
+    if (r < a.H) {
+      if (a.out_dtype == 0) reinterpret_cast<float*>(a.out)[(size_t)t * a.H + r] = v;
+      else reinterpret_cast<uint16_t*>(a.out)[(size_t)t * a.H + r] = f32_to_bf16_bits(v);
     }
   }
 }
 
-template <int CHG, int CHD>
-static hipError_t launch_decode_t(int stage, const void* x, int T, int H, int I, const WeightArgs& gate,
-                                  const WeightArgs& up, const WeightArgs& down, int E, const int32_t* ids,
-                                  const float* w, int topk, void* out, int out_dtype, float* h, int32_t* hdr,
-                                  hipStream_t st) {
-  const int P = T * topk;
-  if (stage == 0) {
-    dim3 g1((I + 15) / 16, P);
-    decode_gateup_kernel<CHG><<<g1, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), H, I, gate, up, E, ids, P,
-                                                  topk, h, hdr);
-  } else {
-    dim3 g2((H + 7) / 8);
-    decode_down_kernel<CHD, 8><<<g2, 128, 0, st>>>(h, H, I, down, E, ids, w, P, topk, T, out, out_dtype);
-  }
+// Dynamic LDS budget of one block (of the 160 KiB per CU, the rest is static LDS).
+constexpr size_t kDecLdsBudget = 152 * 1024;
+
+static size_t decode_lds_bytes(const DecodeArgs& a) {
+  return x_lds_bytes(a.T, a.H) + (a.h_in_lds ? h_lds_bytes(a.P, a.I) : 0);
+}
+
+template <int MODE, int CHG, int CHD>
+static hipError_t launch_mode(const DecodeArgs& a, hipStream_t st) {
+  const size_t lds = decode_lds_bytes(a);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<MODE, CHG, CHD>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((a.H + kRowsPerBlock - 1) / kRowsPerBlock);
+  decode_kernel<MODE, CHG, CHD><<<grid, kDecThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate,
-                         const WeightArgs& up, const WeightArgs& down, int E, const int32_t* ids, const float* w,
-                         int topk, void* out, int out_dtype, float* h, int32_t* hdr, hipStream_t st) {
+// The fused form needs every block of its grid resident at once.
+template <int CHG, int CHD>
+static bool fused_fits(const DecodeArgs& a) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<2, CHG, CHD>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes(a)) != hipSuccess)
+    return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<2, CHG, CHD>, kDecThreads,
+                                                   decode_lds_bytes(a)) != hipSuccess)
+    return false;
+  return (long long)((a.H + kRowsPerBlock - 1) / kRowsPerBlock) <= (long long)cus * per_cu;
+}
+
+template <int CHG, int CHD>
+static hipError_t launch_decode_t(int stage, const DecodeArgs& a, hipStream_t st) {
+  if (stage == 0) return launch_mode<0, CHG, CHD>(a, st);
+  if (stage == 1) return launch_mode<1, CHG, CHD>(a, st);
+  // fused only when h fits in LDS: phase 2 then reads h once, with agent-coherent loads
+  if (a.h_in_lds && fused_fits<CHG, CHD>(a)) return launch_mode<2, CHG, CHD>(a, st);
+  const hipError_t e = launch_mode<0, CHG, CHD>(a, st);
+  return e != hipSuccess ? e : launch_mode<1, CHG, CHD>(a, st);
+}
+
+hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
+                         const WeightArgs& down, int E, const int32_t* ids, const float* w, int topk, void* out,
+                         int out_dtype, float* h, int32_t* hdr, hipStream_t st) {
+  DecodeArgs a;
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.T = T; a.H = H; a.I = I; a.E = E; a.P = T * topk; a.topk = topk;
+  a.gate = gate; a.up = up; a.down = down;
+  a.ids = ids; a.w = w; a.h = h; a.out = out; a.out_dtype = out_dtype;
+  a.hdr = hdr;
+  a.barrier = reinterpret_cast<unsigned long long*>(hdr + 4);
+  a.spin_limit = 1 << 22;
+  a.h_in_lds = 0;
+  a.h_in_lds = decode_lds_bytes(a) + h_lds_bytes(a.P, I) <= kDecLdsBudget ? 1 : 0;
   const int chg = ((H >> 5) + 15) / 16;  // 1..16 for H <= 8192
   const int chd = ((I >> 5) + 15) / 16;
-#define NVFP4_DEC(G, D)                                                                                          \
-  if (chg <= G && chd <= D)                                                                                      \
-    return launch_decode_t<G, D>(stage, x, T, H, I, gate, up, down, E, ids, w, topk, out, out_dtype, h, hdr, st);
+#define NVFP4_DEC(G, D) \
+  if (chg <= G && chd <= D) return launch_decode_t<G, D>(stage, a, st);
   NVFP4_DEC(1, 1)
   NVFP4_DEC(2, 1)
   NVFP4_DEC(2, 2)

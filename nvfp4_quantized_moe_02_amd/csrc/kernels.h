@@ -45,7 +45,10 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, 
 // decode.hip
 constexpr int kDecodeMaxT = 8;
 constexpr int kDecodeMaxPairs = 64;
-// stage 0: gate/up + SwiGLU; stage 1: down + combine
+constexpr int kDecodeMaxTH = 40960;  // T * H: the bf16 activations of a block live in LDS
+// stage 0: gate/up + SwiGLU; 1: down + combine; 2: both in one persistent launch (falls
+// back to 0 then 1 when the grid cannot be co-resident). hdr: [0] dropped pairs,
+// [1] error flags, [4..5] the grid-barrier counter (zero before first use).
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
                          const WeightArgs& down, int E, const int32_t* ids, const float* w, int topk,
                          void* out, int out_dtype, float* h, int32_t* hdr, hipStream_t st);

@@ -327,12 +327,13 @@ def test_decode_stages_equal_full_call():
     lay, dl, x, ids, w = _small_problem(T=4)
     out_full = torch.empty((4, dl.H), dtype=torch.float32, device=DEV)
     out_st = torch.empty_like(out_full)
-    ws = torch.empty(nv.decode_workspace_size(4, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nv.decode_workspace_size(4, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
     nv.PreparedCall("decode", x, dl, ids, w, out_full, ws).run()
     c = nv.PreparedCall("decode", x, dl, ids, w, out_st, ws)
     c.stage(0)
     c.stage(1)
-    assert torch.equal(out_full, out_st)
+    assert torch.equal(out_full, out_st)  # one persistent launch == two launches, bit for bit
+    assert int(ws[4:8].view(torch.int32).item()) == 0  # no grid-barrier timeout
 
 
 @pytest.mark.parametrize("kind", ["decode", "prefill"])
@@ -343,7 +344,7 @@ def test_graph_replays_match_eager(kind):
     lay, dl, x, ids, w = _small_problem(T=T)
     out = torch.empty((T, dl.H), dtype=torch.float32, device=DEV)
     if kind == "decode":
-        ws = torch.empty(nv.decode_workspace_size(T, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(nv.decode_workspace_size(T, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
     else:
         ws = torch.empty(nv.prefill_workspace_size(T, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
     call = nv.PreparedCall(kind, x, dl, ids, w, out, ws)
@@ -356,7 +357,10 @@ def test_graph_replays_match_eager(kind):
         call.run()
     for rep in range(4):
         out.fill_(float("nan"))
-        ws.fill_(0xA5)
+        if kind == "prefill":
+            ws.fill_(0xA5)  # every prefill call rewrites its whole workspace
+        else:
+            ws[64:].fill_(0xA5)  # decode keeps its grid-barrier counter in the header
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
