@@ -147,9 +147,8 @@ int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const
  * in fp32, rounded once). `act` selects the activation handling (nvfp4_act).
  * ws needs nvfp4_moe_prefill_workspace_size() bytes. ("Strata NVFP4" README: prompt
  * chunks up to 32K tokens, where every chunk streams every layer's experts once.)
- * The down projection adds each pair's contribution into the fp32 accumulator with
- * atomic adds, so the summation order of the (at most topk) terms of an output element
- * can differ between runs. T == 0 is a no-op and may pass null tensors.
+ * Each pair's down output is kept in fp32 and the slots of a token are summed in slot
+ * order, so the result is deterministic. T == 0 is a no-op and may pass null tensors.
  * Errors: EINVAL (null pointers, shapes that disagree, unknown act, out_dtype F16);
  * EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128, E > 8192, x_dtype
  * other than BF16; EWORKSPACE. */
@@ -166,7 +165,7 @@ int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
  * Decode stages: 0 gate/up + SwiGLU (h into the workspace), 1 down + combine.
  * Prefill stages: 0 zero the accumulator, route, stage the activations (fp16, or int8
  * codes and row scales for W4A8); 1 gate/up + SwiGLU (W4A8: then requantize h);
- * 2 down + weighted combine; 3 final rounding to the output dtype.
+ * 2 down, scaled per pair; 3 top-k combine in slot order and the final rounding.
  * Errors: those of the full call, and EINVAL for a stage outside that range. */
 int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,
                            const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down,

@@ -31,7 +31,7 @@ struct Carver {
 };
 
 struct RouteLayout {
-  size_t hdr, counts, dropped, offsets, sorted, tiles, end;
+  size_t hdr, counts, dropped, offsets, sorted, tiles, inv, end;
   int nblk, max_tiles;
 };
 
@@ -45,13 +45,14 @@ RouteLayout route_layout(int64_t P, int E, bool with_tiles, Carver& c) {
   l.offsets = c.take((size_t)(E + 1) * 4);
   l.sorted = c.take((size_t)P * 4);
   l.tiles = c.take((size_t)l.max_tiles * sizeof(TileDesc));
+  l.inv = c.take(with_tiles ? (size_t)P * 4 : 0);
   l.end = c.off;
   return l;
 }
 
 struct PrefillLayout {
   RouteLayout r;
-  size_t a16, sx, h, qh16, sh, acc, end;
+  size_t a16, sx, h, qh16, sh, y, end;
 };
 
 PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
@@ -65,7 +66,7 @@ PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
   l.h = c.take((size_t)P * I * (w4a8 ? 4 : 2));
   l.qh16 = c.take(w4a8 ? (size_t)P * I * 2 : 0);
   l.sh = c.take(w4a8 ? (size_t)P * 4 : 0);
-  l.acc = c.take((size_t)T * H * 4);
+  l.y = c.take((size_t)P * H * 4);
   l.end = c.off;
   return l;
 }
@@ -138,7 +139,7 @@ int nvfp4_moe_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
   Carver c;
   const RouteLayout l = route_layout((int64_t)T * topk, E, false, c);
   if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
-  RouteWs rw{at<int32_t>(ws, l.counts), at<int32_t>(ws, l.dropped), at<int32_t>(ws, l.hdr), nullptr};
+  RouteWs rw{at<int32_t>(ws, l.counts), at<int32_t>(ws, l.dropped), at<int32_t>(ws, l.hdr), nullptr, nullptr};
   (void)hipGetLastError();
   return hip_status(
       launch_route(topk_ids, (int64_t)T * topk, E, expert_offsets, sorted_pairs, rw, kTileM, as_stream(stream)));
@@ -237,7 +238,7 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const int64_t P = (int64_t)T * topk;
-  float* acc = out_dtype == NVFP4_F32 ? reinterpret_cast<float*>(out) : at<float>(ws, l.acc);
+  float* y = at<float>(ws, l.y);
   int32_t* offsets = at<int32_t>(ws, l.r.offsets);
   int32_t* sorted = at<int32_t>(ws, l.r.sorted);
   int32_t* hdr = at<int32_t>(ws, l.r.hdr);
@@ -248,12 +249,9 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   const int mode = act == NVFP4_ACT_BF16 ? 0 : 1;
   for (int stage = first; stage <= last; ++stage) {
     hipError_t e = hipSuccess;
-    if (stage == 0) {  // zero the accumulator, route, stage the activations
-      e = launch_zero(acc, (int64_t)T * H * 4, s);
-      if (e == hipSuccess) {
-        RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles};
-        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
-      }
+    if (stage == 0) {  // route, stage the activations
+      RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles, at<int32_t>(ws, l.r.inv)};
+      e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
       if (e == hipSuccess) {
         if (act == NVFP4_ACT_BF16) e = launch_bf16_to_f16(x, a16, (int64_t)T * H, s);
         else e = launch_quant_rows(x, NVFP4_BF16, T, H, a16, 1, sx, s);
@@ -263,12 +261,12 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
                              to_args(gate), to_args(up), at<void>(ws, l.h), s);
       if (e == hipSuccess && mode == 1)
         e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<void>(ws, l.qh16), 1, sh, s);
-    } else if (stage == 2) {  // down + weighted combine into the fp32 accumulator
+    } else if (stage == 2) {  // down, scaled by gamma_d and the router weight, per pair
       const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh16);
       e = launch_gemm_down(mode, hA, sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
-                           to_args(down), topk_weights, acc, s);
-    } else if (out_dtype == NVFP4_BF16) {  // one rounding of the accumulator
-      e = launch_finalize_bf16(acc, out, (int64_t)T * H, s);
+                           to_args(down), topk_weights, y, s);
+    } else {  // top-k combine in slot order, one rounding to the output dtype
+      e = launch_combine(y, at<int32_t>(ws, l.r.inv), T, topk, H, out, out_dtype, s);
     }
     if (e != hipSuccess) return NVFP4_EHIP;
   }

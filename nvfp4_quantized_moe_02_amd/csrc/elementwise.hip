@@ -236,4 +236,39 @@ hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStrea
   return hipGetLastError();
 }
 
+// Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic.
+template <int OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y, const int32_t* __restrict__ inv,
+                                                      int T, int topk, int H4, void* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * H4) return;
+  const int t = (int)(i / H4), c = (int)(i - (int64_t)t * H4);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < topk; ++j) {
+    const int pos = inv[(size_t)t * topk + j];
+    if (pos < 0) continue;
+    const float4 v = y[(size_t)pos * H4 + c];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (OUT == 0) {
+    reinterpret_cast<float4*>(out)[i] = s;
+  } else {
+    reinterpret_cast<uint2*>(out)[i] =
+        make_uint2((uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16),
+                   (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16));
+  }
+}
+
+hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, int H, void* out, int out_dtype,
+                          hipStream_t st) {
+  const int64_t n = (int64_t)T * (H / 4);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (out_dtype == 0)
+    combine_kernel<0><<<grid, 256, 0, st>>>(reinterpret_cast<const float4*>(y), inv, T, topk, H / 4, out);
+  else
+    combine_kernel<1><<<grid, 256, 0, st>>>(reinterpret_cast<const float4*>(y), inv, T, topk, H / 4, out);
+  return hipGetLastError();
+}
+
 }  // namespace nvfp4

@@ -28,6 +28,9 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols,
 hipError_t launch_bf16_to_f16(const void* x, void* y, int64_t n, hipStream_t st);
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st);
+// out[t][n] = sum over slots j (in order) of y[inv[t*topk + j]][n]; dropped slots skipped.
+hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, int H, void* out, int out_dtype,
+                          hipStream_t st);
 
 // route.hip
 constexpr int kRouteChunk = 4096;  // pairs per counting block
@@ -37,6 +40,7 @@ struct RouteWs {
   int32_t* dropped;   // [nblk]
   int32_t* hdr;       // hdr[0] = dropped pairs, hdr[1] = tile count
   TileDesc* tiles;    // [max_tiles] (optional)
+  int32_t* inv;       // [P] sorted position of each pair, -1 if dropped (optional)
 };
 int route_blocks(int64_t P);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
@@ -59,9 +63,10 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
                               const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
                               int max_tiles, int topk, int H, int I, const WeightArgs& gate,
                               const WeightArgs& up, void* h, hipStream_t st);
+// y[pos][n] = gamma_down * w[pair] * (h[pos] . Wdown[n]) for every sorted position pos
 hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* sorted_pairs,
                             const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
                             int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
-                            float* out_acc, hipStream_t st);
+                            float* y, hipStream_t st);
 
 }  // namespace nvfp4

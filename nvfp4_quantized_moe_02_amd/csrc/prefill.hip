@@ -25,7 +25,8 @@
 // gate/up: wave w computes gate and up for the same 32 intermediate indices, so SwiGLU
 // runs in registers: h = SiLU(gamma_g * g) * (gamma_u * u) (gate scale before SiLU, the
 // "Strata NVFP4" README's per-projection output scale). down: the epilogue multiplies by
-// gamma_d and the router weight and adds into an fp32 [T][H] accumulator.
+// gamma_d and the router weight and writes each pair's fp32 row; a separate combine sums
+// the slots of each token in slot order, so the result is deterministic.
 #include <type_traits>
 
 #include "kernels.h"
@@ -77,6 +78,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
                                           const WeightArgs& w0, const WeightArgs& w1, void* __restrict__ out,
                                           int ldo, char* lds, const int* s_src, const int* s_tok,
                                           const float* s_coef) {
+  (void)s_tok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nkb = K / KBLK;
@@ -159,25 +161,48 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 
   if (GATEUP) {
     const float gg = w0.global[tc.e], gu = w1.global[tc.e];
-    const int jcol = tc.nb * 128 + wave * 32 + l32;
+    if (!HOUT32) {
+      // fp16 h through LDS: [rows][128 intermediate indices], 16-byte chunks XOR-swizzled by
+      // row; then every thread stores whole 16-byte chunks (256 contiguous bytes per row).
+      __syncthreads();  // every wave is done with the A stages
+      uint16_t* hl = reinterpret_cast<uint16_t*>(lds);
+      const int col = wave * 32 + l32;
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+      for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        if (r < tc.rows) {
+        for (int i = 0; i < 16; ++i) {
+          const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
           const float xs = s_coef[r];
-          const float g = acc[rb][0][i] * (xs * gg);
-          const float u = acc[rb][1][i] * (xs * gu);
-          const float hv = silu_fast(g) * u;
-          const size_t o = (size_t)(tc.base + tc.m0 + r) * ldo + jcol;
-          if (HOUT32) reinterpret_cast<float*>(out)[o] = hv;
-          else reinterpret_cast<uint16_t*>(out)[o] = f32_to_f16_bits(hv);
+          const float hv = silu_fast(acc[rb][0][i] * (xs * gg)) * (acc[rb][1][i] * (xs * gu));
+          hl[r * 128 + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f32_to_f16_bits(hv);
         }
+      __syncthreads();
+      uint16_t* h = reinterpret_cast<uint16_t*>(out);
+      for (int k = tid; k < NRB * 32 * 16; k += 256) {
+        const int r = k >> 4, c = k & 15;
+        if (r < tc.rows)
+          *reinterpret_cast<uint4*>(h + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * 128 + c * 8) =
+              *reinterpret_cast<const uint4*>(hl + r * 128 + ((c ^ (r & 15)) << 3));
       }
+    } else {
+      const int jcol = tc.nb * 128 + wave * 32 + l32;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (r < tc.rows) {
+            const float xs = s_coef[r];
+            const float hv = silu_fast(acc[rb][0][i] * (xs * gg)) * (acc[rb][1][i] * (xs * gu));
+            reinterpret_cast<float*>(out)[(size_t)(tc.base + tc.m0 + r) * ldo + jcol] = hv;
+          }
+        }
+    }
   } else {
+    // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order (lanes 0..31 of a row
+    // write 128 contiguous bytes); the combine kernel sums each token's slots.
     const float gd = w0.global[tc.e];
-    float* o = reinterpret_cast<float*>(out);
+    float* y = reinterpret_cast<float*>(out);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -185,9 +210,9 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
         const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
         if (r < tc.rows) {
           const float c = s_coef[r] * gd;
-          float* orow = o + (size_t)s_tok[r] * ldo + tc.nb * 256 + wave * 64 + l32;
-          unsafeAtomicAdd(orow, acc[rb][0][i] * c);
-          unsafeAtomicAdd(orow + 32, acc[rb][1][i] * c);
+          float* yrow = y + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * 256 + wave * 64 + l32;
+          yrow[0] = acc[rb][0][i] * c;
+          yrow[32] = acc[rb][1][i] * c;
         }
       }
   }
@@ -295,7 +320,7 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
 hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* sorted_pairs,
                             const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
                             int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
-                            float* out_acc, hipStream_t st) {
+                            float* y, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
   const int NB = H / 256;
   const dim3 grid(grid_for(max_tiles, NB));
@@ -303,11 +328,11 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
   if (act == 0)
     moe_gemm_f16_kernel<false, false, false><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles,
                                                                    tile_count, topk, I, NB, down, down, w,
-                                                                   out_acc, H);
+                                                                   y, H);
   else
     moe_gemm_f16_kernel<false, true, false><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles,
                                                                   tile_count, topk, I, NB, down, down, w,
-                                                                  out_acc, H);
+                                                                  y, H);
   return hipGetLastError();
 }
 

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int E, int nblk, int64
 // bits), so the scatter is stable.
 __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
                                                            int nblk, const int32_t* __restrict__ bases,
-                                                           int32_t* __restrict__ sorted_pairs) {
+                                                           int32_t* __restrict__ sorted_pairs,
+                                                           int32_t* __restrict__ inv) {
   extern __shared__ int32_t run[];
   const int b = blockIdx.x, lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) run[e] = bases[(size_t)e * nblk + b];
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       sorted_pairs[pos] = (int32_t)p;
       if ((m >> lane) == 1ull) run[e] += __popcll(m);
     }
+    if (inv != nullptr && p < p1) inv[p] = valid ? pos : -1;  // sorted position of pair p
     __syncthreads();
   }
 }
@@ -151,7 +153,7 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nblk > 0) {
-    route_scatter_kernel<<<nblk, 64, lds, st>>>(ids, P, E, nblk, ws.counts, sorted_pairs);
+    route_scatter_kernel<<<nblk, 64, lds, st>>>(ids, P, E, nblk, ws.counts, sorted_pairs, ws.inv);
     e = hipGetLastError();
   }
   return e;
