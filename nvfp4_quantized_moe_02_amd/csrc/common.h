@@ -47,40 +47,28 @@ __device__ __forceinline__ bf16x2_t e2m1x2_bf16(uint32_t word) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
 }
 
-// A scale split for the fp16 unpack: the E2M1 convert applies 2^exponent(s); the
-// remaining factor sign(s) * 1.mmm (at most 4 significant bits, exact in fp16) is
-// applied with one packed fp16 multiply. e2m1 * e4m3 is exact in fp16 (at most 5
-// significant bits, magnitudes 2^-10 .. 2688), so the product of the two steps is
-// the exact dequantized weight. A NaN scale gives a NaN factor, so NaN propagates.
-struct F16Scale {
-  float expo;     // passed to the convert; only its exponent field matters
-  f16x2_t mant;   // (m, m)
-};
-
-__device__ __forceinline__ F16Scale f16_scale(float s) {
-  uint32_t b = __float_as_uint(s);
-  float m = __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
-  if ((b & 0x7F800000u) == 0x7F800000u) m = __uint_as_float(0x7FC00000u);
-  F16Scale r;
-  r.expo = s;
-  _Float16 mh = (_Float16)m;
-  r.mant = f16x2_t{mh, mh};
-  return r;
+// Two E4M3 scale bytes (bytes 2*HI and 2*HI+1 of `word`) as fp16. Every E4M3 value,
+// subnormals and NaN included, is an fp16 value, so the convert is exact.
+template <bool HI>
+__device__ __forceinline__ f16x2_t e4m3x2_f16(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, HI);
 }
 
-// Byte SEL of `word` -> two exact fp16 weights e2m1 * scale.
+// Byte SEL of `word` -> two weights e2m1 * s in fp16. The E2M1 convert is exact; the
+// product has at most 5 significant bits (1 from the code, 4 from the scale) and
+// magnitude 2^-10 .. 2688, so the fp16 multiply is exact too. A NaN scale gives NaN.
 template <int SEL>
-__device__ __forceinline__ f16x2_t e2m1x2_f16_scaled(uint32_t word, const F16Scale& sc) {
-  f16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, sc.expo, SEL);
-  return v * sc.mant;
+__device__ __forceinline__ f16x2_t e2m1x2_f16_scaled(uint32_t word, _Float16 s) {
+  const f16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, SEL);
+  return v * f16x2_t{s, s};
 }
 
 // Four bytes (8 codes) -> 8 exact fp16 weights, element order = k order.
-__device__ __forceinline__ void unpack8_f16(uint32_t word, const F16Scale& sc, f16x2_t out[4]) {
-  out[0] = e2m1x2_f16_scaled<0>(word, sc);
-  out[1] = e2m1x2_f16_scaled<1>(word, sc);
-  out[2] = e2m1x2_f16_scaled<2>(word, sc);
-  out[3] = e2m1x2_f16_scaled<3>(word, sc);
+__device__ __forceinline__ void unpack8_f16(uint32_t word, _Float16 s, f16x2_t out[4]) {
+  out[0] = e2m1x2_f16_scaled<0>(word, s);
+  out[1] = e2m1x2_f16_scaled<1>(word, s);
+  out[2] = e2m1x2_f16_scaled<2>(word, s);
+  out[3] = e2m1x2_f16_scaled<3>(word, s);
 }
 
 // ---------------------------------------------------------------- bf16 helpers

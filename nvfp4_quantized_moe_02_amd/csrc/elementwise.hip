@@ -8,8 +8,8 @@ namespace nvfp4 {
 // One thread per 16-input group: 8 code bytes + 1 scale byte -> 16 outputs.
 // F32: e2m1 (exact) * e4m3 (exact product) * global: one rounding.
 // BF16 / F16 with a global: that fp32 value rounded once more. F16 without a global:
-// the same unpack the prefill GEMMs feed to the matrix cores (exponent-scaled convert
-// times the scale's mantissa factor), so this output checks that unpack bit for bit.
+// the same unpack the prefill GEMMs feed to the matrix cores (fp16 code times fp16
+// scale), so this output checks that unpack bit for bit.
 template <int OUT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const bool has_g = global != nullptr;
   const float gam = has_g ? global[0] : 1.0f;
   if (OUT == 2 && !has_g) {
-    const F16Scale sc = f16_scale(s);
+    const _Float16 sc = e4m3x2_f16<false>(sb)[0];
     f16x2_t o[8];
     unpack8_f16(cw.x, sc, o);
     unpack8_f16(cw.y, sc, o + 4);

@@ -14,11 +14,11 @@
 // c ^ (r & 7), so the 32 rows of an MFMA fragment read hit 8 distinct slots (no bank
 // conflicts). Rows are gathered by token for gate/up and contiguous for down.
 //
-// B operand (NVFP4 weights): each lane loads the 16 code bytes and 2 scale bytes its
-// fragment needs (two K-blocks ahead, in registers) and unpacks them exactly to
-// fp16: the E2M1 convert applies 2^exponent(scale), one packed fp16 multiply applies the
-// scale's mantissa factor (e2m1 * e4m3 has at most 5 significant bits). Weight bytes
-// never pass through LDS and are decoded once per wave. Within a K-block the reduction
+// B operand (NVFP4 weights): each lane loads the 16 code bytes its fragment needs (two
+// K-blocks ahead, in registers) and its column's scale bytes for four K-blocks at once,
+// and unpacks them exactly to fp16: E2M1 codes and the E4M3 scale both convert exactly
+// to fp16, and their product (at most 5 significant bits) is exact in one packed fp16
+// multiply. Weight bytes never pass through LDS and are decoded once per wave. Within a K-block the reduction
 // order of the 64 inputs is permuted (lane half 0 takes inputs 0..31, half 1 inputs
 // 32..63); A is read with the same permutation, so the dot products are unchanged.
 //
@@ -38,25 +38,13 @@ constexpr int KBLK = 64;                        // inputs per K-block
 constexpr int NSTAGE = 2;                       // LDS stages of A
 constexpr int STAGE_BYTES = BM * KBLK * 2;      // 16 KiB per stage
 
-struct BRaw {
-  uint4 c;     // 32 codes
-  uint32_t s;  // 2 scale bytes (the two groups of this lane's 32 inputs)
-};
-
-__device__ __forceinline__ BRaw load_braw(const uint8_t* pc, const uint8_t* ps) {
-  BRaw r;
-  r.c = *reinterpret_cast<const uint4*>(pc);
-  r.s = *reinterpret_cast<const uint16_t*>(ps);
-  return r;
-}
-
 __device__ __forceinline__ uint32_t word_of(const uint4& c, int s) {
   return s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
 }
 
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f16x8_t bfrag(uint32_t word, const F16Scale& sc) {
+__device__ __forceinline__ f16x8_t bfrag(uint32_t word, _Float16 sc) {
   f16x2_t o[4];
   unpack8_f16(word, sc, o);
   const f16x4_t lo = __builtin_shufflevector(o[0], o[1], 0, 1, 2, 3);
@@ -72,7 +60,21 @@ struct TileCtx {
   int e, m0, rows, base, nb;
 };
 
-template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB>
+// Scale bytes are loaded KQ K-blocks at a time (4 * KQ bytes of one column's scale row
+// per lane, 16-byte aligned for KQ = 4 when K is a multiple of 256, 8-byte for KQ = 2);
+// one byte permute per two K-blocks keeps the two bytes of each K-block this lane uses.
+template <int KQ>
+struct ScaleRaw;
+template <>
+struct ScaleRaw<4> {
+  typedef uint4 type;
+};
+template <>
+struct ScaleRaw<2> {
+  typedef uint2 type;
+};
+
+template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ>
 __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
                                           const uint8_t* const* bc, const uint8_t* const* bs,
                                           const WeightArgs& w0, const WeightArgs& w1, void* __restrict__ out,
@@ -93,11 +95,27 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 
   const uint8_t* pc0 = bc[0] + half * 16;
   const uint8_t* pc1 = bc[1] + half * 16;
-  const uint8_t* ps0 = bs[0] + half * 2;
-  const uint8_t* ps1 = bs[1] + half * 2;
-  auto load_b = [&](int kb, int cb) -> BRaw {
+  auto load_b = [&](int kb, int cb) -> uint4 {
     const int kc = kb < nkb ? kb : nkb - 1;  // past the end: refetch the last block (never used)
-    return cb == 0 ? load_braw(pc0 + kc * 32, ps0 + kc * 4) : load_braw(pc1 + kc * 32, ps1 + kc * 4);
+    return *reinterpret_cast<const uint4*>((cb == 0 ? pc0 : pc1) + kc * 32);
+  };
+  // Scales: K-block kb of a column holds 4 bytes (groups 4kb .. 4kb+3); lane half h uses
+  // bytes 2h and 2h+1. A group of KQ K-blocks is one load per column.
+  typedef typename ScaleRaw<KQ>::type SRaw;
+  const int ngrp = nkb / KQ;
+  auto load_s = [&](int j, int cb) -> SRaw {
+    const int jc = j < ngrp ? j : ngrp - 1;
+    return *reinterpret_cast<const SRaw*>(bs[cb] + jc * (4 * KQ));
+  };
+  const uint32_t psel = half ? 0x07060302u : 0x05040100u;
+  // compact word c holds, for K-blocks 2c and 2c+1 of the group, this lane's two bytes each
+  auto compact = [&](const SRaw& r, uint32_t* c) {
+    if constexpr (KQ == 4) {
+      c[0] = __builtin_amdgcn_perm(r.y, r.x, psel);
+      c[1] = __builtin_amdgcn_perm(r.w, r.z, psel);
+    } else {
+      c[0] = __builtin_amdgcn_perm(r.y, r.x, psel);
+    }
   };
   auto load_a = [&](int kb, int i) -> uint4 {
     const int kc = kb < nkb ? kb : nkb - 1;
@@ -112,10 +130,12 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] = 0.f;
 
-  // Two K-blocks of A (registers) and B (registers) in flight. Iteration kb: store
+  // Two K-blocks of A (registers) and B codes (registers) in flight. Iteration kb: store
   // A(kb) into LDS stage kb & 1, barrier, issue A(kb+2) and B(kb+2), compute K-block kb.
+  // Scales run one group of KQ K-blocks ahead.
   uint4 aq[2][NRB];
-  BRaw bq[2][2];
+  uint4 bq[2][2];
+  SRaw sq[2] = {load_s(0, 0), load_s(0, 1)};
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
 #pragma unroll
@@ -123,9 +143,11 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     bq[d][0] = load_b(d, 0);
     bq[d][1] = load_b(d, 1);
   }
+  uint32_t sc0[KQ / 2], sc1[KQ / 2];
 
-  auto kstep = [&](auto ring, int kb) {
-    constexpr int R = decltype(ring)::value;
+  auto kstep = [&](auto qpos, int kb) {
+    constexpr int Q = decltype(qpos)::value;  // position in the scale group
+    constexpr int R = Q & 1;                  // LDS stage / register ring slot
     char* st = lds + R * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < NRB; ++i) *reinterpret_cast<uint4*>(st + (arow + 32 * i) * 128 + aslot) = aq[R][i];
@@ -134,15 +156,15 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NRB; ++i) aq[R][i] = load_a(kb + 2, i);
-    const BRaw cur0 = bq[R][0], cur1 = bq[R][1];
+    const uint4 cur0 = bq[R][0], cur1 = bq[R][1];
     bq[R][0] = load_b(kb + 2, 0);
     bq[R][1] = load_b(kb + 2, 1);
-    const F16Scale sc00 = f16_scale(e4m3_f32<0>(cur0.s)), sc01 = f16_scale(e4m3_f32<1>(cur0.s));
-    const F16Scale sc10 = f16_scale(e4m3_f32<0>(cur1.s)), sc11 = f16_scale(e4m3_f32<1>(cur1.s));
+    const f16x2_t s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
+    const f16x2_t s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8_t b0 = bfrag(word_of(cur0.c, s), s < 2 ? sc00 : sc01);
-      const f16x8_t b1 = bfrag(word_of(cur1.c, s), s < 2 ? sc10 : sc11);
+      const f16x8_t b0 = bfrag(word_of(cur0, s), s0[s >> 1]);
+      const f16x8_t b1 = bfrag(word_of(cur1, s), s1[s >> 1]);
       const int chunk = half * 4 + s;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
@@ -153,10 +175,19 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
       }
     }
   };
-  // nkb is even (K is a multiple of 128)
-  for (int kb = 0; kb < nkb; kb += 2) {
+  // nkb is a multiple of KQ
+  for (int j = 0; j < ngrp; ++j) {
+    compact(sq[0], sc0);
+    compact(sq[1], sc1);
+    sq[0] = load_s(j + 1, 0);
+    sq[1] = load_s(j + 1, 1);
+    const int kb = j * KQ;
     kstep(std::integral_constant<int, 0>{}, kb);
     kstep(std::integral_constant<int, 1>{}, kb + 1);
+    if constexpr (KQ == 4) {
+      kstep(std::integral_constant<int, 2>{}, kb + 2);
+      kstep(std::integral_constant<int, 3>{}, kb + 3);
+    }
   }
 
   if (GATEUP) {
@@ -221,7 +252,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
 // ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
 // HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
-template <bool GATEUP, bool ASCALE, bool HOUT32>
+template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ>
 __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ sorted_pairs,
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
@@ -286,13 +317,13 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
 
   const int nrb = (tc.rows + 31) >> 5;
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -308,12 +339,13 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
   const int NB = I / 128;
   const dim3 grid(grid_for(max_tiles, NB));
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a);
+  // H is a multiple of 256: scale groups of 4 K-blocks
   if (act == 0)
-    moe_gemm_f16_kernel<true, false, false><<<grid, 256, 0, st>>>(A, a_scale, sorted_pairs, offsets, tiles,
-                                                                  tile_count, topk, H, NB, gate, up, nullptr, h, I);
+    moe_gemm_f16_kernel<true, false, false, 4><<<grid, 256, 0, st>>>(
+        A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, NB, gate, up, nullptr, h, I);
   else
-    moe_gemm_f16_kernel<true, true, true><<<grid, 256, 0, st>>>(A, a_scale, sorted_pairs, offsets, tiles,
-                                                                tile_count, topk, H, NB, gate, up, nullptr, h, I);
+    moe_gemm_f16_kernel<true, true, true, 4><<<grid, 256, 0, st>>>(
+        A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, NB, gate, up, nullptr, h, I);
   return hipGetLastError();
 }
 
@@ -325,14 +357,23 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
   const int NB = H / 256;
   const dim3 grid(grid_for(max_tiles, NB));
   const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
-  if (act == 0)
-    moe_gemm_f16_kernel<false, false, false><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles,
-                                                                   tile_count, topk, I, NB, down, down, w,
-                                                                   y, H);
-  else
-    moe_gemm_f16_kernel<false, true, false><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles,
-                                                                  tile_count, topk, I, NB, down, down, w,
-                                                                  y, H);
+  // I is a multiple of 128: scale groups of 4 K-blocks when it is a multiple of 256
+#define NVFP4_DOWN(ASC, KQ)                                                                               \
+  moe_gemm_f16_kernel<false, ASC, false, KQ><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles, \
+                                                                  tile_count, topk, I, NB, down, down, w, y, H)
+  const bool q4 = I % 256 == 0;
+  if (act == 0) {
+    if (q4)
+      NVFP4_DOWN(false, 4);
+    else
+      NVFP4_DOWN(false, 2);
+  } else {
+    if (q4)
+      NVFP4_DOWN(true, 4);
+    else
+      NVFP4_DOWN(true, 2);
+  }
+#undef NVFP4_DOWN
   return hipGetLastError();
 }
 
