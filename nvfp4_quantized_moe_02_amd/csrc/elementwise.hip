@@ -236,7 +236,9 @@ hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStrea
   return hipGetLastError();
 }
 
-// Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic.
+// Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic. All
+// slot loads are issued before the first add (an absent slot reads row 0 and adds nothing);
+// y is read once, so its loads are non-temporal.
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y, const int32_t* __restrict__ inv,
                                                       int T, int topk, int H4, void* __restrict__ out) {
@@ -244,11 +246,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   if (i >= (int64_t)T * H4) return;
   const int t = (int)(i / H4), c = (int)(i - (int64_t)t * H4);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < topk; ++j) {
-    const int pos = inv[(size_t)t * topk + j];
-    if (pos < 0) continue;
-    const float4 v = y[(size_t)pos * H4 + c];
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    int pos[8];
+    f32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pos[j] = j0 + j < topk ? inv[(size_t)t * topk + j0 + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y) + (size_t)(pos[j] < 0 ? 0 : pos[j]) * H4 + c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pos[j] >= 0) {
+        s.x += v[j][0]; s.y += v[j][1]; s.z += v[j][2]; s.w += v[j][3];
+      }
   }
   if (OUT == 0) {
     reinterpret_cast<float4*>(out)[i] = s;

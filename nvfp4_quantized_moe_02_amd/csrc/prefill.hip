@@ -74,7 +74,7 @@ struct ScaleRaw<2> {
   typedef uint2 type;
 };
 
-template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ>
+template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB>
 __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
                                           const uint8_t* const* bc, const uint8_t* const* bs,
                                           const WeightArgs& w0, const WeightArgs& w1, void* __restrict__ out,
@@ -85,12 +85,16 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   const int half = lane >> 5, l32 = lane & 31;
   const int nkb = K / KBLK;
 
-  // A: thread t copies 16-byte chunk t & 7 of rows (t >> 3) + 32*i, i < NRB, of a
-  // K-block; it stores chunk c of row r into slot c ^ (r & 7) of that LDS row.
+  // A: thread t copies 16-byte chunk t & 7 of rows (t >> 3) + RPR*i, i < NA, of a
+  // K-block; it stores chunk c of row r into slot c ^ (r & 7) of that LDS row. With 8
+  // waves and an odd NRB the last round also copies 32 rows the MFMAs never read (padding
+  // rows of the tile, so in bounds), which keeps the loop free of branches.
+  constexpr int RPR = WPB * 8;
+  constexpr int NA = (NRB * 32 + RPR - 1) / RPR;
   const int arow = tid >> 3, achunk = tid & 7;
-  const uint16_t* asrc[NRB];
+  const uint16_t* asrc[NA];
 #pragma unroll
-  for (int i = 0; i < NRB; ++i) asrc[i] = A + (size_t)s_src[arow + 32 * i] * K + achunk * 8;
+  for (int i = 0; i < NA; ++i) asrc[i] = A + (size_t)s_src[arow + RPR * i] * K + achunk * 8;
   const int aslot = ((achunk ^ (arow & 7)) << 4);
 
   const uint8_t* pc0 = bc[0] + half * 16;
@@ -132,33 +136,42 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 
   // Two K-blocks of A (registers) and B codes (registers) in flight. Iteration kb: store
   // A(kb) into LDS stage kb & 1, barrier, issue A(kb+2) and B(kb+2), compute K-block kb.
-  // Scales run one group of KQ K-blocks ahead.
-  uint4 aq[2][NRB];
+  // The scales of the next group are loaded two K-blocks before the end of a group and
+  // compacted at its end, inside the same loop iteration (a value carried across the
+  // back-edge while loads are in flight makes the compiler drain every load there).
+  uint4 aq[2][NA];
   uint4 bq[2][2];
   SRaw sq[2] = {load_s(0, 0), load_s(0, 1)};
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) aq[d][i] = load_a(d, i);
+    for (int i = 0; i < NA; ++i) aq[d][i] = load_a(d, i);
     bq[d][0] = load_b(d, 0);
     bq[d][1] = load_b(d, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   uint32_t sc0[KQ / 2], sc1[KQ / 2];
+  compact(sq[0], sc0);
+  compact(sq[1], sc1);
 
   auto kstep = [&](auto qpos, int kb) {
     constexpr int Q = decltype(qpos)::value;  // position in the scale group
     constexpr int R = Q & 1;                  // LDS stage / register ring slot
     char* st = lds + R * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) *reinterpret_cast<uint4*>(st + (arow + 32 * i) * 128 + aslot) = aq[R][i];
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = aq[R][i];
     // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
     // finished those reads before passing the barrier of iteration kb-1.
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) aq[R][i] = load_a(kb + 2, i);
+    for (int i = 0; i < NA; ++i) aq[R][i] = load_a(kb + 2, i);
     const uint4 cur0 = bq[R][0], cur1 = bq[R][1];
     bq[R][0] = load_b(kb + 2, 0);
     bq[R][1] = load_b(kb + 2, 1);
+    // keep the loads here: sunk or reordered loads shorten the prefetch distance and make
+    // the loop-header wait counts pessimistic
+    __builtin_amdgcn_sched_barrier(0);
     const f16x2_t s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
     const f16x2_t s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
 #pragma unroll
@@ -177,24 +190,32 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   };
   // nkb is a multiple of KQ
   for (int j = 0; j < ngrp; ++j) {
-    compact(sq[0], sc0);
-    compact(sq[1], sc1);
-    sq[0] = load_s(j + 1, 0);
-    sq[1] = load_s(j + 1, 1);
     const int kb = j * KQ;
-    kstep(std::integral_constant<int, 0>{}, kb);
-    kstep(std::integral_constant<int, 1>{}, kb + 1);
     if constexpr (KQ == 4) {
+      kstep(std::integral_constant<int, 0>{}, kb);
+      kstep(std::integral_constant<int, 1>{}, kb + 1);
+      sq[0] = load_s(j + 1, 0);
+      sq[1] = load_s(j + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
       kstep(std::integral_constant<int, 2>{}, kb + 2);
       kstep(std::integral_constant<int, 3>{}, kb + 3);
+    } else {
+      sq[0] = load_s(j + 1, 0);
+      sq[1] = load_s(j + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      kstep(std::integral_constant<int, 0>{}, kb);
+      kstep(std::integral_constant<int, 1>{}, kb + 1);
     }
+    compact(sq[0], sc0);
+    compact(sq[1], sc1);
   }
 
-  if (GATEUP) {
+  if constexpr (GATEUP) {
     const float gg = w0.global[tc.e], gu = w1.global[tc.e];
     if (!HOUT32) {
-      // fp16 h through LDS: [rows][128 intermediate indices], 16-byte chunks XOR-swizzled by
-      // row; then every thread stores whole 16-byte chunks (256 contiguous bytes per row).
+      // fp16 h through LDS: [rows][NC intermediate indices], 16-byte chunks XOR-swizzled by
+      // row; then every thread stores whole 16-byte chunks (2*NC contiguous bytes per row).
+      constexpr int NC = WPB * 32;
       __syncthreads();  // every wave is done with the A stages
       uint16_t* hl = reinterpret_cast<uint16_t*>(lds);
       const int col = wave * 32 + l32;
@@ -205,18 +226,19 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
           const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
           const float xs = s_coef[r];
           const float hv = silu_fast(acc[rb][0][i] * (xs * gg)) * (acc[rb][1][i] * (xs * gu));
-          hl[r * 128 + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f32_to_f16_bits(hv);
+          hl[r * NC + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f32_to_f16_bits(hv);
         }
       __syncthreads();
       uint16_t* h = reinterpret_cast<uint16_t*>(out);
-      for (int k = tid; k < NRB * 32 * 16; k += 256) {
-        const int r = k >> 4, c = k & 15;
+      constexpr int CPR = NC / 8;  // 16-byte chunks per row
+      for (int k = tid; k < NRB * 32 * CPR; k += WPB * 64) {
+        const int r = k / CPR, c = k % CPR;
         if (r < tc.rows)
-          *reinterpret_cast<uint4*>(h + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * 128 + c * 8) =
-              *reinterpret_cast<const uint4*>(hl + r * 128 + ((c ^ (r & 15)) << 3));
+          *reinterpret_cast<uint4*>(h + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * NC + c * 8) =
+              *reinterpret_cast<const uint4*>(hl + r * NC + ((c ^ (r & 15)) << 3));
       }
     } else {
-      const int jcol = tc.nb * 128 + wave * 32 + l32;
+      const int jcol = tc.nb * (WPB * 32) + wave * 32 + l32;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -230,35 +252,56 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
         }
     }
   } else {
-    // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order (lanes 0..31 of a row
-    // write 128 contiguous bytes); the combine kernel sums each token's slots.
+    // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order; the combine kernel sums
+    // each token's slots. One row block at a time goes through LDS ([32][NCOL] fp32, 16-byte
+    // chunks XOR-swizzled by row), so every store is a full 16 bytes and a wave writes whole
+    // 1 KB row segments; the stores are non-temporal (y is read once, by the combine).
+    static_assert(WPB == 4, "the down epilogue stages 32 rows of 256 outputs in the A stages");
+    constexpr int NCOL = WPB * 64;
+    static_assert(32 * NCOL * 4 <= NSTAGE * STAGE_BYTES, "LDS");
     const float gd = w0.global[tc.e];
     float* y = reinterpret_cast<float*>(out);
+    float* yl = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int rb = 0; rb < NRB; ++rb) {
+      __syncthreads();  // the A stages / the previous row block are no longer read
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        if (r < tc.rows) {
-          const float c = s_coef[r] * gd;
-          float* yrow = y + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * 256 + wave * 64 + l32;
-          yrow[0] = acc[rb][0][i] * c;
-          yrow[32] = acc[rb][1][i] * c;
+        const int rr = (i >> 2) * 8 + half * 4 + (i & 3);
+        const float c = s_coef[rb * 32 + rr] * gd;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int col = wave * 64 + cb * 32 + l32;
+          yl[rr * NCOL + (((col >> 2) ^ (rr & 7)) << 2) + (col & 3)] = acc[rb][cb][i] * c;
         }
       }
+      __syncthreads();
+      for (int k = tid; k < 32 * (NCOL / 4); k += WPB * 64) {
+        const int rr = k / (NCOL / 4), cc = k % (NCOL / 4);
+        const int r = rb * 32 + rr;
+        if (r < tc.rows) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(yl + rr * NCOL + ((cc ^ (rr & 7)) << 2));
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(y + (size_t)(tc.base + tc.m0 + r) * ldo +
+                                                                     tc.nb * NCOL + cc * 4));
+        }
+      }
+    }
   }
 }
 
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
 // ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
 // HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
-template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ>
-__global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
+template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB>
+__global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ sorted_pairs,
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
     void* __restrict__ out, int ldo) {
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
+  // the A stages, reused by the fp16 h transpose of gate/up (rows x WPB*32 fp16)
+  constexpr int kLds = (GATEUP && !HOUT32 && BM * WPB * 64 > NSTAGE * STAGE_BYTES) ? BM * WPB * 64
+                                                                                      : NSTAGE * STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_src[BM];
   __shared__ int s_tok[BM];
   __shared__ float s_coef[BM];
@@ -300,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
   const uint8_t* bc[2];
   const uint8_t* bs[2];
   if (GATEUP) {
-    const size_t grow = (size_t)tc.e * w0.N + tc.nb * 128 + wave * 32 + l32;
+    const size_t grow = (size_t)tc.e * w0.N + tc.nb * (WPB * 32) + wave * 32 + l32;
     bc[0] = w0.codes + grow * (K / 2);
     bs[0] = w0.scales + grow * (K / 16);
     bc[1] = w1.codes + grow * (K / 2);
@@ -308,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
   } else {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const size_t grow = (size_t)tc.e * w0.N + tc.nb * 256 + wave * 64 + cb * 32 + l32;
+      const size_t grow = (size_t)tc.e * w0.N + tc.nb * (WPB * 64) + wave * 64 + cb * 32 + l32;
       bc[cb] = w0.codes + grow * (K / 2);
       bs[cb] = w0.scales + grow * (K / 16);
     }
@@ -317,13 +360,13 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_f16_kernel(
 
   const int nrb = (tc.rows + 31) >> 5;
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -336,16 +379,25 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
                               int max_tiles, int topk, int H, int I, const WeightArgs& gate,
                               const WeightArgs& up, void* h, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
-  const int NB = I / 128;
-  const dim3 grid(grid_for(max_tiles, NB));
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a);
-  // H is a multiple of 256: scale groups of 4 K-blocks
-  if (act == 0)
-    moe_gemm_f16_kernel<true, false, false, 4><<<grid, 256, 0, st>>>(
-        A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, NB, gate, up, nullptr, h, I);
-  else
-    moe_gemm_f16_kernel<true, true, true, 4><<<grid, 256, 0, st>>>(
-        A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, NB, gate, up, nullptr, h, I);
+  // 8 waves (256 intermediate indices per block) when I allows, else 4; H is a multiple
+  // of 256, so scale groups of 4 K-blocks.
+#define NVFP4_GU(ASC, H32, WPB)                                                                          \
+  moe_gemm_f16_kernel<true, ASC, H32, 4, WPB><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>( \
+      A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, nullptr, h, I)
+  const bool w8 = I % 256 == 0;
+  if (act == 0) {
+    if (w8)
+      NVFP4_GU(false, false, 8);
+    else
+      NVFP4_GU(false, false, 4);
+  } else {
+    if (w8)
+      NVFP4_GU(true, true, 8);
+    else
+      NVFP4_GU(true, true, 4);
+  }
+#undef NVFP4_GU
   return hipGetLastError();
 }
 
@@ -354,13 +406,12 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
                             int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
                             float* y, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
-  const int NB = H / 256;
-  const dim3 grid(grid_for(max_tiles, NB));
   const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
-  // I is a multiple of 128: scale groups of 4 K-blocks when it is a multiple of 256
-#define NVFP4_DOWN(ASC, KQ)                                                                               \
-  moe_gemm_f16_kernel<false, ASC, false, KQ><<<grid, 256, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles, \
-                                                                  tile_count, topk, I, NB, down, down, w, y, H)
+  // 4 waves, 256 outputs per block; scale groups of 4 K-blocks when I is a multiple of
+  // 256, else 2.
+#define NVFP4_DOWN(ASC, KQ)                                                                           \
+  moe_gemm_f16_kernel<false, ASC, false, KQ, 4><<<grid_for(max_tiles, H / 256), 256, 0, st>>>(        \
+      A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / 256, down, down, w, y, H)
   const bool q4 = I % 256 == 0;
   if (act == 0) {
     if (q4)
