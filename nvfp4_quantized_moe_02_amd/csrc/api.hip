@@ -251,10 +251,11 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
     hipError_t e = hipSuccess;
     if (stage == 0) {  // route, stage the activations
       RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles, at<int32_t>(ws, l.r.inv)};
-      e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
-      if (e == hipSuccess) {
-        if (act == NVFP4_ACT_BF16) e = launch_bf16_to_f16(x, a16, (int64_t)T * H, s);
-        else e = launch_quant_rows(x, NVFP4_BF16, T, H, a16, 1, sx, s);
+      if (act == NVFP4_ACT_BF16) {
+        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s, x, a16, (int64_t)T * H);
+      } else {
+        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
+        if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, a16, 1, sx, s);
       }
     } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
       e = launch_gemm_gateup(mode, a16, sx, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,

@@ -183,26 +183,6 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols,
 
 // ------------------------------------------------------------------ activation staging
 // bf16 -> fp16 (round to nearest even; exact for |x| in the fp16 normal range).
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ y,
-                                                          int64_t n8) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  uint4 v = x[i];
-  uint32_t in[4] = {v.x, v.y, v.z, v.w}, o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = (uint32_t)f32_to_f16_bits(bf16_lo(in[j])) | ((uint32_t)f32_to_f16_bits(bf16_hi(in[j])) << 16);
-  y[i] = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
-hipError_t launch_bf16_to_f16(const void* x, void* y, int64_t n, hipStream_t st) {
-  const int64_t n8 = n / 8;
-  if (n8 == 0) return hipSuccess;
-  bf16_to_f16_kernel<<<dim3((unsigned)((n8 + 255) / 256)), 256, 0, st>>>(
-      reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(y), n8);
-  return hipGetLastError();
-}
-
 // Zero fill (a kernel rather than a memset node, so the sequence can be graph-captured).
 __global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)

@@ -25,7 +25,6 @@ hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes
                          const float* global, int N, int K, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
                              float* scale, hipStream_t st);
-hipError_t launch_bf16_to_f16(const void* x, void* y, int64_t n, hipStream_t st);
 hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st);
 // out[t][n] = sum over slots j (in order) of y[inv[t*topk + j]][n]; dropped slots skipped.
@@ -33,7 +32,7 @@ hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, i
                           hipStream_t st);
 
 // route.hip
-constexpr int kRouteChunk = 4096;  // pairs per counting block
+constexpr int kRouteChunk = 512;  // pairs per counting / scatter block
 constexpr int kMaxExperts = 8192;
 struct RouteWs {
   int32_t* counts;    // [E][nblk]
@@ -43,8 +42,11 @@ struct RouteWs {
   int32_t* inv;       // [P] sorted position of each pair, -1 if dropped (optional)
 };
 int route_blocks(int64_t P);
+// cvt_src (optional): n bf16 values converted to fp16 into cvt_dst by extra blocks of the
+// first launch (n a multiple of 8).
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
-                        const RouteWs& ws, int tile_m, hipStream_t st);
+                        const RouteWs& ws, int tile_m, hipStream_t st, const void* cvt_src = nullptr,
+                        void* cvt_dst = nullptr, int64_t cvt_n = 0);
 
 // decode.hip
 constexpr int kDecodeMaxT = 8;

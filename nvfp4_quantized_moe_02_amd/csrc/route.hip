@@ -10,12 +10,29 @@ namespace nvfp4 {
 
 int route_blocks(int64_t P) { return (int)((P + kRouteChunk - 1) / kRouteChunk); }
 
+// Blocks [0, nblk): expert histogram of one chunk of kRouteChunk pairs. Blocks after that
+// (optional) convert the bf16 activations to fp16 for the prefill GEMMs, 2048 values per
+// block: the routing grid is small, so the conversion runs beside it in the same launch.
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
                                                           int nblk, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ dropped) {
+                                                          int32_t* __restrict__ dropped,
+                                                          const uint4* __restrict__ cvt_src,
+                                                          uint4* __restrict__ cvt_dst, int64_t cvt_n8) {
   extern __shared__ int32_t hist[];
   __shared__ int32_t drop;
   const int b = blockIdx.x, tid = threadIdx.x;
+  if (b >= nblk) {
+    const int64_t i = (int64_t)(b - nblk) * 256 + tid;
+    if (i >= cvt_n8) return;
+    const uint4 v = cvt_src[i];
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (uint32_t)f32_to_f16_bits(bf16_lo(in[j])) | ((uint32_t)f32_to_f16_bits(bf16_hi(in[j])) << 16);
+    cvt_dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    return;
+  }
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   if (tid == 0) drop = 0;
   __syncthreads();
@@ -51,74 +68,94 @@ __device__ int block_scan_1024(int v, int* sh, int* total) {
   return incl - v;
 }
 
-// One block of 1024 threads: counts (e-major, chunk-minor) -> bases in place, expert
-// offsets, the dropped total, -1 padding of sorted_pairs, and the tile list.
-__global__ __launch_bounds__(1024) void route_scan_kernel(int E, int nblk, int64_t P, int32_t* __restrict__ counts,
-                                                          const int32_t* __restrict__ dropped,
+// One wave per expert: that expert's chunk counts (contiguous, e-major) -> exclusive
+// prefix in place (the expert-local base of each chunk), and the expert's total into
+// totals[e].
+__global__ __launch_bounds__(256) void route_expert_scan_kernel(int E, int nblk, int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  int32_t* c = counts + (size_t)e * nblk;
+  int run = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < nblk ? c[b] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += u;
+    }
+    if (b < nblk) c[b] = run + incl - v;
+    run += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) totals[e] = run;
+}
+
+// One block of 1024 threads: expert totals (in offsets[0..E); all zero when there are no
+// chunks) -> exclusive offsets in place and offsets[E]; the dropped total; -1 padding of
+// sorted_pairs; the tile list.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int E, int nblk, int64_t P, const int32_t* __restrict__ dropped,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_pairs,
                                                           int32_t* __restrict__ hdr, TileDesc* __restrict__ tiles,
                                                           int tile_m) {
   __shared__ int sh[1024];
   const int tid = threadIdx.x;
-  const int n = E * nblk;
-  const int per = (n + 1023) / 1024;
-  const int start = tid * per < n ? tid * per : n;
-  const int end = start + per < n ? start + per : n;
+  const int per = (E + 1023) / 1024;
+  const int start = tid * per < E ? tid * per : E;
+  const int end = start + per < E ? start + per : E;
   int local = 0;
-  for (int i = start; i < end; ++i) local += counts[i];
+  for (int i = start; i < end; ++i) local += nblk ? offsets[i] : 0;
   int total;
   int run = block_scan_1024(local, sh, &total);
+  int my = 0;  // tiles of tile_m rows per expert, in expert order
   for (int i = start; i < end; ++i) {
-    const int c = counts[i];
-    counts[i] = run;
+    const int c = nblk ? offsets[i] : 0;
+    offsets[i] = run;
     run += c;
+    my += (c + tile_m - 1) / tile_m;
   }
   int d = 0;
   for (int b = tid; b < nblk; b += 1024) d += dropped[b];
   int dtotal;
   block_scan_1024(d, sh, &dtotal);
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) offsets[e] = nblk ? counts[(size_t)e * nblk] : 0;
   if (tid == 0) {
     offsets[E] = total;
     hdr[0] = dtotal;
   }
   for (int64_t i = total + tid; i < P; i += 1024) sorted_pairs[i] = -1;
   if (tiles == nullptr) return;
-  __syncthreads();
-  // tiles of tile_m rows per expert, in expert order
-  int my = 0;
-  for (int e = tid; e < E; e += 1024) {
-    const int cnt = ((e + 1 < E) ? offsets[e + 1] : total) - offsets[e];
-    my += (cnt + tile_m - 1) / tile_m;
-  }
   int ntiles;
   int base = block_scan_1024(my, sh, &ntiles);
-  for (int e = tid; e < E; e += 1024) {
-    const int cnt = ((e + 1 < E) ? offsets[e + 1] : total) - offsets[e];
-    for (int m0 = 0; m0 < cnt; m0 += tile_m) tiles[base++] = TileDesc{e, m0};
+  __syncthreads();  // offsets of this thread's range are final (written above by this thread)
+  for (int i = start; i < end; ++i) {
+    const int cnt = (i + 1 < end ? offsets[i + 1] : run) - offsets[i];
+    for (int m0 = 0; m0 < cnt; m0 += tile_m) tiles[base++] = TileDesc{i, m0};
   }
   if (tid == 0) hdr[1] = ntiles;
 }
 
-// One wave per chunk: walks its pairs in order, 64 at a time; lanes holding the same
-// expert get consecutive slots in lane order (a match built from ballots over the id
-// bits), so the scatter is stable.
-__global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
-                                                           int nblk, const int32_t* __restrict__ bases,
-                                                           int32_t* __restrict__ sorted_pairs,
-                                                           int32_t* __restrict__ inv) {
-  extern __shared__ int32_t run[];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = bases[(size_t)e * nblk + b];
+// One block of 4 waves per chunk, 256 pairs per round. Within a wave, lanes holding the
+// same expert are ranked in lane order (a match built from ballots over the id bits); the
+// four waves of a round then take their positions from the running per-expert position in
+// wave order, one wave per barrier-separated phase, so the scatter is stable.
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                            int nblk, const int32_t* __restrict__ bases,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pairs,
+                                                            int32_t* __restrict__ inv) {
+  extern __shared__ int32_t run[];  // [E] next sorted position per expert
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 256) run[e] = offsets[e] + bases[(size_t)e * nblk + b];
   __syncthreads();
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const int64_t p0 = (int64_t)b * kRouteChunk;
   const int64_t p1 = p0 + kRouteChunk < P ? p0 + kRouteChunk : P;
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int64_t base = p0; base < p1; base += 64) {
-    const int64_t p = base + lane;
+  for (int64_t base = p0; base < p1; base += 256) {
+    const int64_t p = base + tid;
     const int e = p < p1 ? ids[p] : -1;
     const bool valid = p < p1 && (unsigned)e < (unsigned)E;
     uint64_t m = __ballot(valid);
@@ -127,33 +164,43 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       const uint64_t bb = __ballot(set);
       m &= set ? bb : ~bb;
     }
-    int pos = 0;
-    if (valid) pos = run[e] + __popcll(m & lt);
-    __syncthreads();
-    if (valid) {
-      sorted_pairs[pos] = (int32_t)p;
-      if ((m >> lane) == 1ull) run[e] += __popcll(m);
+    int pos = -1;
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w && valid) {
+        pos = run[e] + __popcll(m & lt);
+        if ((m >> lane) == 1ull) run[e] = pos + 1;  // highest lane of its expert
+      }
+      __syncthreads();
     }
-    if (inv != nullptr && p < p1) inv[p] = valid ? pos : -1;  // sorted position of pair p
-    __syncthreads();
+    if (valid) sorted_pairs[pos] = (int32_t)p;
+    if (inv != nullptr && p < p1) inv[p] = pos;  // sorted position of pair p, -1 if dropped
   }
 }
 
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
-                        const RouteWs& ws, int tile_m, hipStream_t st) {
+                        const RouteWs& ws, int tile_m, hipStream_t st, const void* cvt_src, void* cvt_dst,
+                        int64_t cvt_n) {
   const int nblk = route_blocks(P);
-  const size_t lds = (size_t)E * sizeof(int32_t);
-  if (nblk > 0) {
-    route_count_kernel<<<nblk, 256, lds, st>>>(ids, P, E, nblk, ws.counts, ws.dropped);
+  const int64_t cvt_n8 = cvt_src != nullptr ? cvt_n / 8 : 0;
+  const int64_t cvt_blocks = (cvt_n8 + 255) / 256;
+  if (nblk + cvt_blocks > 0) {
+    route_count_kernel<<<dim3((unsigned)(nblk + cvt_blocks)), 256, (size_t)E * sizeof(int32_t), st>>>(
+        ids, P, E, nblk, ws.counts, ws.dropped, reinterpret_cast<const uint4*>(cvt_src),
+        reinterpret_cast<uint4*>(cvt_dst), cvt_n8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  route_scan_kernel<<<1, 1024, 0, st>>>(E, nblk, P, ws.counts, ws.dropped, offsets, sorted_pairs, ws.hdr,
-                                        ws.tiles, tile_m);
+  if (nblk > 0) {
+    route_expert_scan_kernel<<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(E, nblk, ws.counts, offsets);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  route_scan_kernel<<<1, 1024, 0, st>>>(E, nblk, P, ws.dropped, offsets, sorted_pairs, ws.hdr, ws.tiles, tile_m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nblk > 0) {
-    route_scatter_kernel<<<nblk, 64, lds, st>>>(ids, P, E, nblk, ws.counts, sorted_pairs, ws.inv);
+    route_scatter_kernel<<<nblk, 256, (size_t)E * sizeof(int32_t), st>>>(ids, P, E, nblk, ws.counts, offsets,
+                                                                        sorted_pairs, ws.inv);
     e = hipGetLastError();
   }
   return e;
