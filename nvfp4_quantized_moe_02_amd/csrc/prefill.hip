@@ -3,10 +3,11 @@
 // Strata": an MMQ group's experts gathered in one launch; prompt chunks up to 32K
 // tokens, each streaming every expert of a layer once).
 //
-// Tile = (expert, up to 128 routed rows) x one N block; 4 waves. Each wave owns an
-// NRB*32 x 64 output block (NRB row blocks x 2 column blocks of v_mfma_f32_32x32x16_f16),
-// where NRB = ceil(rows / 32) is a template parameter, so partial tiles skip the empty
-// row blocks without branches in the K loop.
+// Tile = (expert, up to 128 routed rows) x one N block of WPB*64 weight rows; WPB = 8
+// waves when the shape allows, else 4. Each wave owns an NRB*32 x 64 output block (NRB row
+// blocks x 2 column blocks of v_mfma_f32_32x32x16_f16), where NRB = ceil(rows / 32) is a
+// template parameter, so partial tiles skip the empty row blocks without branches in the
+// K loop.
 //
 // A operand (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into
 // registers and stored to a 2-stage LDS ring at the top of the iteration that uses it.
@@ -14,13 +15,16 @@
 // c ^ (r & 7), so the 32 rows of an MFMA fragment read hit 8 distinct slots (no bank
 // conflicts). Rows are gathered by token for gate/up and contiguous for down.
 //
-// B operand (NVFP4 weights): each lane loads the 16 code bytes its fragment needs (two
-// K-blocks ahead, in registers) and its column's scale bytes for four K-blocks at once,
-// and unpacks them exactly to fp16: E2M1 codes and the E4M3 scale both convert exactly
-// to fp16, and their product (at most 5 significant bits) is exact in one packed fp16
-// multiply. Weight bytes never pass through LDS and are decoded once per wave. Within a K-block the reduction
-// order of the 64 inputs is permuted (lane half 0 takes inputs 0..31, half 1 inputs
-// 32..63); A is read with the same permutation, so the dot products are unchanged.
+// B operand (NVFP4 weights): the block stages its weight rows' codes GK K-blocks at a
+// time with coalesced loads (consecutive threads read one row's GK*32 contiguous bytes)
+// one group ahead in registers, stores each group to an XOR-swizzled LDS tile, and every
+// lane reads its fragment's 16 code bytes per K-block from there. Each lane loads its
+// column's scale bytes for four K-blocks at once. The unpack to fp16 is exact: E2M1 codes
+// and the E4M3 scale both convert exactly to fp16, and their product (at most 5
+// significant bits) is exact in one packed fp16 multiply; each weight is decoded once per
+// block. Within a K-block the reduction order of the 64 inputs is permuted (lane half 0
+// takes inputs 0..31, half 1 inputs 32..63); A is read with the same permutation, so the
+// dot products are unchanged.
 //
 // gate/up: wave w computes gate and up for the same 32 intermediate indices, so SwiGLU
 // runs in registers: h = SiLU(gamma_g * g) * (gamma_u * u) (gate scale before SiLU, the
@@ -74,12 +78,26 @@ struct ScaleRaw<2> {
   typedef uint2 type;
 };
 
-template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB>
+// B tile of a block: NCB = WPB * 64 weight rows (gate/up: WPB*32 gate rows, then the
+// same WPB*32 up rows; down: WPB*64 rows), GK K-blocks at a time, in LDS.
+template <int WPB, int GK>
+struct BTile {
+  static constexpr int NCB = WPB * 64;
+  static constexpr int ROWB = GK * 32;                  // code bytes of one row per group
+  static constexpr int CPR = GK * 2;                    // 16-byte chunks per row per group
+  static constexpr int SHIFT = GK == 2 ? 1 : 0;         // swizzle: chunk ^ ((row >> SHIFT) & (CPR-1))
+  static constexpr int BYTES = NCB * ROWB;
+  static constexpr int CH = BYTES / (WPB * 64 * 16);    // 16-byte chunks staged per thread
+  static constexpr int RPT = WPB * 64 / CPR;            // rows covered by one staging round
+  __device__ static int slot(int row, int ch) { return row * ROWB + ((ch ^ ((row >> SHIFT) & (CPR - 1))) << 4); }
+};
+
+template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB, int GK>
 __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
-                                          const uint8_t* const* bc, const uint8_t* const* bs,
-                                          const WeightArgs& w0, const WeightArgs& w1, void* __restrict__ out,
-                                          int ldo, char* lds, const int* s_src, const int* s_tok,
-                                          const float* s_coef) {
+                                          const uint8_t* b0row, const uint8_t* b1row,
+                                          const uint8_t* const* bs, const WeightArgs& w0,
+                                          const WeightArgs& w1, void* __restrict__ out, int ldo, char* lds,
+                                          const int* s_src, const int* s_tok, const float* s_coef) {
   (void)s_tok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -97,12 +115,26 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   for (int i = 0; i < NA; ++i) asrc[i] = A + (size_t)s_src[arow + RPR * i] * K + achunk * 8;
   const int aslot = ((achunk ^ (arow & 7)) << 4);
 
-  const uint8_t* pc0 = bc[0] + half * 16;
-  const uint8_t* pc1 = bc[1] + half * 16;
-  auto load_b = [&](int kb, int cb) -> uint4 {
-    const int kc = kb < nkb ? kb : nkb - 1;  // past the end: refetch the last block (never used)
-    return *reinterpret_cast<const uint4*>((cb == 0 ? pc0 : pc1) + kc * 32);
+  // B codes: the block's NCB weight rows, GK K-blocks (GK*32 bytes of each row) per
+  // group. Thread t stages chunks j*(WPB*64) + t of the group tile, i.e. chunk t % CPR of
+  // rows j*RPT + t / CPR: CPR consecutive threads read one row's GK*32 contiguous bytes.
+  // They go to LDS once per group; each lane then reads its fragments from there.
+  typedef BTile<WPB, GK> BT;
+  char* btiles = lds + NSTAGE * STAGE_BYTES;
+  const int brow = tid / BT::CPR, bch = tid % BT::CPR;
+  const int ngb = nkb / GK;
+  auto load_bg = [&](int g, int j) -> uint4 {
+    const int gc = g < ngb ? g : ngb - 1;  // past the end: refetch the last group (never used)
+    const int row = j * BT::RPT + brow;
+    // gate/up: rows [0, NCB/2) are gate rows, [NCB/2, NCB) the same up rows (j is a
+    // compile-time index, so the tensor choice is too)
+    const uint8_t* base = (GATEUP && j * BT::RPT >= BT::NCB / 2) ? b1row + (size_t)(row - BT::NCB / 2) * (K / 2)
+                                                                 : b0row + (size_t)row * (K / 2);
+    return *reinterpret_cast<const uint4*>(base + gc * BT::ROWB + bch * 16);
   };
+  // tile row of this lane's fragment in column block cb
+  const int frow0 = GATEUP ? wave * 32 + l32 : wave * 64 + l32;
+  const int frow1 = GATEUP ? BT::NCB / 2 + wave * 32 + l32 : wave * 64 + 32 + l32;
   // Scales: K-block kb of a column holds 4 bytes (groups 4kb .. 4kb+3); lane half h uses
   // bytes 2h and 2h+1. A group of KQ K-blocks is one load per column.
   typedef typename ScaleRaw<KQ>::type SRaw;
@@ -134,21 +166,24 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rb][cb][i] = 0.f;
 
-  // Two K-blocks of A (registers) and B codes (registers) in flight. Iteration kb: store
-  // A(kb) into LDS stage kb & 1, barrier, issue A(kb+2) and B(kb+2), compute K-block kb.
-  // The scales of the next group are loaded two K-blocks before the end of a group and
-  // compacted at its end, inside the same loop iteration (a value carried across the
+  // Two K-blocks of A in registers; B codes one group ahead in registers. Iteration kb:
+  // store A(kb) into LDS stage kb & 1, barrier; at a group start also store the staged
+  // group into the B tile (every wave finished the previous group's reads at the barrier),
+  // barrier, and stage the next group; issue A(kb+2); compute K-block kb.
+  // The scales of the next group are loaded two K-blocks before the end of a scale group
+  // and compacted at its end, inside the same loop iteration (a value carried across the
   // back-edge while loads are in flight makes the compiler drain every load there).
   uint4 aq[2][NA];
-  uint4 bq[2][2];
+  uint4 bg[BT::CH];
   SRaw sq[2] = {load_s(0, 0), load_s(0, 1)};
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < BT::CH; ++j) bg[j] = load_bg(0, j);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) aq[d][i] = load_a(d, i);
-    bq[d][0] = load_b(d, 0);
-    bq[d][1] = load_b(d, 1);
     __builtin_amdgcn_sched_barrier(0);
   }
   uint32_t sc0[KQ / 2], sc1[KQ / 2];
@@ -164,14 +199,23 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
     // finished those reads before passing the barrier of iteration kb-1.
     __syncthreads();
+    if constexpr (Q % GK == 0) {
+#pragma unroll
+      for (int j = 0; j < BT::CH; ++j)
+        *reinterpret_cast<uint4*>(btiles + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < BT::CH; ++j) bg[j] = load_bg(kb / GK + 1, j);
+    }
+    const char* btile = btiles;
 #pragma unroll
     for (int i = 0; i < NA; ++i) aq[R][i] = load_a(kb + 2, i);
-    const uint4 cur0 = bq[R][0], cur1 = bq[R][1];
-    bq[R][0] = load_b(kb + 2, 0);
-    bq[R][1] = load_b(kb + 2, 1);
     // keep the loads here: sunk or reordered loads shorten the prefetch distance and make
     // the loop-header wait counts pessimistic
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int q = Q % GK;  // K-block within the B group: chunks 2q (half 0), 2q+1 (half 1)
+    const uint4 cur0 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow0, 2 * q + half));
+    const uint4 cur1 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow1, 2 * q + half));
     const f16x2_t s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
     const f16x2_t s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
 #pragma unroll
@@ -255,10 +299,9 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order; the combine kernel sums
     // each token's slots. One row block at a time goes through LDS ([32][NCOL] fp32, 16-byte
     // chunks XOR-swizzled by row), so every store is a full 16 bytes and a wave writes whole
-    // 1 KB row segments; the stores are non-temporal (y is read once, by the combine).
-    static_assert(WPB == 4, "the down epilogue stages 32 rows of 256 outputs in the A stages");
+    // 1 KB row segments; the stores are non-temporal (y is read once, by the combine). The
+    // kernel's LDS holds 32 * NCOL * 4 bytes.
     constexpr int NCOL = WPB * 64;
-    static_assert(32 * NCOL * 4 <= NSTAGE * STAGE_BYTES, "LDS");
     const float gd = w0.global[tc.e];
     float* y = reinterpret_cast<float*>(out);
     float* yl = reinterpret_cast<float*>(lds);
@@ -292,15 +335,17 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
 // ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
 // HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
-template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB>
+template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB, int GK>
 __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ sorted_pairs,
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
     void* __restrict__ out, int ldo) {
-  // the A stages, reused by the fp16 h transpose of gate/up (rows x WPB*32 fp16)
-  constexpr int kLds = (GATEUP && !HOUT32 && BM * WPB * 64 > NSTAGE * STAGE_BYTES) ? BM * WPB * 64
-                                                                                      : NSTAGE * STAGE_BYTES;
+  // A stages and the B tile; the epilogue reuses them (gate/up fp16 h transpose: rows x
+  // WPB*32 fp16; down: 32 rows x WPB*64 fp32)
+  constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, GK>::BYTES;
+  constexpr int kEpi = GATEUP ? (HOUT32 ? 0 : BM * WPB * 64) : 32 * WPB * 64 * 4;
+  constexpr int kLds = kMain > kEpi ? kMain : kEpi;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_src[BM];
   __shared__ int s_tok[BM];
@@ -340,33 +385,38 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     }
   }
 
-  const uint8_t* bc[2];
+  // first weight row of the block in each tensor; per-lane scale rows of its fragments
+  const uint8_t* b0row;
+  const uint8_t* b1row;
   const uint8_t* bs[2];
   if (GATEUP) {
-    const size_t grow = (size_t)tc.e * w0.N + tc.nb * (WPB * 32) + wave * 32 + l32;
-    bc[0] = w0.codes + grow * (K / 2);
-    bs[0] = w0.scales + grow * (K / 16);
-    bc[1] = w1.codes + grow * (K / 2);
-    bs[1] = w1.scales + grow * (K / 16);
+    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (WPB * 32);
+    b0row = w0.codes + row0 * (K / 2);
+    b1row = w1.codes + row0 * (K / 2);
+    bs[0] = w0.scales + (row0 + wave * 32 + l32) * (K / 16);
+    bs[1] = w1.scales + (row0 + wave * 32 + l32) * (K / 16);
   } else {
+    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (WPB * 64);
+    b0row = w0.codes + row0 * (K / 2);
+    b1row = b0row;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const size_t grow = (size_t)tc.e * w0.N + tc.nb * (WPB * 64) + wave * 64 + cb * 32 + l32;
-      bc[cb] = w0.codes + grow * (K / 2);
-      bs[cb] = w0.scales + grow * (K / 16);
-    }
+    for (int cb = 0; cb < 2; ++cb) bs[cb] = w0.scales + (row0 + wave * 64 + cb * 32 + l32) * (K / 16);
   }
   __syncthreads();
 
   const int nrb = (tc.rows + 31) >> 5;
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
+                                                   s_coef);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
+                                                   s_coef);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
+                                                   s_coef);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB>(tc, A, K, bc, bs, w0, w1, out, ldo, lds, s_src, s_tok, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
+                                                   s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -380,22 +430,22 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
                               const WeightArgs& up, void* h, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a);
-  // 8 waves (256 intermediate indices per block) when I allows, else 4; H is a multiple
-  // of 256, so scale groups of 4 K-blocks.
-#define NVFP4_GU(ASC, H32, WPB)                                                                          \
-  moe_gemm_f16_kernel<true, ASC, H32, 4, WPB><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>( \
+  // 8 waves (256 intermediate indices per block, B groups of 4 K-blocks) when I allows,
+  // else 4 waves (groups of 2); H is a multiple of 256, so scale groups of 4 K-blocks.
+#define NVFP4_GU(ASC, H32, WPB, GK)                                                                      \
+  moe_gemm_f16_kernel<true, ASC, H32, 4, WPB, GK><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>( \
       A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, nullptr, h, I)
   const bool w8 = I % 256 == 0;
   if (act == 0) {
     if (w8)
-      NVFP4_GU(false, false, 8);
+      NVFP4_GU(false, false, 8, 2);
     else
-      NVFP4_GU(false, false, 4);
+      NVFP4_GU(false, false, 4, 2);
   } else {
     if (w8)
-      NVFP4_GU(true, true, 8);
+      NVFP4_GU(true, true, 8, 2);
     else
-      NVFP4_GU(true, true, 4);
+      NVFP4_GU(true, true, 4, 2);
   }
 #undef NVFP4_GU
   return hipGetLastError();
@@ -407,23 +457,33 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
                             float* y, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
-  // 4 waves, 256 outputs per block; scale groups of 4 K-blocks when I is a multiple of
-  // 256, else 2.
-#define NVFP4_DOWN(ASC, KQ)                                                                           \
-  moe_gemm_f16_kernel<false, ASC, false, KQ, 4><<<grid_for(max_tiles, H / 256), 256, 0, st>>>(        \
-      A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / 256, down, down, w, y, H)
+  // 8 waves (512 outputs per block) when H allows, else 4 (256); scale groups of 4
+  // K-blocks when I is a multiple of 256, else 2; B groups as the scale groups with 8
+  // waves, of 2 K-blocks with 4 (register budget).
+#define NVFP4_DOWN(ASC, KQ, WPB)                                                                          \
+  moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2>                                    \
+      <<<grid_for(max_tiles, H / (WPB * 64)), WPB * 64, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles, \
+                                                                tile_count, topk, I, H / (WPB * 64), down, down, w, y, H)
+#define NVFP4_DOWN_W(ASC, KQ) \
+  if (H % 512 == 0)           \
+    NVFP4_DOWN(ASC, KQ, 8);   \
+  else                        \
+    NVFP4_DOWN(ASC, KQ, 4);
   const bool q4 = I % 256 == 0;
   if (act == 0) {
-    if (q4)
-      NVFP4_DOWN(false, 4);
-    else
-      NVFP4_DOWN(false, 2);
+    if (q4) {
+      NVFP4_DOWN_W(false, 4)
+    } else {
+      NVFP4_DOWN_W(false, 2)
+    }
   } else {
-    if (q4)
-      NVFP4_DOWN(true, 4);
-    else
-      NVFP4_DOWN(true, 2);
+    if (q4) {
+      NVFP4_DOWN_W(true, 4)
+    } else {
+      NVFP4_DOWN_W(true, 2)
+    }
   }
+#undef NVFP4_DOWN_W
 #undef NVFP4_DOWN
   return hipGetLastError();
 }
