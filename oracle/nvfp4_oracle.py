@@ -257,14 +257,19 @@ def quant_rows_i8(x32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
-def w4a8_expert_ffn(xq: np.ndarray, Wg, gg, Wu, gu, Wd, gd) -> np.ndarray:
-    """Expert FFN on already-dequantized int8 activations x_hat = q * s (float64);
-    h is rounded to fp32, quantized per row to int8, and the down projection
-    consumes h_hat = q_h * s_h."""
+def w4a8_hidden(xq: np.ndarray, Wg, gg, Wu, gu) -> np.ndarray:
+    """The W4A8 expert's hidden rows on already-dequantized int8 activations
+    x_hat = q * s (float64): h = SiLU(gg * x Wg^T) * (gu * x Wu^T), rounded to fp32
+    (the value the down projection's int8 quantization starts from)."""
     g = (xq @ Wg.T) * gg
     u = (xq @ Wu.T) * gu
-    h = silu(g) * u
-    qh, sh = quant_rows_i8(h.astype(np.float32))
+    return (silu(g) * u).astype(np.float32)
+
+
+def w4a8_expert_ffn(xq: np.ndarray, Wg, gg, Wu, gu, Wd, gd) -> np.ndarray:
+    """Expert FFN on already-dequantized int8 activations: h (fp32) is quantized per
+    row to int8, and the down projection consumes h_hat = q_h * s_h."""
+    qh, sh = quant_rows_i8(w4a8_hidden(xq, Wg, gg, Wu, gu))
     hh = qh.astype(np.float64) * sh.astype(np.float64)[:, None]
     return (hh @ Wd.T) * gd
 
@@ -280,6 +285,27 @@ def moe_w4a8(x_bf16_bits: np.ndarray, layer, ids, w, rows=None) -> np.ndarray:
     """W4A8 MoE: both expert GEMMs take per-row int8 activations."""
     xh = w4a8_activations(x_bf16_bits)
     return moe_grouped(xh, layer, ids, w, rows=rows, ffn=w4a8_expert_ffn)
+
+
+def w4a8_pair_hidden(x_bf16_bits: np.ndarray, layer, ids, rows=None):
+    """For the routed pairs of the given token rows, expert by expert in route()
+    order: (expert id, sorted pair indices into ids[rows], fp32 hidden rows h, their
+    int8 scales s), i.e. the inputs of every requantization decision moe_w4a8 takes."""
+    xh = w4a8_activations(x_bf16_bits)
+    T, k = ids.shape
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    offsets, sp = route(ids[rows], layer.E)
+    out = []
+    for e in range(layer.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        pairs = sp[a:b]
+        Wg, gg, Wu, gu, _, _ = _expert(layer, e)
+        h = w4a8_hidden(xh[rows[pairs // k]], Wg, gg, Wu, gu)
+        _, s = quant_rows_i8(h)
+        out.append((e, pairs, h, s))
+    return out
 
 
 # ----------------------------------------------------------------- comparison
