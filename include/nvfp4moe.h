@@ -126,12 +126,13 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
  * strata-safetensors": the quality profile keeps canonical FP32 expert decode).
  * x [T][H] bf16; gate/up: N = I, K = H; down: N = H, K = I; out [T][H] in out_dtype
  * (F32 or BF16). ws needs nvfp4_moe_decode_workspace_size() bytes and must be
- * zero-filled before its first use (it holds a grid-barrier counter that every successful
- * call leaves ready for the next; zero it again if H changes or after an error). Bytes
+ * zero-filled before its first use (it holds a grid-barrier counter and per-block release
+ * flags that every successful call leaves ready for the next; zero it again if H changes
+ * or after an error). Bytes
  * 4..7 of ws hold an error word: bit 0 is set if a call's grid barrier timed out (the
  * output of that call is then invalid). The result does not depend on scheduling: every
  * output element is summed in a fixed order. Calls sharing one workspace must not
- * overlap. The whole call is one persistent launch when its grid (H/4 blocks) fits on the
+ * overlap. The whole call is one persistent launch when its grid (H/8 blocks) fits on the
  * device at once, else two launches with identical results.
  * Errors: EINVAL (null pointers, shapes that disagree, H or I not a multiple of 32,
  * topk < 1, E < 1); EUNSUPPORTED for x not bf16, T > 8, topk * T > 64, H or I above

@@ -72,13 +72,14 @@ PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
 }
 
 struct DecodeLayout {
-  size_t hdr, h, end;
+  size_t hdr, flags, h, end;
 };
 
-DecodeLayout decode_layout(int T, int I, int topk) {
+DecodeLayout decode_layout(int T, int H, int I, int topk) {
   Carver c;
   DecodeLayout l;
   l.hdr = c.take(64);
+  l.flags = c.take(decode_flag_bytes(H));
   l.h = c.take((size_t)T * topk * I * 4);
   l.end = c.off;
   return l;
@@ -158,7 +159,7 @@ size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t 
   (void)H;
   (void)E;
   if (T < 0 || I < 1 || topk < 1) return 0;
-  return decode_layout(T, I, topk).end;
+  return decode_layout(T, H, I, topk).end;
 }
 
 static int check_moe_common(const void* x, int32_t T, int32_t H, const nvfp4_weight* gate, const nvfp4_weight* up,
@@ -184,7 +185,7 @@ static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int3
   const int I = gate->N;
   if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > 8192 || I > 8192) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * H > kDecodeMaxTH) return NVFP4_EUNSUPPORTED;  // activations are staged in LDS
-  const DecodeLayout l = decode_layout(T, I, topk);
+  const DecodeLayout l = decode_layout(T, H, I, topk);
   if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
   if (T == 0) return NVFP4_OK;
   (void)hipGetLastError();
@@ -192,7 +193,7 @@ static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int3
   const int mode = (first == 0 && last == 1) ? 2 : first;
   hipError_t e = launch_decode(mode, x, T, H, I, to_args(gate), to_args(up), to_args(down), E, topk_ids,
                                topk_weights, topk, out, out_dtype, at<float>(ws, l.h), at<int32_t>(ws, l.hdr),
-                               as_stream(stream));
+                               at<unsigned long long>(ws, l.flags), as_stream(stream));
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

@@ -7,8 +7,8 @@
 //            bf16 activations into LDS.
 //   phase 1  gate/up + SwiGLU: units of (unique expert, 4 intermediate rows) are spread
 //            over all waves of the grid; h (fp32) goes to the workspace.
-//   barrier  one arrival per block on an agent-scope counter (release), a relaxed poll
-//            with a bounded spin, one acquire.
+//   barrier  one arrival per block on an agent-scope counter; the last arrival writes
+//            every block's release flag, each block polls its own (bounded spin).
 //   phase 2  down + top-k combine: block b owns output rows 8b .. 8b+7; every block
 //            copies h into LDS once; waves w and w+2, w+4, w+6 share a quad of rows and
 //            split the unique experts, each sums its experts' pairs in a fixed order, and
@@ -30,7 +30,7 @@ namespace nvfp4 {
 
 constexpr int kDecWaves = 8;     // waves per block
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kRowsPerBlock = 8;  // output rows per block in phase 2 (two quads of 4)
+constexpr int kRowsPerBlock = kDecodeRowsPerBlock;  // output rows per block in phase 2 (two quads of 4)
 constexpr int kUB = 4;            // down units (one expert x 4 rows) a wave loads at once
 
 struct DecodeSmem {
@@ -39,7 +39,8 @@ struct DecodeSmem {
   int list[64];   // pairs grouped by unique expert, each group in pair order
   int start[65];  // group boundaries in list
   float wp[64];   // router weight of each pair
-  int nu, drop, ok;
+  int nu, drop, ok, last;
+  unsigned long long target;
   float part[kDecWaves][4][kDecodeMaxT];
 };
 
@@ -68,6 +69,7 @@ struct DecodeArgs {
   int out_dtype;
   int32_t* hdr;                  // [0] dropped pairs, [1] error flags
   unsigned long long* barrier;   // grid barrier counter
+  unsigned long long* flags;     // grid barrier release flags, one 128-byte line per block
   int spin_limit;
   int h_in_lds;                  // phase 2 reads h from LDS (P * I * 4 bytes fit)
 };
@@ -100,29 +102,25 @@ __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x)
     const int ev = valid ? e : -1;
     sm.ids[tid] = ev;
     sm.wp[tid] = wv;
-    bool first = valid;
-#pragma unroll
-    for (int q = 0; q < 64; ++q) {
-      const int eq = __builtin_amdgcn_readlane(ev, q);  // lane q's id, no LDS round trip
-      if (q < tid && eq == ev) first = false;
-    }
+    // Group the pairs by expert, experts in order of first appearance: the lowest lane
+    // not yet grouped names the next expert (scalar bit scan + readlane, no LDS reads),
+    // a ballot finds all lanes holding it, ranks in lane order give the pair order.
     const uint64_t lt = (1ull << tid) - 1ull;
-    const uint64_t fm = __ballot(first);
+    uint64_t rem = __ballot(valid);
     const uint64_t dm = __ballot(tid < a.P && !valid);
-    const int nu = __popcll(fm);
-    // uniq[rank of my first appearance] = my id; then every lane reads the list back
-    if (first) sm.uniq[__popcll(fm & lt)] = ev;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    int start = 0;
-    for (int u = 0; u < nu; ++u) {
-      const int eu = sm.uniq[u];
+    int start = 0, nu = 0;
+    while (rem) {
+      const int eu = __builtin_amdgcn_readlane(ev, __builtin_ctzll(rem));
       const bool m = ev == eu;
       const uint64_t mm = __ballot(m);
       if (m) sm.list[start + __popcll(mm & lt)] = tid;
-      if (tid == 0) sm.start[u] = start;
+      if (tid == 0) {
+        sm.uniq[nu] = eu;
+        sm.start[nu] = start;
+      }
       start += __popcll(mm);
+      ++nu;
+      rem &= ~mm;
     }
     if (tid == 0) {
       sm.start[nu] = start;
@@ -348,10 +346,13 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
 
 // Grid barrier over gridDim.x co-resident blocks. h was stored write-through (agent
 // scope), so arrival only needs every wave's stores complete (vmcnt 0) before one
-// relaxed atomic per block; readers then load h with agent-coherent loads. The counter
-// only grows: the k-th arrival of a call sees old = base + k with base a multiple of
-// the grid size, so every block of the call waits for base + gridDim.x. Returns false
-// (and sets bit 0 of hdr[1]) if the wait exceeds the spin limit, so every wave exits.
+// relaxed atomic per block. The counter only grows: the k-th arrival of a call sees
+// old = base + k with base a multiple of the grid size, so the call's target is
+// base + gridDim.x. The block that completes the count writes the target into every
+// block's flag (one 128-byte line each, so the waiting blocks poll different lines
+// instead of all polling the counter); a block waits until its flag reaches the target.
+// Readers then load h with agent-coherent loads. Returns false (and sets bit 0 of
+// hdr[1]) if the wait exceeds the spin limit, so every wave exits.
 __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
@@ -360,16 +361,27 @@ __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
     const unsigned long long old =
         __hip_atomic_fetch_add(a.barrier, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long target = (old / G + 1) * G;
-    int ok = 1;
+    sm.target = target;
+    sm.last = old + 1 == target;
+    sm.ok = 1;
+  }
+  __syncthreads();
+  const unsigned long long target = sm.target;
+  if (sm.last) {
+    for (unsigned b = threadIdx.x; b < gridDim.x; b += kDecThreads)
+      __hip_atomic_store(a.flags + (size_t)b * 16, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  if (threadIdx.x == 0) {
+    const unsigned long long* f = a.flags + (size_t)blockIdx.x * 16;
     int n = 0;
-    while (__hip_atomic_load(a.barrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (++n > a.spin_limit) {
-        ok = 0;
+        sm.ok = 0;
         __hip_atomic_fetch_or(a.hdr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    sm.ok = ok;
   }
   __syncthreads();
   return sm.ok != 0;
@@ -476,7 +488,7 @@ static hipError_t launch_decode_t(int stage, const DecodeArgs& a, hipStream_t st
 
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
                          const WeightArgs& down, int E, const int32_t* ids, const float* w, int topk, void* out,
-                         int out_dtype, float* h, int32_t* hdr, hipStream_t st) {
+                         int out_dtype, float* h, int32_t* hdr, unsigned long long* flags, hipStream_t st) {
   DecodeArgs a;
   a.x = reinterpret_cast<const uint16_t*>(x);
   a.T = T; a.H = H; a.I = I; a.E = E; a.P = T * topk; a.topk = topk;
@@ -484,6 +496,7 @@ hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const We
   a.ids = ids; a.w = w; a.h = h; a.out = out; a.out_dtype = out_dtype;
   a.hdr = hdr;
   a.barrier = reinterpret_cast<unsigned long long*>(hdr + 4);
+  a.flags = flags;
   a.spin_limit = 1 << 22;
   a.h_in_lds = 0;
   a.h_in_lds = decode_lds_bytes(a) + h_lds_bytes(a.P, I) <= kDecLdsBudget ? 1 : 0;

@@ -54,10 +54,14 @@ constexpr int kDecodeMaxPairs = 64;
 constexpr int kDecodeMaxTH = 40960;  // T * H: the bf16 activations of a block live in LDS
 // stage 0: gate/up + SwiGLU; 1: down + combine; 2: both in one persistent launch (falls
 // back to 0 then 1 when the grid cannot be co-resident). hdr: [0] dropped pairs,
-// [1] error flags, [4..5] the grid-barrier counter (zero before first use).
+// [1] error flags, [4..5] the grid-barrier counter; flags: decode_flag_bytes(H) of
+// per-block release flags (counter and flags zero before first use).
+constexpr int kDecodeRowsPerBlock = 8;
+inline size_t decode_flag_bytes(int H) { return (size_t)((H + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock) * 128; }
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
                          const WeightArgs& down, int E, const int32_t* ids, const float* w, int topk,
-                         void* out, int out_dtype, float* h, int32_t* hdr, hipStream_t st);
+                         void* out, int out_dtype, float* h, int32_t* hdr, unsigned long long* flags,
+                         hipStream_t st);
 
 // prefill.hip
 constexpr int kTileM = 128;

@@ -377,7 +377,9 @@ def test_graph_replays_match_eager(kind):
         if kind == "prefill":
             ws.fill_(0xA5)  # every prefill call rewrites its whole workspace
         else:
-            ws[64:].fill_(0xA5)  # decode keeps its grid-barrier counter in the header
+            # decode keeps its grid-barrier state (counter, release flags) at the front of
+            # the workspace; its scratch h (T * 8 * I fp32) is the tail
+            ws[ws.numel() - T * 8 * dl.I * 4:].fill_(0xA5)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
