@@ -89,11 +89,18 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 // ---------------------------------------------------------------- wave reductions
 // Sum over groups of 16 consecutive lanes (every lane of the group gets the total).
+// Sum over each row of 16 lanes (lanes 16r .. 16r+15), the result in all 16 lanes, with
+// DPP moves (VALU only, no LDS crossbar): swap neighbours, swap pairs, then rotate the
+// row by 4 and by 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x124>(v);  // row_ror:4
+  v += dpp_mov<0x128>(v);  // row_ror:8
   return v;
 }
 

@@ -427,8 +427,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) {
-    const float v = sum16(acc[t]);
-    if (l16 == 0) sm.part[wave][lane >> 4][t] = v;
+    if (t < a.T) {
+      const float v = sum16(acc[t]);
+      if (l16 == 0) sm.part[wave][lane >> 4][t] = v;
+    }
   }
   __syncthreads();
   if (tid < kRowsPerBlock * a.T) {
