@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run device-to-device copies of 1 GiB (the plain copy kernel whose HBM "
+                         "counter readings scale the GEMM's FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -156,6 +159,49 @@ def bench_decode(layers, index, rounds):
                 gbs_down=U * 768 * 2048 * 9 / 16 / (res["down"] * 1e-6) / 1e9)
 
 
+# Kernel sources whose hash a traffic profile records: counters taken on other sources
+# no longer describe the kernel and are not reported.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gateup_t8192_zipf_traffic.md")
+TRAFFIC_SOURCES = ["nvfp4_quantized_moe_02_amd/csrc/prefill.hip", "nvfp4_quantized_moe_02_amd/csrc/common.h",
+                   "nvfp4_quantized_moe_02_amd/csrc/kernels.h"]
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def gemm_traffic():
+    """HBM bytes per gate/up launch from the committed counter profile, or None when the
+    profile is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if line.startswith("traffic-record: "):
+                    rec = json.loads(line[len("traffic-record: "):])
+                    if rec.get("source_hash") == source_hash():
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
+def copy_calibration():
+    """Device-to-device copies of exactly 1 GiB each (read 1 GiB, write 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 4, "source_hash": source_hash()}), flush=True)
+
+
 def cpu_baseline(n_tokens):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -179,6 +225,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import nvfp4_quantized_moe_02_amd as nv
     import workloads as W
@@ -220,6 +269,7 @@ def main():
         gu_ms = pre["stages_ms"][1]
         dn_ms = pre["stages_ms"][2]
         achieved = pre["gu_flops"] / (gu_ms * 1e-3) / 1e12
+        trec = gemm_traffic()
         result = {
             "metric": "NVFP4 MoE layer: prefill tokens/s (% MFMA peak); decode HBM GB/s (% peak)",
             "value": round(pre["tokens_per_s"], 1),
@@ -241,7 +291,11 @@ def main():
                        "layers_rotated": args.layers},
             "roofline": {"bound": "mfma", "kernel": "moe_gemm_f16_kernel (gate/up + SwiGLU)",
                          "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None},
+                         "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                         "traffic": trec["hbm_bytes_per_launch"] if trec else None,
+                         "traffic_source": (f"rocprofv3 FETCH_SIZE + WRITE_SIZE per gate/up launch, scaled by "
+                                            f"a 1 GiB copy ({os.path.relpath(TRAFFIC_PROFILE, ROOT)})")
+                                           if trec else "no counter profile for the current kernel sources"},
             "prefill_detail": {
                 "stage_ms": {"route_stage": round(pre["stages_ms"][0], 4), "gateup": round(gu_ms, 4),
                              "down": round(dn_ms, 4), "finalize": round(pre["stages_ms"][3], 4)},
