@@ -183,39 +183,6 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols,
 
 // ------------------------------------------------------------------ activation staging
 // bf16 -> fp16 (round to nearest even; exact for |x| in the fp16 normal range).
-// Zero fill (a kernel rather than a memset node, so the sequence can be graph-captured).
-__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    p[i] = make_uint4(0, 0, 0, 0);
-}
-
-hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st) {
-  const int64_t n16 = bytes / 16;
-  if (n16 == 0) return hipSuccess;
-  int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  zero_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(reinterpret_cast<uint4*>(p), n16);
-  return hipGetLastError();
-}
-
-// fp32 accumulator -> output dtype (bf16: round to nearest even).
-__global__ __launch_bounds__(256) void finalize_bf16_kernel(const float4* __restrict__ acc, uint2* __restrict__ out,
-                                                            int64_t n4) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  float4 v = acc[i];
-  out[i] = make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
-                      (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
-}
-
-hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st) {
-  const int64_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
-  finalize_bf16_kernel<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
-      reinterpret_cast<const float4*>(acc), reinterpret_cast<uint2*>(out), n4);
-  return hipGetLastError();
-}
-
 // Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic. All
 // slot loads are issued before the first add (an absent slot reads row 0 and adds nothing);
 // y is read once, so its loads are non-temporal.

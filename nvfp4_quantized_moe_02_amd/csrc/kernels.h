@@ -25,8 +25,6 @@ hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes
                          const float* global, int N, int K, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
                              float* scale, hipStream_t st);
-hipError_t launch_zero(void* p, int64_t bytes, hipStream_t st);
-hipError_t launch_finalize_bf16(const float* acc, void* out, int64_t n, hipStream_t st);
 // out[t][n] = sum over slots j (in order) of y[inv[t*topk + j]][n]; dropped slots skipped.
 hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, int H, void* out, int out_dtype,
                           hipStream_t st);
