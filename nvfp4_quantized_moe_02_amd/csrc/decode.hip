@@ -284,10 +284,17 @@ struct DownRows {
   uint4 c[kUB][CH];
   uint32_t s[kUB][CH];
   float gd[kUB];  // global scales of the experts, loaded with their rows
+  // the experts' pairs: list positions [ps, pe); the first pair and its router weight are
+  // read here, ahead of the h exchange, so phase 2 starts without an LDS round trip
+  int ps[kUB], pe[kUB], p0[kUB];
+  float w0[kUB];
 };
 
 __device__ __forceinline__ int down_expert(int wave, int ub) { return (wave >> 1) + 4 * ub; }
 
+// Loads the weight chunks of this wave's experts ub0 .. ub0+kUB-1 for output row `row`;
+// experts beyond the unique list get an empty pair range and rows beyond H zero codes,
+// scales and global scale (they add exactly 0).
 template <int CH>
 __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
                                           DownRows<CH>& d) {
@@ -296,51 +303,69 @@ __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem&
 #pragma unroll
   for (int b = 0; b < kUB; ++b) {
     const int u = down_expert(wave, ub0 + b);
-    if (u < sm.nu && row < a.H) {
-      d.gd[b] = a.down.global[sm.uniq[u]];
-      const size_t grow = (size_t)sm.uniq[u] * a.H + row;
-      const uint8_t* rc = a.down.codes + grow * (a.I / 2);
-      const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scales + grow * (a.I / 16));
+    const bool have = u < sm.nu;
+    d.ps[b] = have ? sm.start[u] : 0;
+    d.pe[b] = have ? sm.start[u + 1] : 0;
+    d.p0[b] = have ? sm.list[d.ps[b]] : 0;
+    d.w0[b] = have ? sm.wp[d.p0[b]] : 0.f;
+    const bool ok = have && row < a.H;
+    d.gd[b] = ok ? a.down.global[sm.uniq[u]] : 0.f;
+    const size_t grow = ok ? (size_t)sm.uniq[u] * a.H + row : 0;
+    const uint8_t* rc = a.down.codes + grow * (a.I / 2);
+    const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scales + grow * (a.I / 16));
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int ch = l16 + 16 * c;
-        if (ch < nch) {
-          d.c[b][c] = *reinterpret_cast<const uint4*>(rc + ch * 16);
-          d.s[b][c] = rs[ch];
-        }
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int ch = l16 + 16 * c;
+      const bool ld = ok && ch < nch;
+      d.c[b][c] = ld ? *reinterpret_cast<const uint4*>(rc + ch * 16) : make_uint4(0, 0, 0, 0);
+      d.s[b][c] = ld ? (uint32_t)rs[ch] : 0u;
     }
   }
 }
 
+// One pair's partial dot products for this lane's chunks: all h reads are issued before
+// the arithmetic (chunks past I read chunk 0 and meet zero weights).
 template <int CH, bool HLDS>
-__device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
-                                           const DownRows<CH>& d, float (&acc)[kDecodeMaxT]) {
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ float down_pair(const DecodeArgs& a, const DownRows<CH>& d, int b, int p, int l16,
+                                           int xb) {
   const int nch = a.I >> 5;
+  float part = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ch = l16 + 16 * c < nch ? l16 + 16 * c : 0;
+    const float* hp = HLDS ? h_lds_chunk(xb, p, a.I, ch) : a.h + (size_t)p * a.I + ch * 32;
+    part += dot_chunk_f32(d.c[b][c], d.s[b][c], hp);
+  }
+  return part;
+}
+
+template <int CH, bool HLDS>
+__device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem& sm, const DownRows<CH>& d,
+                                           int l16, float (&acc)[kDecodeMaxT]) {
   const int xb = (int)x_lds_bytes(a.T, a.H);
 #pragma unroll
   for (int b = 0; b < kUB; ++b) {
-    const int u = down_expert(wave, ub0 + b);
-    if (u >= sm.nu) break;
-    const float gd = d.gd[b];
-    for (int i = sm.start[u]; i < sm.start[u + 1]; ++i) {
-      const int p = sm.list[i];
+    if (d.ps[b] >= d.pe[b]) break;  // uniform: this wave has no expert b (nor later ones)
+    {
+      const int p = d.p0[b];
+      const float part = down_pair<CH, HLDS>(a, d, b, p, l16, xb);
       const int t = p / a.topk;
-      float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int ch = l16 + 16 * c;
-        if (ch < nch && row < a.H) {
-          const float* hp = HLDS ? h_lds_chunk(xb, p, a.I, ch) : a.h + (size_t)p * a.I + ch * 32;
-          part += dot_chunk_f32(d.c[b][c], d.s[b][c], hp);
-        }
-      }
-      const float coef = sm.wp[p] * gd;
+      const float coef = d.w0[b] * d.gd[b];
 #pragma unroll
       for (int tt = 0; tt < kDecodeMaxT; ++tt)
         if (tt == t) acc[tt] = fmaf(coef, part, acc[tt]);
     }
+    for (int i = d.ps[b] + 1; i < d.pe[b]; ++i) {
+      const int p = sm.list[i];
+      const float part = down_pair<CH, HLDS>(a, d, b, p, l16, xb);
+      const int t = p / a.topk;
+      const float coef = sm.wp[p] * d.gd[b];
+#pragma unroll
+      for (int tt = 0; tt < kDecodeMaxT; ++tt)
+        if (tt == t) acc[tt] = fmaf(coef, part, acc[tt]);
+    }
+    // one expert's h reads in flight at a time (keeps the register count down)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -422,8 +447,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   const int per_wave = (sm.nu - (wave >> 1) + 3) / 4;  // experts of this wave
   for (int ub0 = 0; ub0 < per_wave; ub0 += kUB) {
     if (ub0 > 0) down_load<CHD>(a, sm, ub0, row, l16, d);
-    if (a.h_in_lds) down_accum<CHD, true>(a, sm, ub0, row, l16, d, acc);
-    else down_accum<CHD, false>(a, sm, ub0, row, l16, d, acc);
+    if (a.h_in_lds) down_accum<CHD, true>(a, sm, d, l16, acc);
+    else down_accum<CHD, false>(a, sm, d, l16, acc);
   }
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) {
