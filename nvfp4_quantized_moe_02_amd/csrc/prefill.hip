@@ -9,13 +9,13 @@
 // template parameter, so partial tiles skip the empty row blocks without branches in the
 // K loop.
 //
-// A operand (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into
-// registers and stored to a 2-stage LDS ring at the top of the iteration that uses it.
+// A (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into registers and
+// stored to a 2-stage LDS ring at the top of the iteration that uses it.
 // Each LDS row holds 64 inputs (8 slots of 16 bytes); slot c of row r holds chunk
 // c ^ (r & 7), so the 32 rows of an MFMA fragment read hit 8 distinct slots (no bank
 // conflicts). Rows are gathered by token for gate/up and contiguous for down.
 //
-// B operand (NVFP4 weights): the block stages its weight rows' codes GK K-blocks at a
+// B (NVFP4 weights): the block stages its weight rows' codes GK K-blocks at a
 // time with coalesced loads (consecutive threads read one row's GK*32 contiguous bytes)
 // one group ahead in registers, stores each group to an XOR-swizzled LDS tile, and every
 // lane reads its fragment's 16 code bytes per K-block from there. Each lane loads its
@@ -26,11 +26,19 @@
 // takes inputs 0..31, half 1 inputs 32..63); A is read with the same permutation, so the
 // dot products are unchanged.
 //
+// Inside a K-block each lane reads its A fragments two ahead of their MFMAs (the LDS
+// latency hides under the MFMAs in between), unpacks the B fragments of the next step
+// right after issuing the current step's last MFMA, and issues the global loads of later
+// K-blocks spread over the MFMAs: all waves issuing them in one burst after the barrier
+// made each wave queue in the address unit before its first MFMA.
+//
 // gate/up: wave w computes gate and up for the same 32 intermediate indices, so SwiGLU
 // runs in registers: h = SiLU(gamma_g * g) * (gamma_u * u) (gate scale before SiLU, the
-// "Strata NVFP4" README's per-projection output scale). down: the epilogue multiplies by
-// gamma_d and the router weight and writes each pair's fp32 row; a separate combine sums
-// the slots of each token in slot order, so the result is deterministic.
+// "Strata NVFP4" README's per-projection output scale); the weights are the MFMA's first
+// operand, so each lane ends with four adjacent h values of a row and stores them directly.
+// down: the epilogue multiplies by gamma_d and the router weight and writes each pair's
+// fp32 row through LDS as whole 1 KB row segments; a separate combine sums the slots of
+// each token in slot order, so the result is deterministic.
 #include <type_traits>
 
 #include "kernels.h"
@@ -97,8 +105,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
                                           const uint8_t* b0row, const uint8_t* b1row,
                                           const uint8_t* const* bs, const WeightArgs& w0,
                                           const WeightArgs& w1, void* __restrict__ out, int ldo, char* lds,
-                                          const int* s_src, const int* s_tok, const float* s_coef) {
-  (void)s_tok;
+                                          const int* s_src, const float* s_coef) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nkb = K / KBLK;
@@ -204,31 +211,58 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
       for (int j = 0; j < BT::CH; ++j)
         *reinterpret_cast<uint4*>(btiles + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < BT::CH; ++j) bg[j] = load_bg(kb / GK + 1, j);
     }
     const char* btile = btiles;
+    // The next B group (at a group start) and A(kb+2) are loaded spread over the MFMAs of
+    // this K-block: a burst of loads from every wave right after the barrier queues in the
+    // address unit and holds back each wave's first MFMAs.
+    constexpr int NBL = (Q % GK == 0) ? BT::CH : 0;
+    constexpr int NLD = NBL + NA;
+    auto issue_loads = [&](int idx, int nf) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) aq[R][i] = load_a(kb + 2, i);
-    // keep the loads here: sunk or reordered loads shorten the prefetch distance and make
-    // the loop-header wait counts pessimistic
-    __builtin_amdgcn_sched_barrier(0);
+      for (int g = 0; g < NLD; ++g) {
+        if (g * nf / NLD == idx) {
+          if (g < NBL) bg[g < NBL ? g : 0] = load_bg(kb / GK + 1, g < NBL ? g : 0);
+          else aq[R][g - NBL] = load_a(kb + 2, g - NBL);
+        }
+      }
+    };
     constexpr int q = Q % GK;  // K-block within the B group: chunks 2q (half 0), 2q+1 (half 1)
     const uint4 cur0 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow0, 2 * q + half));
     const uint4 cur1 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow1, 2 * q + half));
     const f16x2_t s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
     const f16x2_t s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
+    // A fragments are read LA fragments ahead of their MFMAs (a ring of LA+1), so the LDS
+    // latency of each read hides under the MFMAs issued in between; the B fragments of
+    // step s+1 are unpacked right after the last MFMA of step s is issued.
+    constexpr int NF = 4 * NRB, LA = 2;
+    f16x8_t ring[LA + 1];
+    auto read_a = [&](int idx) -> f16x8_t {
+      const int s = idx / NRB, rb = idx % NRB;
+      const int row = rb * 32 + l32, chunk = half * 4 + s;
+      return *reinterpret_cast<const f16x8_t*>(st + row * 128 + ((chunk ^ (row & 7)) << 4));
+    };
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8_t b0 = bfrag(word_of(cur0, s), s0[s >> 1]);
-      const f16x8_t b1 = bfrag(word_of(cur1, s), s1[s >> 1]);
-      const int chunk = half * 4 + s;
+    for (int i = 0; i < LA; ++i) ring[i] = read_a(i);
+    f16x8_t b0 = bfrag(word_of(cur0, 0), s0[0]);
+    f16x8_t b1 = bfrag(word_of(cur1, 0), s1[0]);
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int row = rb * 32 + l32;
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(st + row * 128 + ((chunk ^ (row & 7)) << 4));
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[rb][1], 0, 0, 0);
+    for (int idx = 0; idx < NF; ++idx) {
+      if (idx + LA < NF) ring[(idx + LA) % (LA + 1)] = read_a(idx + LA);
+      issue_loads(idx, NF);
+      __builtin_amdgcn_sched_barrier(0);
+      const int s = idx / NRB, rb = idx % NRB;
+      // gate/up: weights as the first operand (output-major accumulators, see the epilogue)
+      if constexpr (GATEUP) {
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, ring[idx % (LA + 1)], acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, ring[idx % (LA + 1)], acc[rb][1], 0, 0, 0);
+      } else {
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[idx % (LA + 1)], b0, acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[idx % (LA + 1)], b1, acc[rb][1], 0, 0, 0);
+      }
+      if (rb == NRB - 1 && s < 3) {
+        b0 = bfrag(word_of(cur0, s + 1), s0[(s + 1) >> 1]);
+        b1 = bfrag(word_of(cur1, s + 1), s1[(s + 1) >> 1]);
       }
     }
   };
@@ -255,45 +289,35 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   }
 
   if constexpr (GATEUP) {
+    // The weights are the first MFMA operand, so element v of acc[rb][cb] is intermediate
+    // index 8*(v/4) + 4*half + v%4 of the wave's 32, for token row rb*32 + l32: four
+    // consecutive v are four adjacent h values of one row, stored as one 8-byte (fp16) or
+    // 16-byte (fp32) piece straight to memory.
     const float gg = w0.global[tc.e], gu = w1.global[tc.e];
-    if (!HOUT32) {
-      // fp16 h through LDS: [rows][NC intermediate indices], 16-byte chunks XOR-swizzled by
-      // row; then every thread stores whole 16-byte chunks (2*NC contiguous bytes per row).
-      constexpr int NC = WPB * 32;
-      __syncthreads();  // every wave is done with the A stages
-      uint16_t* hl = reinterpret_cast<uint16_t*>(lds);
-      const int col = wave * 32 + l32;
+    const int col0 = tc.nb * (WPB * 32) + wave * 32 + 4 * half;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = rb * 32 + l32;
+      const float xs = s_coef[r];
+      const float cg = xs * gg, cu = xs * gu;
+      const size_t rowoff = (size_t)(tc.base + tc.m0 + r) * ldo + col0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          const float xs = s_coef[r];
-          const float hv = silu_fast(acc[rb][0][i] * (xs * gg)) * (acc[rb][1][i] * (xs * gu));
-          hl[r * NC + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f32_to_f16_bits(hv);
-        }
-      __syncthreads();
-      uint16_t* h = reinterpret_cast<uint16_t*>(out);
-      constexpr int CPR = NC / 8;  // 16-byte chunks per row
-      for (int k = tid; k < NRB * 32 * CPR; k += WPB * 64) {
-        const int r = k / CPR, c = k % CPR;
-        if (r < tc.rows)
-          *reinterpret_cast<uint4*>(h + (size_t)(tc.base + tc.m0 + r) * ldo + tc.nb * NC + c * 8) =
-              *reinterpret_cast<const uint4*>(hl + r * NC + ((c ^ (r & 15)) << 3));
-      }
-    } else {
-      const int jcol = tc.nb * (WPB * 32) + wave * 32 + l32;
+      for (int g = 0; g < 4; ++g) {
+        float hv[4];
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = rb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (r < tc.rows) {
-            const float xs = s_coef[r];
-            const float hv = silu_fast(acc[rb][0][i] * (xs * gg)) * (acc[rb][1][i] * (xs * gu));
-            reinterpret_cast<float*>(out)[(size_t)(tc.base + tc.m0 + r) * ldo + jcol] = hv;
+        for (int v = 0; v < 4; ++v)
+          hv[v] = silu_fast(acc[rb][0][4 * g + v] * cg) * (acc[rb][1][4 * g + v] * cu);
+        if (r < tc.rows) {
+          if constexpr (HOUT32) {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + rowoff + 8 * g) =
+                f32x4_t{hv[0], hv[1], hv[2], hv[3]};
+          } else {
+            const uint2 pk = {(uint32_t)f32_to_f16_bits(hv[0]) | ((uint32_t)f32_to_f16_bits(hv[1]) << 16),
+                              (uint32_t)f32_to_f16_bits(hv[2]) | ((uint32_t)f32_to_f16_bits(hv[3]) << 16)};
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + rowoff + 8 * g) = pk;
           }
         }
+      }
     }
   } else {
     // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order; the combine kernel sums
@@ -341,14 +365,12 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
     void* __restrict__ out, int ldo) {
-  // A stages and the B tile; the epilogue reuses them (gate/up fp16 h transpose: rows x
-  // WPB*32 fp16; down: 32 rows x WPB*64 fp32)
+  // A stages and the B tile; the down epilogue reuses them (32 rows x WPB*64 fp32)
   constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, GK>::BYTES;
-  constexpr int kEpi = GATEUP ? (HOUT32 ? 0 : BM * WPB * 64) : 32 * WPB * 64 * 4;
+  constexpr int kEpi = GATEUP ? 0 : 32 * WPB * 64 * 4;
   constexpr int kLds = kMain > kEpi ? kMain : kEpi;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_src[BM];
-  __shared__ int s_tok[BM];
   __shared__ float s_coef[BM];
 
   // XCD-aware order: consecutive logical tiles (the N blocks of one row tile, then the
@@ -380,7 +402,6 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
       s_coef[tid] = ASCALE ? a_scale[p / topk] : 1.0f;
     } else {
       s_src[tid] = pos;
-      s_tok[tid] = p / topk;
       s_coef[tid] = route_w[p] * (ASCALE ? a_scale[pos] : 1.0f);
     }
   }
@@ -406,17 +427,13 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
 
   const int nrb = (tc.rows + 31) >> 5;
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
-                                                   s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
-                                                   s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
-                                                   s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_tok,
-                                                   s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -430,8 +447,8 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
                               const WeightArgs& up, void* h, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a);
-  // 8 waves (256 intermediate indices per block, B groups of 4 K-blocks) when I allows,
-  // else 4 waves (groups of 2); H is a multiple of 256, so scale groups of 4 K-blocks.
+  // 8 waves (256 intermediate indices per block) when I allows, else 4 (128); H is a
+  // multiple of 256, so scale groups of 4 K-blocks; B groups of 2 K-blocks.
 #define NVFP4_GU(ASC, H32, WPB, GK)                                                                      \
   moe_gemm_f16_kernel<true, ASC, H32, 4, WPB, GK><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>( \
       A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, nullptr, h, I)
@@ -458,8 +475,7 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
   if (max_tiles == 0) return hipSuccess;
   const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
   // 8 waves (512 outputs per block) when H allows, else 4 (256); scale groups of 4
-  // K-blocks when I is a multiple of 256, else 2; B groups as the scale groups with 8
-  // waves, of 2 K-blocks with 4 (register budget).
+  // K-blocks when I is a multiple of 256, else 2; B groups of 2 K-blocks.
 #define NVFP4_DOWN(ASC, KQ, WPB)                                                                          \
   moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2>                                    \
       <<<grid_for(max_tiles, H / (WPB * 64)), WPB * 64, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles, \
