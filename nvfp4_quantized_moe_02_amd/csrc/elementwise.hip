@@ -167,9 +167,77 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
   if (threadIdx.x == 0) scale[r] = s;
 }
 
+// The same quantization with one wave per row and 8 elements per access (16-byte loads of
+// bf16, two of fp32; 16-byte fp16 or 8-byte int8 stores): cols % 8 == 0 and aligned rows.
+// The row is read twice; the second read comes from cache.
+template <int XT, int OUTQ>
+__global__ __launch_bounds__(256) void quant_rows_vec_kernel(const void* __restrict__ x, int64_t rows, int cols,
+                                                             void* __restrict__ q, float* __restrict__ scale) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63, nch = cols >> 3;
+  auto load8 = [&](int ch, float* v) {
+    if (XT == 1) {
+      const uint4 w = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + r * cols)[ch];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_lo(u[j]);
+        v[2 * j + 1] = bf16_hi(u[j]);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + r * cols) + 2 * ch;
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  };
+  float m = 0.f;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float v[8];
+    load8(ch, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  const float s = m / 127.0f;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float v[8];
+    load8(ch, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s > 0.f ? fminf(fmaxf(rintf(v[j] / s), -127.f), 127.f) : 0.f;
+    if (OUTQ == 0) {
+      uint32_t w[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j >> 2] |= ((uint32_t)(int)v[j] & 0xFFu) << (8 * (j & 3));
+      reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(q) + r * cols)[ch] = make_uint2(w[0], w[1]);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)f32_to_f16_bits(v[2 * j]) | ((uint32_t)f32_to_f16_bits(v[2 * j + 1]) << 16);
+      reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(q) + r * cols)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  if (lane == 0) scale[r] = s;
+}
+
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
                              float* scale, hipStream_t st) {
   if (rows == 0) return hipSuccess;
+  const bool vec = cols % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(q) % (q_f16 ? 16 : 8) == 0;
+  if (vec) {
+    const dim3 g((unsigned)((rows + 3) / 4));
+    if (x_dtype == 1) {
+      if (q_f16) quant_rows_vec_kernel<1, 1><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
+      else quant_rows_vec_kernel<1, 0><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
+    } else {
+      if (q_f16) quant_rows_vec_kernel<0, 1><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
+      else quant_rows_vec_kernel<0, 0><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
+    }
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)rows);
   if (x_dtype == 1) {
     if (q_f16) quant_rows_kernel<1, 1><<<grid, 256, 0, st>>>(x, cols, q, scale);

@@ -135,6 +135,15 @@ def test_quant_rows_bit_exact():
     rq, rs = O.quant_rows_i8(x)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), rq)
+    # the one-block-per-row kernel (cols not a multiple of 8) and the one-wave-per-row kernel
+    # with more than 64 chunks of 8 per row
+    rng = np.random.default_rng(2)
+    for shape in ((37, 12), (9, 776)):
+        x = (rng.standard_normal(shape) * rng.uniform(1e-3, 1e2, (shape[0], 1))).astype(np.float32)
+        q, s = nv.quant_rows_i8(torch.from_numpy(x).to(DEV))
+        rq, rs = O.quant_rows_i8(x)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(q.cpu().numpy(), rq)
 
 
 # ------------------------------------------------------------------ decode
