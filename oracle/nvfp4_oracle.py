@@ -26,6 +26,12 @@ Sources (the pages, by title and section):
   [FP4-L]    #2727 "tools: add opt-in FP4-Local CSF checkpoint conversion",
              Validation list: expert tensors stack 512 experts; three-expert
              CUDA parity on relative output error.
+  [S-MIX]    "Strata NVFP4" README, the re-quantized experts pack: in 27 of the
+             48 layers the down projection is Q8_0 (more bytes, less error).
+             The pages name the format but not its bytes; this oracle takes
+             GGML's Q8_0 element rule: blocks of 32 int8 weights along the
+             inputs, one fp16 scale d per block, weight = d * q (exact in
+             float64: 8 + 11 significant bits).
 Element formats are the public OCP Microscaling definitions that NVFP4 uses:
 E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit, no inf/NaN) and
 FP8 E4M3 "FN" (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no inf,
@@ -51,6 +57,9 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 GROUP = 16
+
+
+Q8_BLOCK = 32
 
 
 # ----------------------------------------------------------------- element codecs
@@ -163,12 +172,28 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def dequant_q8_0(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Q8_0 rows [S-MIX]: codes int8 [..][K], scales fp16 bit patterns (uint16)
+    [..][K/32]; W[n][k] = fp16(scales[n][k // 32]) * codes[n][k], exact in float64."""
+    q = np.asarray(codes, dtype=np.int8).astype(np.float64)
+    d = np.asarray(scales, dtype=np.uint16).view(np.float16).astype(np.float64)
+    K = q.shape[-1]
+    assert K % Q8_BLOCK == 0 and d.shape[-1] * Q8_BLOCK == K
+    return q * np.repeat(d, Q8_BLOCK, axis=-1)
+
+
+def _dequant_proj(proj, s: int) -> np.ndarray:
+    if getattr(proj, "fmt", "nvfp4") == "q8_0":
+        return dequant_q8_0(proj.codes[s], proj.scales[s])
+    return dequant(proj.codes[s], proj.scales[s])
+
+
 def _expert(layer, e: int):
     s = layer.slot(e)
     return (
-        dequant(layer.gate.codes[s], layer.gate.scales[s]), float(layer.gate.gamma[s]),
-        dequant(layer.up.codes[s], layer.up.scales[s]), float(layer.up.gamma[s]),
-        dequant(layer.down.codes[s], layer.down.scales[s]), float(layer.down.gamma[s]),
+        _dequant_proj(layer.gate, s), float(layer.gate.gamma[s]),
+        _dequant_proj(layer.up, s), float(layer.up.gamma[s]),
+        _dequant_proj(layer.down, s), float(layer.down.gamma[s]),
     )
 
 

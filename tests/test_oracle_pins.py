@@ -427,3 +427,106 @@ def test_negative_controls_are_caught(monkeypatch):
     s = np.float32(12.7) / np.float32(127)
     q64 = np.rint(x.astype(np.float64) / float(s))
     assert q64[0, 1] == -63 and O.quant_rows_i8(x)[0][0, 1] == -64
+
+
+# ------------------------------------------------------------------ Q8_0 down projection
+def _fp16_value(bits):
+    """IEEE binary16 value of a bit pattern, as an exact Fraction (by the definition)."""
+    s, e, m = (bits >> 15) & 1, (bits >> 10) & 0x1F, bits & 0x3FF
+    assert e != 0x1F
+    v = Fraction(m, 1024) * Fraction(2) ** -14 if e == 0 else (1 + Fraction(m, 1024)) * Fraction(2) ** (e - 15)
+    return -v if s else v
+
+
+def test_q8_0_dequant_bruteforce_all_codes():
+    """Every int8 code with normal, subnormal, negative and zero fp16 scales, against the
+    exact rational product; scale b covers inputs 32b .. 32b+31."""
+    scale_bits = [0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x1C00, 0x3C00, 0x3555, 0x7BFF, 0xBC00, 0xC4D2, 0x2E66]
+    K = 256 * len(scale_bits)
+    codes = np.tile(np.arange(-128, 128, dtype=np.int16), len(scale_bits))
+    # element k takes scale k // 32: repeat each scale over 8 blocks of 32 = 256 codes
+    scales = np.repeat(np.array(scale_bits, np.uint16), 8)
+    got = O.dequant_q8_0(codes.astype(np.int8)[None], scales[None])[0]
+    assert got.shape == (K,)
+    for k in range(K):
+        want = _fp16_value(int(scales[k // 32])) * int(codes[k])
+        assert Fraction(got[k]) == want, (k, got[k], want)
+
+
+def test_q8_0_layout_hand():
+    """Hand example, K = 64: row 1, input 40 is code -3 with scale 2^-3 (block 1)."""
+    codes = np.zeros((2, 64), np.int8)
+    scales = np.zeros((2, 2), np.uint16)
+    codes[1, 40], codes[1, 31], codes[0, 32] = -3, 7, 5
+    scales[1] = [0x3C00, 0x3000]   # 1.0, 0.125
+    scales[0] = [0x4000, 0x4400]   # 2.0, 4.0
+    W_ = O.dequant_q8_0(codes, scales)
+    assert W_[1, 40] == -0.375 and W_[1, 31] == 7.0 and W_[0, 32] == 20.0
+    assert np.count_nonzero(W_) == 3
+
+
+def _paired_nvfp4_and_q8(seed, E, N, K):
+    """An NVFP4 projection whose two 16-groups of every 32-block share one E4M3 scale s,
+    and the Q8_0 projection of the same real matrix: q = 2 * e2m1 (an integer in
+    [-12, 12]) and d = s / 2 (exact in fp16)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    sb = rng.integers(0x18, 0x59, size=(E, N, K // 32), dtype=np.uint8)
+    scales = np.repeat(sb, 2, axis=-1)
+    nib = np.empty((E, N, K), np.int64)
+    nib[..., 0::2] = codes & 0x0F
+    nib[..., 1::2] = codes >> 4
+    mag = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)           # 2 * |e2m1|
+    q = np.where(nib & 8, -mag[nib & 7], mag[nib & 7]).astype(np.int8)
+    half = np.array([float(_e4m3_frac(int(b)) / 2) for b in range(256)])
+    d = half[sb].astype(np.float16)
+    assert np.array_equal(d.astype(np.float64), half[sb])          # s / 2 is exact in fp16
+    return codes, scales, q, d.view(np.uint16)
+
+
+def _e4m3_frac(b):
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def test_q8_0_down_equals_nvfp4_down_on_the_same_matrix():
+    """The MoE with a Q8_0 down projection equals the (separately pinned) NVFP4 MoE when
+    both hold the same real matrix."""
+    lay = W.draw_layer(4, E=5, H=64, I=96)
+    codes, scales, q, d = _paired_nvfp4_and_q8(11, lay.E, lay.H, lay.I)
+    lay.down = W.Proj(codes, scales, lay.down.gamma)
+    lay8 = W.Layer(lay.gate, lay.up, W.Q8Proj(q, d, lay.down.gamma.copy()), lay.E, lay.H, lay.I)
+    assert np.array_equal(O.dequant(codes, scales), O.dequant_q8_0(q, d))
+    rng = np.random.default_rng(12)
+    T, k = 7, 3
+    x = rng.standard_normal((T, lay.H))
+    ids = rng.integers(0, lay.E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    a = O.moe_pairwise(x, lay, ids, w)
+    b = O.moe_pairwise(x, lay8, ids, w)
+    c = O.moe_grouped(x, lay8, ids, w)
+    assert np.array_equal(a, b)
+    assert np.abs(c - a).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_q8_0_negative_controls(monkeypatch):
+    """Plausible mistakes in the Q8_0 decoder fail the pins above."""
+    def unsigned_codes(codes, scales):
+        q = np.asarray(codes).view(np.uint8).astype(np.float64)
+        dd = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
+        return q * np.repeat(dd, 32, axis=-1)
+    def block16(codes, scales):
+        q = np.asarray(codes, np.int8).astype(np.float64)
+        dd = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)
+        return q * np.repeat(dd, 16, axis=-1)[..., :q.shape[-1]]
+    def bf16_scales(codes, scales):
+        q = np.asarray(codes, np.int8).astype(np.float64)
+        dd = (np.asarray(scales, np.uint32) << 16).view(np.float32).astype(np.float64)
+        return q * np.repeat(dd, 32, axis=-1)
+    for bad in (unsigned_codes, block16, bf16_scales):
+        monkeypatch.setattr(O.nvfp4_oracle, "dequant_q8_0", bad)
+        monkeypatch.setattr(O, "dequant_q8_0", bad)
+        with pytest.raises((AssertionError, ValueError)):
+            test_q8_0_dequant_bruteforce_all_codes()
+        monkeypatch.undo()

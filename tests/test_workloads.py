@@ -55,3 +55,22 @@ def test_linear_case():
     assert x.shape == (4, 128) and x.dtype == np.float32
     assert codes.shape == (64, 64) and scales.shape == (64, 8)
     assert gamma[0] == np.float32(1.0 / 2688.0)
+
+
+def test_q8_0_down_layer():
+    """Q8_0 down draws: shapes, all code bytes used, normal fp16 scales in [2^-14, 2^-12],
+    unit gamma, the same bytes for a subset of experts, gate/up unchanged."""
+    full = W.draw_layer(W.config_seed(2), E=6, H=64, I=96, down_fmt="q8_0")
+    assert full.down.fmt == "q8_0" and full.gate.fmt == "nvfp4"
+    assert full.down.codes.shape == (6, 64, 96) and full.down.codes.dtype == np.int8
+    assert full.down.scales.shape == (6, 64, 3) and full.down.scales.dtype == np.uint16
+    d = full.down.scales.view(np.float16).astype(np.float64)
+    assert d.min() >= 2.0 ** -14 and d.max() <= 2.0 ** -12
+    assert np.all(full.down.gamma == 1.0)
+    sub = W.draw_layer(W.config_seed(2), E=6, H=64, I=96, experts=[4, 1], down_fmt="q8_0")
+    assert np.array_equal(sub.down.codes[sub.slot(4)], full.down.codes[4])
+    assert np.array_equal(sub.down.scales[sub.slot(1)], full.down.scales[1])
+    nv = W.draw_layer(W.config_seed(2), E=6, H=64, I=96)
+    assert np.array_equal(nv.gate.codes, full.gate.codes) and np.array_equal(nv.up.scales, full.up.scales)
+    big = W.draw_layer(W.config_seed(2), E=1, H=256, I=256, down_fmt="q8_0")
+    assert len(np.unique(big.down.codes)) == 256

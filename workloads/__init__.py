@@ -33,6 +33,16 @@ Recipe (per config index c, seed = 20261203 + c, numpy PCG64):
     Gumbel-top-k (equivalent to sequential weighted sampling without
     replacement);
   * router weights: softmax of k i.i.d. N(0, 1) logits, in fp32.
+
+Q8_0 down projections (the "Strata NVFP4" README's mixed pack: an 8-bit down
+projection in selected layers; the format is GGML's Q8_0, blocks of 32 int8 weights
+along the inputs with one fp16 scale each):
+  codes  int8   [E][N][K]      one weight per byte
+  scales uint16 [E][N][K/32]   fp16 bit patterns, scale b covers inputs 32b .. 32b+31
+  gamma  float32 [E]           all 1.0 (the format has no tensor scale)
+Recipe: code bytes uniform over all 256 values; scale = fp16(2^v / 8192) with
+v ~ U[-1, 1] per block (always a normal fp16 value), so weights are of the same
+order as the NVFP4 ones.
 """
 from __future__ import annotations
 
@@ -49,7 +59,8 @@ EXPERTS = 512
 TOPK = 8
 GROUP = 16
 
-PROJ_TAG = {"gate": 1, "up": 2, "down": 3}
+PROJ_TAG = {"gate": 1, "up": 2, "down": 3, "down_q8": 4}
+Q8_BLOCK = 32
 _TAG_X, _TAG_IDS, _TAG_W, _TAG_GAMMA, _TAG_OUTLIER, _TAG_PERM = 11, 12, 13, 14, 15, 16
 
 
@@ -78,10 +89,30 @@ class Proj:
 
 
 @dataclass
+class Q8Proj:
+    """One Q8_0 projection of E experts: rows = outputs (N), inputs = K."""
+    codes: np.ndarray   # int8 [E][N][K]
+    scales: np.ndarray  # uint16 (fp16 bits) [E][N][K/32]
+    gamma: np.ndarray   # float32 [E]
+    fmt = "q8_0"
+
+    @property
+    def N(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def K(self) -> int:
+        return int(self.codes.shape[2])
+
+
+Proj.fmt = "nvfp4"
+
+
+@dataclass
 class Layer:
     gate: Proj
     up: Proj
-    down: Proj
+    down: "Proj | Q8Proj"
     E: int
     H: int
     I: int
@@ -103,6 +134,15 @@ def draw_proj_expert(seed: int, proj: str, e: int, N: int, K: int):
     return codes, scales
 
 
+def draw_q8_expert(seed: int, e: int, N: int, K: int):
+    """Q8_0 code bytes (int8) and fp16 scale bits of one expert's down projection."""
+    g = _rng(seed, PROJ_TAG["down_q8"], int(e))
+    codes = np.frombuffer(g.bytes(N * K), dtype=np.int8).reshape(N, K).copy()
+    v = g.uniform(-1.0, 1.0, size=(N, K // Q8_BLOCK))
+    scales = (np.exp2(v) / 8192.0).astype(np.float16).view(np.uint16)
+    return codes, scales
+
+
 def draw_gammas(seed: int, E: int) -> Dict[str, np.ndarray]:
     g = _rng(seed, _TAG_GAMMA)
     u = g.uniform(-1.0, 1.0, size=(3, E))
@@ -113,12 +153,22 @@ def draw_gammas(seed: int, E: int) -> Dict[str, np.ndarray]:
 
 
 def draw_layer(seed: int, E: int = EXPERTS, H: int = HIDDEN, I: int = INTER,
-               experts: Optional[Iterable[int]] = None) -> Layer:
-    """A full layer (experts=None) or only the listed experts (same bytes)."""
+               experts: Optional[Iterable[int]] = None, down_fmt: str = "nvfp4") -> Layer:
+    """A full layer (experts=None) or only the listed experts (same bytes). down_fmt
+    "q8_0" draws the down projection in Q8_0 instead of NVFP4."""
     gam = draw_gammas(seed, E)
     ids = np.arange(E) if experts is None else np.array(sorted(set(int(e) for e in experts)), dtype=np.int64)
     shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
     projs = {}
+    if down_fmt == "q8_0":
+        codes = np.empty((len(ids), H, I), dtype=np.int8)
+        scales = np.empty((len(ids), H, I // Q8_BLOCK), dtype=np.uint16)
+        for s, e in enumerate(ids):
+            codes[s], scales[s] = draw_q8_expert(seed, int(e), H, I)
+        projs["down"] = Q8Proj(codes, scales, np.ones(len(ids), dtype=np.float32))
+        del shapes["down"]
+    elif down_fmt != "nvfp4":
+        raise ValueError(down_fmt)
     for p, (N, K) in shapes.items():
         codes = np.empty((len(ids), N, K // 2), dtype=np.uint8)
         scales = np.empty((len(ids), N, K // GROUP), dtype=np.uint8)
