@@ -19,6 +19,10 @@
  *   - W4A8 prompt path: activations quantized per row to int8 with an FP32 scale
  *     absmax / 127 before each expert GEMM ("Strata NVFP4" README, "How it differs from
  *     upstream Strata": an int8 (W4A8) prompt path that keeps 8-bit activations).
+ *   - Mixed packs: the down projection of a layer may be Q8_0 instead of NVFP4 ("Strata
+ *     NVFP4" README, the re-quantized experts pack: Q8_0 down projections in 27 of the 48
+ *     layers). The pages name the format only; its element rule here is GGML's: blocks
+ *     of 32 int8 weights along the inputs with one fp16 scale each, weight = d * q.
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor's
@@ -36,6 +40,10 @@
  *                                  element 2j+1 in the high nibble;
  *       scales uint8 [E][N][K/16]  scale byte g covers inputs 16g .. 16g+15;
  *       global float [E]           one FP32 scale per expert tensor.
+ *     Q8_0 projections (format NVFP4_FMT_Q8_0, down projection only):
+ *       codes  int8   [E][N][K]    one weight per byte;
+ *       scales fp16   [E][N][K/32] scale b covers inputs 32b .. 32b+31 (raw fp16 bits);
+ *       global float [E] or NULL   NULL means 1.
  *     K must be a multiple of 32. Code and scale planes must be 16-byte aligned.
  *   - topk_ids int32 [T][topk], topk_weights float [T][topk]. Ids outside [0, E) are
  *     dropped (they contribute nothing); the number dropped is written as an int32 to
@@ -72,13 +80,17 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
  *                       matrix cores (int8 values are exact in fp16). */
 typedef enum { NVFP4_ACT_BF16 = 0, NVFP4_ACT_W4A8 = 1, NVFP4_ACT_W4A8_F16 = 2 } nvfp4_act;
 
+/* Weight format of a projection: NVFP4 (every projection) or Q8_0 (down only). */
+typedef enum { NVFP4_FMT_NVFP4 = 0, NVFP4_FMT_Q8_0 = 1 } nvfp4_format;
+
 /* One projection (gate, up or down) of all E experts of a layer. Device pointers. */
 typedef struct {
-  const uint8_t* codes;  /* [E][N][K/2] */
-  const uint8_t* scales; /* [E][N][K/16] */
-  const float* global;   /* [E] */
+  const uint8_t* codes;  /* NVFP4: [E][N][K/2]; Q8_0: int8 [E][N][K] */
+  const uint8_t* scales; /* NVFP4: [E][N][K/16] E4M3; Q8_0: fp16 [E][N][K/32] */
+  const float* global;   /* [E]; may be NULL for Q8_0 */
   int32_t N;             /* outputs per expert (rows) */
   int32_t K;             /* inputs per expert, multiple of 32 */
+  int32_t format;        /* nvfp4_format; a zero-initialized struct is NVFP4 */
 } nvfp4_weight;
 
 /* Dequantize `rows` NVFP4 rows of K inputs: out[r][k] = e2m1 * e4m3 [* global[0]].
@@ -95,7 +107,8 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
 /* Single-expert NVFP4 linear: out[t][n] = w->global[expert] * sum_k x[t][k] * W_e[n][k].
  * x [T][w->K] in x_dtype (F32 or BF16), out float [T][w->N]. (Same sources as above.)
  * Errors: EINVAL for null pointers, T < 0, expert outside [0, E) (E is not known here:
- * the caller guarantees the arrays hold expert+1 experts), bad K. */
+ * the caller guarantees the arrays hold expert+1 experts), bad K, unknown format;
+ * EUNSUPPORTED for a Q8_0 weight. */
 int nvfp4_linear(const void* x, int32_t x_dtype, int32_t T, const nvfp4_weight* w, int32_t expert,
                  float* out, void* stream);
 
@@ -124,7 +137,8 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
 /* Decode (small token batches): the full routed-expert projection above for
  * 1 <= T <= 8 tokens, with FP32 arithmetic throughout and h kept in fp32 ("#1858
  * strata-safetensors": the quality profile keeps canonical FP32 expert decode).
- * x [T][H] bf16; gate/up: N = I, K = H; down: N = H, K = I; out [T][H] in out_dtype
+ * x [T][H] bf16; gate/up: N = I, K = H, NVFP4; down: N = H, K = I, NVFP4 or Q8_0
+ * (Q8_0 dot products in FP32, each 32-input block scaled once); out [T][H] in out_dtype
  * (F32 or BF16). ws needs nvfp4_moe_decode_workspace_size() bytes and must be
  * zero-filled before its first use (it holds a grid-barrier counter and per-block release
  * flags that every successful call leaves ready for the next; zero it again if H changes
@@ -135,8 +149,9 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
  * overlap. The whole call is one persistent launch when its grid (H/8 blocks) fits on the
  * device at once, else two launches with identical results.
  * Errors: EINVAL (null pointers, shapes that disagree, H or I not a multiple of 32,
- * topk < 1, E < 1); EUNSUPPORTED for x not bf16, T > 8, topk * T > 64, H or I above
- * 8192, T * H above 40960; EWORKSPACE. T == 0 is a no-op and may pass null tensors. */
+ * topk < 1, E < 1, unknown format); EUNSUPPORTED for x not bf16, T > 8, topk * T > 64,
+ * H or I above 8192, T * H above 40960, a Q8_0 gate or up projection; EWORKSPACE.
+ * T == 0 is a no-op and may pass null tensors. */
 size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk);
 int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
                      const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
@@ -150,9 +165,12 @@ int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const
  * chunks up to 32K tokens, where every chunk streams every layer's experts once.)
  * Each pair's down output is kept in fp32 and the slots of a token are summed in slot
  * order, so the result is deterministic. T == 0 is a no-op and may pass null tensors.
- * Errors: EINVAL (null pointers, shapes that disagree, unknown act, out_dtype F16);
- * EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128, E > 8192, x_dtype
- * other than BF16; EWORKSPACE. */
+ * The down projection may be Q8_0: its weights enter the fp16 matrix cores as
+ * fp16(d * q), one rounding per weight (relative error at most 2^-11), the only
+ * operand of the path that is not exact.
+ * Errors: EINVAL (null pointers, shapes that disagree, unknown act or format,
+ * out_dtype F16); EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128,
+ * E > 8192, x_dtype other than BF16, a Q8_0 gate or up projection; EWORKSPACE. */
 size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                         int32_t act);
 int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,

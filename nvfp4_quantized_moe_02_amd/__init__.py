@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     NVFP4Error,
     PreparedCall,
     Proj,
+    Q8Proj,
+    FORMAT,
     Layer,
     dequant,
     lib_path,

@@ -35,7 +35,11 @@ class _Weight(ctypes.Structure):
         ("global_", ctypes.c_void_p),
         ("N", ctypes.c_int32),
         ("K", ctypes.c_int32),
+        ("format", ctypes.c_int32),
     ]
+
+
+FORMAT = {"nvfp4": 0, "q8_0": 1}
 
 
 def lib_path() -> str:
@@ -130,20 +134,50 @@ class Proj:
     def K(self) -> int:
         return int(self.codes.shape[2]) * 2
 
+    fmt = "nvfp4"
+
     def cstruct(self) -> _Weight:
-        return _Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.gamma), self.N, self.K)
+        return _Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.gamma), self.N, self.K, FORMAT[self.fmt])
 
     @staticmethod
     def from_numpy(p, device) -> "Proj":
+        if getattr(p, "fmt", "nvfp4") == "q8_0":
+            return Q8Proj.from_numpy(p, device)
         return Proj(torch.from_numpy(p.codes).to(device), torch.from_numpy(p.scales).to(device),
                     torch.from_numpy(p.gamma).to(device))
+
+
+@dataclass
+class Q8Proj:
+    """One Q8_0 projection of E experts on the device (down projections): codes int8
+    [E][N][K], scales fp16 bits (int16) [E][N][K/32], gamma float32 [E] or None (= 1)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    gamma: Optional[torch.Tensor] = None
+    fmt = "q8_0"
+
+    @property
+    def N(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def K(self) -> int:
+        return int(self.codes.shape[2])
+
+    def cstruct(self) -> _Weight:
+        return _Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.gamma), self.N, self.K, FORMAT[self.fmt])
+
+    @staticmethod
+    def from_numpy(p, device, with_gamma: bool = False) -> "Q8Proj":
+        return Q8Proj(torch.from_numpy(p.codes).to(device), torch.from_numpy(p.scales.view("int16")).to(device),
+                      torch.from_numpy(p.gamma).to(device) if with_gamma else None)
 
 
 @dataclass
 class Layer:
     gate: Proj
     up: Proj
-    down: Proj
+    down: "Proj | Q8Proj"
 
     @property
     def E(self) -> int:

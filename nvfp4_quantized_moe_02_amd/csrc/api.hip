@@ -14,11 +14,14 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 inline int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
 
 bool weight_ok(const nvfp4_weight* w) {
-  return w && w->codes && w->scales && w->global && w->N > 0 && w->K > 0 && (w->K % 32) == 0 &&
-         aligned(w->codes, 16) && aligned(w->scales, 16);
+  if (!w || (w->format != NVFP4_FMT_NVFP4 && w->format != NVFP4_FMT_Q8_0)) return false;
+  return w->codes && w->scales && (w->global || w->format == NVFP4_FMT_Q8_0) && w->N > 0 && w->K > 0 &&
+         (w->K % 32) == 0 && aligned(w->codes, 16) && aligned(w->scales, 16);
 }
 
-WeightArgs to_args(const nvfp4_weight* w) { return WeightArgs{w->codes, w->scales, w->global, w->N, w->K}; }
+WeightArgs to_args(const nvfp4_weight* w) {
+  return WeightArgs{w->codes, w->scales, w->global, w->N, w->K, w->format == NVFP4_FMT_Q8_0 ? 1 : 0};
+}
 
 // Workspace carving: offsets are computed identically by the size query and the call.
 struct Carver {
@@ -118,6 +121,7 @@ int nvfp4_linear(const void* x, int32_t x_dtype, int32_t T, const nvfp4_weight* 
                  void* stream) {
   if (!x || !out || T < 0 || expert < 0 || !weight_ok(w)) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (w->format != NVFP4_FMT_NVFP4) return NVFP4_EUNSUPPORTED;
   if (!aligned(x, 4)) return NVFP4_EINVAL;
   (void)hipGetLastError();
   const size_t er = (size_t)expert * w->N;
@@ -171,6 +175,7 @@ static int check_moe_common(const void* x, int32_t T, int32_t H, const nvfp4_wei
   const int I = gate->N;
   if (gate->K != H || up->K != H || up->N != I || down->N != H || down->K != I) return NVFP4_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, 16)) return NVFP4_EINVAL;
+  if (gate->format != NVFP4_FMT_NVFP4 || up->format != NVFP4_FMT_NVFP4) return NVFP4_EUNSUPPORTED;
   return NVFP4_OK;
 }
 

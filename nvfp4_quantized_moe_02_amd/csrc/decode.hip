@@ -23,7 +23,8 @@
 //
 // Lane mapping: 16 lanes per weight row, each lane reads 16-byte chunks (32 inputs =
 // two scale groups) with 128-bit loads; a wave covers 4 rows, so each load instruction
-// reads 4 rows x 256 contiguous bytes.
+// reads 4 rows x 256 contiguous bytes. A Q8_0 down projection (template parameter Q8)
+// keeps the mapping with 32-byte chunks (32 int8 weights, one fp16 scale).
 #include "kernels.h"
 
 namespace nvfp4 {
@@ -168,6 +169,27 @@ __device__ __forceinline__ float dot_chunk_f32(const uint4 c, uint32_t sc, const
   return g2[0] * e4m3_f32<0>(sc) + g2[1] * e4m3_f32<1>(sc);
 }
 
+// One Q8_0 block (32 int8 weights in two 16-byte words, fp16 scale bits in `sc`) dotted
+// with 32 fp32 h values: FP32 products and sums, the scale applied once per block.
+__device__ __forceinline__ float dot_chunk_q8(const uint4 c0, const uint4 c1, uint32_t sc,
+                                              const float* __restrict__ hp) {
+  const uint32_t wd[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float4* h4 = reinterpret_cast<const float4*>(hp);
+  float g2[2] = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 hv = h4[q];
+    const int32_t w = (int32_t)wd[q];
+    float s = g2[q & 1];
+    s = fmaf((float)((w << 24) >> 24), hv.x, s);
+    s = fmaf((float)((w << 16) >> 24), hv.y, s);
+    s = fmaf((float)((w << 8) >> 24), hv.z, s);
+    s = fmaf((float)(w >> 24), hv.w, s);
+    g2[q & 1] = s;
+  }
+  return (g2[0] + g2[1]) * (float)__builtin_bit_cast(_Float16, (uint16_t)sc);
+}
+
 // ---- phase 1: a unit is (unique expert slot u, intermediate rows 4q .. 4q+3)
 template <int CH>
 struct GateUpRows {
@@ -279,10 +301,10 @@ __device__ void phase1(const DecodeArgs& a, const DecodeSmem& sm, Phase1<CH>& st
 
 // ---- phase 2: wave w owns the row quad (w & 1) of its block and the unique experts
 // (w >> 1) + 4i.
-template <int CH>
+template <int CH, bool Q8>
 struct DownRows {
-  uint4 c[kUB][CH];
-  uint32_t s[kUB][CH];
+  uint4 c[kUB][CH][Q8 ? 2 : 1];  // NVFP4: 16 bytes (32 inputs); Q8_0: 32 bytes
+  uint32_t s[kUB][CH];           // NVFP4: two E4M3 bytes; Q8_0: fp16 bits
   float gd[kUB];  // global scales of the experts, loaded with their rows
   // the experts' pairs: list positions [ps, pe); the first pair and its router weight are
   // read here, ahead of the h exchange, so phase 2 starts without an LDS round trip
@@ -295,9 +317,9 @@ __device__ __forceinline__ int down_expert(int wave, int ub) { return (wave >> 1
 // Loads the weight chunks of this wave's experts ub0 .. ub0+kUB-1 for output row `row`;
 // experts beyond the unique list get an empty pair range and rows beyond H zero codes,
 // scales and global scale (they add exactly 0).
-template <int CH>
+template <int CH, bool Q8>
 __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
-                                          DownRows<CH>& d) {
+                                          DownRows<CH, Q8>& d) {
   const int wave = threadIdx.x >> 6;
   const int nch = a.I >> 5;
 #pragma unroll
@@ -309,15 +331,18 @@ __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem&
     d.p0[b] = have ? sm.list[d.ps[b]] : 0;
     d.w0[b] = have ? sm.wp[d.p0[b]] : 0.f;
     const bool ok = have && row < a.H;
-    d.gd[b] = ok ? a.down.global[sm.uniq[u]] : 0.f;
+    d.gd[b] = ok ? (a.down.global ? a.down.global[sm.uniq[u]] : 1.0f) : 0.f;
     const size_t grow = ok ? (size_t)sm.uniq[u] * a.H + row : 0;
-    const uint8_t* rc = a.down.codes + grow * (a.I / 2);
+    // per row: NVFP4 I/2 code bytes and I/16 scale bytes; Q8_0 I code bytes and I/32 fp16
+    const uint8_t* rc = a.down.codes + grow * (Q8 ? a.I : a.I / 2);
     const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scales + grow * (a.I / 16));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = l16 + 16 * c;
       const bool ld = ok && ch < nch;
-      d.c[b][c] = ld ? *reinterpret_cast<const uint4*>(rc + ch * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < (Q8 ? 2 : 1); ++v)
+        d.c[b][c][v] = ld ? *reinterpret_cast<const uint4*>(rc + ch * (Q8 ? 32 : 16) + 16 * v) : make_uint4(0, 0, 0, 0);
       d.s[b][c] = ld ? (uint32_t)rs[ch] : 0u;
     }
   }
@@ -325,8 +350,8 @@ __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem&
 
 // One pair's partial dot products for this lane's chunks: all h reads are issued before
 // the arithmetic (chunks past I read chunk 0 and meet zero weights).
-template <int CH, bool HLDS>
-__device__ __forceinline__ float down_pair(const DecodeArgs& a, const DownRows<CH>& d, int b, int p, int l16,
+template <int CH, bool Q8, bool HLDS>
+__device__ __forceinline__ float down_pair(const DecodeArgs& a, const DownRows<CH, Q8>& d, int b, int p, int l16,
                                            int xb) {
   const int nch = a.I >> 5;
   float part = 0.f;
@@ -334,13 +359,16 @@ __device__ __forceinline__ float down_pair(const DecodeArgs& a, const DownRows<C
   for (int c = 0; c < CH; ++c) {
     const int ch = l16 + 16 * c < nch ? l16 + 16 * c : 0;
     const float* hp = HLDS ? h_lds_chunk(xb, p, a.I, ch) : a.h + (size_t)p * a.I + ch * 32;
-    part += dot_chunk_f32(d.c[b][c], d.s[b][c], hp);
+    if constexpr (Q8)
+      part += dot_chunk_q8(d.c[b][c][0], d.c[b][c][1], d.s[b][c], hp);
+    else
+      part += dot_chunk_f32(d.c[b][c][0], d.s[b][c], hp);
   }
   return part;
 }
 
-template <int CH, bool HLDS>
-__device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem& sm, const DownRows<CH>& d,
+template <int CH, bool Q8, bool HLDS>
+__device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem& sm, const DownRows<CH, Q8>& d,
                                            int l16, float (&acc)[kDecodeMaxT]) {
   const int xb = (int)x_lds_bytes(a.T, a.H);
 #pragma unroll
@@ -348,7 +376,7 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
     if (d.ps[b] >= d.pe[b]) break;  // uniform: this wave has no expert b (nor later ones)
     {
       const int p = d.p0[b];
-      const float part = down_pair<CH, HLDS>(a, d, b, p, l16, xb);
+      const float part = down_pair<CH, Q8, HLDS>(a, d, b, p, l16, xb);
       const int t = p / a.topk;
       const float coef = d.w0[b] * d.gd[b];
 #pragma unroll
@@ -357,7 +385,7 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
     }
     for (int i = d.ps[b] + 1; i < d.pe[b]; ++i) {
       const int p = sm.list[i];
-      const float part = down_pair<CH, HLDS>(a, d, b, p, l16, xb);
+      const float part = down_pair<CH, Q8, HLDS>(a, d, b, p, l16, xb);
       const int t = p / a.topk;
       const float coef = sm.wp[p] * d.gd[b];
 #pragma unroll
@@ -413,7 +441,8 @@ __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
 }
 
 // MODE 0: phase 1 only; MODE 1: phase 2 only; MODE 2: both with the grid barrier.
-template <int MODE, int CHG, int CHD>
+// Q8: the down projection is Q8_0.
+template <int MODE, int CHG, int CHD, bool Q8>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ DecodeSmem sm;
   decode_prepare(sm, a, MODE != 1);
@@ -424,8 +453,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   const int row = blockIdx.x * kRowsPerBlock + (wave & 1) * 4 + (lane >> 4);
   Phase1<CHG> p1;
   if (MODE != 1) phase1_issue<CHG>(a, sm, blockIdx.x * kDecWaves + wave, p1);
-  DownRows<CHD> d;
-  if (MODE != 0) down_load<CHD>(a, sm, 0, row, l16, d);  // in flight during phase 1 and the wait
+  DownRows<CHD, Q8> d;
+  if (MODE != 0) down_load<CHD, Q8>(a, sm, 0, row, l16, d);  // in flight during phase 1 and the wait
   if (MODE != 1) phase1<CHG>(a, sm, p1);
   if (MODE == 0) return;
   if (MODE == 2 && !grid_barrier(a, sm)) return;
@@ -446,9 +475,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   for (int t = 0; t < kDecodeMaxT; ++t) acc[t] = 0.f;
   const int per_wave = (sm.nu - (wave >> 1) + 3) / 4;  // experts of this wave
   for (int ub0 = 0; ub0 < per_wave; ub0 += kUB) {
-    if (ub0 > 0) down_load<CHD>(a, sm, ub0, row, l16, d);
-    if (a.h_in_lds) down_accum<CHD, true>(a, sm, d, l16, acc);
-    else down_accum<CHD, false>(a, sm, d, l16, acc);
+    if (ub0 > 0) down_load<CHD, Q8>(a, sm, ub0, row, l16, d);
+    if (a.h_in_lds) down_accum<CHD, Q8, true>(a, sm, d, l16, acc);
+    else down_accum<CHD, Q8, false>(a, sm, d, l16, acc);
   }
 #pragma unroll
   for (int t = 0; t < kDecodeMaxT; ++t) {
@@ -477,40 +506,45 @@ static size_t decode_lds_bytes(const DecodeArgs& a) {
   return x_lds_bytes(a.T, a.H) + (a.h_in_lds ? h_lds_bytes(a.P, a.I) : 0);
 }
 
-template <int MODE, int CHG, int CHD>
+template <int MODE, int CHG, int CHD, bool Q8>
 static hipError_t launch_mode(const DecodeArgs& a, hipStream_t st) {
   const size_t lds = decode_lds_bytes(a);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<MODE, CHG, CHD>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<MODE, CHG, CHD, Q8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid((a.H + kRowsPerBlock - 1) / kRowsPerBlock);
-  decode_kernel<MODE, CHG, CHD><<<grid, kDecThreads, lds, st>>>(a);
+  decode_kernel<MODE, CHG, CHD, Q8><<<grid, kDecThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
 // The fused form needs every block of its grid resident at once.
-template <int CHG, int CHD>
+template <int CHG, int CHD, bool Q8>
 static bool fused_fits(const DecodeArgs& a) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<2, CHG, CHD>),
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<2, CHG, CHD, Q8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes(a)) != hipSuccess)
     return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<2, CHG, CHD>, kDecThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<2, CHG, CHD, Q8>, kDecThreads,
                                                    decode_lds_bytes(a)) != hipSuccess)
     return false;
   return (long long)((a.H + kRowsPerBlock - 1) / kRowsPerBlock) <= (long long)cus * per_cu;
 }
 
+template <int CHG, int CHD, bool Q8>
+static hipError_t launch_decode_q(int stage, const DecodeArgs& a, hipStream_t st) {
+  if (stage == 0) return launch_mode<0, CHG, CHD, Q8>(a, st);
+  if (stage == 1) return launch_mode<1, CHG, CHD, Q8>(a, st);
+  // fused only when h fits in LDS: phase 2 then reads h once, with agent-coherent loads
+  if (a.h_in_lds && fused_fits<CHG, CHD, Q8>(a)) return launch_mode<2, CHG, CHD, Q8>(a, st);
+  const hipError_t e = launch_mode<0, CHG, CHD, Q8>(a, st);
+  return e != hipSuccess ? e : launch_mode<1, CHG, CHD, Q8>(a, st);
+}
+
 template <int CHG, int CHD>
 static hipError_t launch_decode_t(int stage, const DecodeArgs& a, hipStream_t st) {
-  if (stage == 0) return launch_mode<0, CHG, CHD>(a, st);
-  if (stage == 1) return launch_mode<1, CHG, CHD>(a, st);
-  // fused only when h fits in LDS: phase 2 then reads h once, with agent-coherent loads
-  if (a.h_in_lds && fused_fits<CHG, CHD>(a)) return launch_mode<2, CHG, CHD>(a, st);
-  const hipError_t e = launch_mode<0, CHG, CHD>(a, st);
-  return e != hipSuccess ? e : launch_mode<1, CHG, CHD>(a, st);
+  return a.down.fmt == 1 ? launch_decode_q<CHG, CHD, true>(stage, a, st) : launch_decode_q<CHG, CHD, false>(stage, a, st);
 }
 
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,

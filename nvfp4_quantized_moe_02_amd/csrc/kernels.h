@@ -6,11 +6,15 @@
 
 namespace nvfp4 {
 
+// One projection of all experts. fmt 0: NVFP4 (codes [E][N][K/2], E4M3 scales [E][N][K/16],
+// global [E]); fmt 1: Q8_0 (int8 codes [E][N][K], fp16 scales [E][N][K/32], global [E] or
+// null for 1).
 struct WeightArgs {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* global;
   int N, K;
+  int fmt;
 };
 
 struct TileDesc {

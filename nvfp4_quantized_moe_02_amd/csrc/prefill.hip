@@ -64,6 +64,23 @@ __device__ __forceinline__ f16x8_t bfrag(uint32_t word, _Float16 sc) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Q8_0 fragment: 8 int8 weights (two words) -> fp16 exactly (each byte with its sign bit
+// flipped, q + 128, becomes the mantissa of the fp16 value 1024 + q + 128 by a byte
+// permute; subtracting 1152 is exact), then one fp16 multiply by the block scale d: the
+// one rounding of the path's operands (relative error at most 2^-11).
+__device__ __forceinline__ f16x8_t bfrag_q8(uint32_t lo, uint32_t hi, _Float16 d) {
+  const uint32_t u0 = lo ^ 0x80808080u, u1 = hi ^ 0x80808080u;
+  const f16x2_t k = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2_t dd = {d, d};
+  const f16x2_t o0 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - k) * dd;
+  const f16x2_t o1 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - k) * dd;
+  const f16x2_t o2 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - k) * dd;
+  const f16x2_t o3 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - k) * dd;
+  const f16x4_t lo4 = __builtin_shufflevector(o0, o1, 0, 1, 2, 3);
+  const f16x4_t hi4 = __builtin_shufflevector(o2, o3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // SiLU for the fp16/fp32 h of the prefill path: exp and reciprocal from the hardware
 // approximations (about 1 ulp each).
 __device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
@@ -100,7 +117,7 @@ struct BTile {
   __device__ static int slot(int row, int ch) { return row * ROWB + ((ch ^ ((row >> SHIFT) & (CPR - 1))) << 4); }
 };
 
-template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB, int GK>
+template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB, int GK, bool Q8>
 __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
                                           const uint8_t* b0row, const uint8_t* b1row,
                                           const uint8_t* const* bs, const WeightArgs& w0,
@@ -126,24 +143,29 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   // group. Thread t stages chunks j*(WPB*64) + t of the group tile, i.e. chunk t % CPR of
   // rows j*RPT + t / CPR: CPR consecutive threads read one row's GK*32 contiguous bytes.
   // They go to LDS once per group; each lane then reads its fragments from there.
-  typedef BTile<WPB, GK> BT;
+  // Q8_0 (down only): a group is one K-block, 64 int8 weights per row (the tile geometry
+  // of two NVFP4 K-blocks).
+  constexpr int GKB = Q8 ? 1 : GK;  // K-blocks per B group
+  typedef BTile<WPB, Q8 ? 2 : GK> BT;
+  const size_t rowbytes = Q8 ? K : K / 2;
   char* btiles = lds + NSTAGE * STAGE_BYTES;
   const int brow = tid / BT::CPR, bch = tid % BT::CPR;
-  const int ngb = nkb / GK;
+  const int ngb = nkb / GKB;
   auto load_bg = [&](int g, int j) -> uint4 {
     const int gc = g < ngb ? g : ngb - 1;  // past the end: refetch the last group (never used)
     const int row = j * BT::RPT + brow;
     // gate/up: rows [0, NCB/2) are gate rows, [NCB/2, NCB) the same up rows (j is a
     // compile-time index, so the tensor choice is too)
-    const uint8_t* base = (GATEUP && j * BT::RPT >= BT::NCB / 2) ? b1row + (size_t)(row - BT::NCB / 2) * (K / 2)
-                                                                 : b0row + (size_t)row * (K / 2);
+    const uint8_t* base = (GATEUP && j * BT::RPT >= BT::NCB / 2) ? b1row + (size_t)(row - BT::NCB / 2) * rowbytes
+                                                                 : b0row + (size_t)row * rowbytes;
     return *reinterpret_cast<const uint4*>(base + gc * BT::ROWB + bch * 16);
   };
   // tile row of this lane's fragment in column block cb
   const int frow0 = GATEUP ? wave * 32 + l32 : wave * 64 + l32;
   const int frow1 = GATEUP ? BT::NCB / 2 + wave * 32 + l32 : wave * 64 + 32 + l32;
-  // Scales: K-block kb of a column holds 4 bytes (groups 4kb .. 4kb+3); lane half h uses
-  // bytes 2h and 2h+1. A group of KQ K-blocks is one load per column.
+  // Scales: K-block kb of a column holds 4 bytes (NVFP4: groups 4kb .. 4kb+3; Q8_0: the
+  // fp16 scales of blocks 2kb, 2kb+1); lane half h uses bytes 2h and 2h+1 either way. A
+  // group of KQ K-blocks is one load per column.
   typedef typename ScaleRaw<KQ>::type SRaw;
   const int ngrp = nkb / KQ;
   auto load_s = [&](int j, int cb) -> SRaw {
@@ -206,7 +228,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
     // finished those reads before passing the barrier of iteration kb-1.
     __syncthreads();
-    if constexpr (Q % GK == 0) {
+    if constexpr (Q % GKB == 0) {
 #pragma unroll
       for (int j = 0; j < BT::CH; ++j)
         *reinterpret_cast<uint4*>(btiles + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
@@ -216,22 +238,47 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // The next B group (at a group start) and A(kb+2) are loaded spread over the MFMAs of
     // this K-block: a burst of loads from every wave right after the barrier queues in the
     // address unit and holds back each wave's first MFMAs.
-    constexpr int NBL = (Q % GK == 0) ? BT::CH : 0;
+    constexpr int NBL = (Q % GKB == 0) ? BT::CH : 0;
     constexpr int NLD = NBL + NA;
     auto issue_loads = [&](int idx, int nf) {
 #pragma unroll
       for (int g = 0; g < NLD; ++g) {
         if (g * nf / NLD == idx) {
-          if (g < NBL) bg[g < NBL ? g : 0] = load_bg(kb / GK + 1, g < NBL ? g : 0);
+          if (g < NBL) bg[g < NBL ? g : 0] = load_bg(kb / GKB + 1, g < NBL ? g : 0);
           else aq[R][g - NBL] = load_a(kb + 2, g - NBL);
         }
       }
     };
-    constexpr int q = Q % GK;  // K-block within the B group: chunks 2q (half 0), 2q+1 (half 1)
-    const uint4 cur0 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow0, 2 * q + half));
-    const uint4 cur1 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow1, 2 * q + half));
-    const f16x2_t s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
-    const f16x2_t s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
+    // NVFP4: K-block q of the group is chunks 2q (half 0) and 2q+1 (half 1) of a row, one
+    // 16-byte chunk per lane; Q8_0: chunks 2*half and 2*half+1, 32 bytes per lane
+    constexpr int q = Q % GKB;
+    const uint4 cur0 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow0, Q8 ? 2 * half : 2 * q + half));
+    const uint4 cur1 = *reinterpret_cast<const uint4*>(btile + BT::slot(frow1, Q8 ? 2 * half : 2 * q + half));
+    uint4 cur0b = cur0, cur1b = cur1;
+    if constexpr (Q8) {
+      cur0b = *reinterpret_cast<const uint4*>(btile + BT::slot(frow0, 2 * half + 1));
+      cur1b = *reinterpret_cast<const uint4*>(btile + BT::slot(frow1, 2 * half + 1));
+    }
+    // NVFP4: the lane's two 16-group scales (E4M3 -> fp16); Q8_0: its block scale d twice
+    f16x2_t s0, s1;
+    if constexpr (Q8) {
+      const _Float16 d0 = __builtin_bit_cast(f16x2_t, sc0[Q >> 1])[Q & 1];
+      const _Float16 d1 = __builtin_bit_cast(f16x2_t, sc1[Q >> 1])[Q & 1];
+      s0 = f16x2_t{d0, d0};
+      s1 = f16x2_t{d1, d1};
+    } else {
+      s0 = e4m3x2_f16<(Q & 1) != 0>(sc0[Q >> 1]);
+      s1 = e4m3x2_f16<(Q & 1) != 0>(sc1[Q >> 1]);
+    }
+    // the B fragment of step s (inputs 32*half + 8s .. +7 of the K-block)
+    auto bstep = [&](const uint4& c, const uint4& cb, f16x2_t sc, int s) -> f16x8_t {
+      if constexpr (Q8) {
+        const uint4& w = s < 2 ? c : cb;
+        return (s & 1) ? bfrag_q8(w.z, w.w, sc[0]) : bfrag_q8(w.x, w.y, sc[0]);
+      } else {
+        return bfrag(word_of(c, s), sc[s >> 1]);
+      }
+    };
     // A fragments are read LA fragments ahead of their MFMAs (a ring of LA+1), so the LDS
     // latency of each read hides under the MFMAs issued in between; the B fragments of
     // step s+1 are unpacked right after the last MFMA of step s is issued.
@@ -244,8 +291,8 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     };
 #pragma unroll
     for (int i = 0; i < LA; ++i) ring[i] = read_a(i);
-    f16x8_t b0 = bfrag(word_of(cur0, 0), s0[0]);
-    f16x8_t b1 = bfrag(word_of(cur1, 0), s1[0]);
+    f16x8_t b0 = bstep(cur0, cur0b, s0, 0);
+    f16x8_t b1 = bstep(cur1, cur1b, s1, 0);
 #pragma unroll
     for (int idx = 0; idx < NF; ++idx) {
       if (idx + LA < NF) ring[(idx + LA) % (LA + 1)] = read_a(idx + LA);
@@ -261,8 +308,8 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
         acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[idx % (LA + 1)], b1, acc[rb][1], 0, 0, 0);
       }
       if (rb == NRB - 1 && s < 3) {
-        b0 = bfrag(word_of(cur0, s + 1), s0[(s + 1) >> 1]);
-        b1 = bfrag(word_of(cur1, s + 1), s1[(s + 1) >> 1]);
+        b0 = bstep(cur0, cur0b, s0, s + 1);
+        b1 = bstep(cur1, cur1b, s1, s + 1);
       }
     }
   };
@@ -326,7 +373,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // 1 KB row segments; the stores are non-temporal (y is read once, by the combine). The
     // kernel's LDS holds 32 * NCOL * 4 bytes.
     constexpr int NCOL = WPB * 64;
-    const float gd = w0.global[tc.e];
+    const float gd = w0.global ? w0.global[tc.e] : 1.0f;  // a Q8_0 down may have no tensor scale
     float* y = reinterpret_cast<float*>(out);
     float* yl = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -359,14 +406,14 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
 // ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
 // HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
-template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB, int GK>
+template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB, int GK, bool Q8 = false>
 __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ sorted_pairs,
     const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
     void* __restrict__ out, int ldo) {
   // A stages and the B tile; the down epilogue reuses them (32 rows x WPB*64 fp32)
-  constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, GK>::BYTES;
+  constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, Q8 ? 2 : GK>::BYTES;
   constexpr int kEpi = GATEUP ? 0 : 32 * WPB * 64 * 4;
   constexpr int kLds = kMain > kEpi ? kMain : kEpi;
   __shared__ __attribute__((aligned(16))) char lds[kLds];
@@ -418,7 +465,7 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     bs[1] = w1.scales + (row0 + wave * 32 + l32) * (K / 16);
   } else {
     const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (WPB * 64);
-    b0row = w0.codes + row0 * (K / 2);
+    b0row = w0.codes + row0 * (Q8 ? K : K / 2);
     b1row = b0row;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) bs[cb] = w0.scales + (row0 + wave * 64 + cb * 32 + l32) * (K / 16);
@@ -427,13 +474,13 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
 
   const int nrb = (tc.rows + 31) >> 5;
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -476,10 +523,16 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
   // 8 waves (512 outputs per block) when H allows, else 4 (256); scale groups of 4
   // K-blocks when I is a multiple of 256, else 2; B groups of 2 K-blocks.
-#define NVFP4_DOWN(ASC, KQ, WPB)                                                                          \
-  moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2>                                    \
-      <<<grid_for(max_tiles, H / (WPB * 64)), WPB * 64, 0, st>>>(A, h_scale, sorted_pairs, offsets, tiles, \
-                                                                tile_count, topk, I, H / (WPB * 64), down, down, w, y, H)
+#define NVFP4_DOWN(ASC, KQ, WPB)                                                                           \
+  do {                                                                                                     \
+    const dim3 grid = grid_for(max_tiles, H / (WPB * 64));                                                 \
+    if (down.fmt == 1)                                                                                     \
+      moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2, true><<<grid, WPB * 64, 0, st>>>(                 \
+          A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), down, down, w, y, H); \
+    else                                                                                                   \
+      moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2><<<grid, WPB * 64, 0, st>>>(                       \
+          A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), down, down, w, y, H); \
+  } while (0)
 #define NVFP4_DOWN_W(ASC, KQ) \
   if (H % 512 == 0)           \
     NVFP4_DOWN(ASC, KQ, 8);   \

@@ -24,15 +24,15 @@ def layer_dev(lay, fill_unused_nan=False, used=None):
         mask[np.asarray(sorted(set(int(e) for e in used if 0 <= e < lay.E)), dtype=np.int64)] = False
         idx = torch.from_numpy(np.nonzero(mask)[0]).to(DEV)
         for p in (dl.gate, dl.up, dl.down):
-            p.scales[idx] = 0x7F
+            p.scales[idx] = 0x7E00 if p.fmt == "q8_0" else 0x7F  # fp16 / E4M3 NaN
     return dl
 
 
-def sparse_layer(seed, experts, E=W.EXPERTS, H=W.HIDDEN, I=W.INTER):
+def sparse_layer(seed, experts, E=W.EXPERTS, H=W.HIDDEN, I=W.INTER, down_fmt="nvfp4"):
     """A full-size device layer holding the seeded bytes of `experts` only; all other
     experts have NaN scales. Returns (device layer, host subset layer)."""
     import nvfp4_quantized_moe_02_amd as nv
-    sub = W.draw_layer(seed, E=E, H=H, I=I, experts=experts)
+    sub = W.draw_layer(seed, E=E, H=H, I=I, experts=experts, down_fmt=down_fmt)
     gam = W.draw_gammas(seed, E)
 
     def proj(name, N, K):
@@ -44,7 +44,17 @@ def sparse_layer(seed, experts, E=W.EXPERTS, H=W.HIDDEN, I=W.INTER):
         scales[ids] = torch.from_numpy(p.scales).to(DEV)
         return nv.Proj(codes, scales, torch.from_numpy(gam[name]).to(DEV))
 
-    dl = nv.Layer(proj("gate", I, H), proj("up", I, H), proj("down", H, I))
+    def q8_down():
+        p = sub.down
+        codes = torch.full((E, H, I), 0x11, dtype=torch.int8, device=DEV)
+        scales = torch.full((E, H, I // 32), 0x7E00, dtype=torch.int16, device=DEV)  # fp16 NaN
+        ids = torch.from_numpy(sub.experts).to(DEV)
+        codes[ids] = torch.from_numpy(p.codes).to(DEV)
+        scales[ids] = torch.from_numpy(p.scales.view(np.int16)).to(DEV)
+        return nv.Q8Proj(codes, scales, None)
+
+    down = q8_down() if down_fmt == "q8_0" else proj("down", H, I)
+    dl = nv.Layer(proj("gate", I, H), proj("up", I, H), down)
     return dl, sub
 
 

@@ -1,0 +1,143 @@
+"""GPU parity of the mixed-format layer: NVFP4 gate/up with a Q8_0 down projection
+("Strata NVFP4" README, the re-quantized pack's Q8_0 down projections), through the
+C-ABI, against the float64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import (DEV, TOL, bf16_dev, bf16_out_to_f64, layer_dev, max_row_rel_l2, sparse_layer,
+                      w4a8_check, w4a8_tie_bound)
+
+pytestmark = pytest.mark.gpu
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_decode_q8_down_configs(index):
+    """Decode 1 token (uniform) and 4 tokens (Zipf): FP32 arithmetic, so far below the bar."""
+    wl = W.draw_workload(index)
+    dl, sub = sparse_layer(wl.seed, np.unique(wl.ids), down_fmt="q8_0")
+    x, ids, w = bf16_dev(wl.x), torch.from_numpy(wl.ids).to(DEV), torch.from_numpy(wl.w).to(DEV)
+    y = nv.moe_decode(x, dl, ids, w)
+    ref = O.moe_pairwise(O.bf16_to_f64(wl.x), sub, wl.ids, wl.w)
+    err = max_row_rel_l2(y.cpu().numpy(), ref)
+    print(f"decode config {index}, Q8_0 down: max row rel L2 {err:.3e}")
+    assert err < 1e-5
+    assert torch.equal(y, nv.moe_decode(x, dl, ids, w)), "decode must be deterministic"
+    # the two-launch form gives the same bits
+    ws = torch.zeros(nv.decode_workspace_size(wl.T, W.HIDDEN, W.INTER, W.EXPERTS, wl.ids.shape[1]),
+                     dtype=torch.uint8, device=DEV)
+    c = nv.PreparedCall("decode", x, dl, ids, w, torch.empty_like(y), ws)
+    c.stage(0)
+    c.stage(1)
+    assert torch.equal(c.keep[4], y)
+
+
+def _small(seed, E, H, I, T, k, act="bf16", gamma=False):
+    lay = W.draw_layer(seed, E=E, H=H, I=I, down_fmt="q8_0")
+    dl = layer_dev(lay)
+    if gamma:  # a tensor scale on the Q8_0 down projection (the format allows one)
+        lay.down.gamma = (np.exp2(np.random.default_rng(seed).uniform(-1, 1, E))).astype(np.float32)
+        dl.down.gamma = torch.from_numpy(lay.down.gamma).to(DEV)
+    xb = W.draw_activations(seed, T, H, outlier_frac=0.001)
+    ids = W.draw_routing_zipf(seed, T, E, k, s=1.1)
+    w = W.draw_router_weights(seed, T, k)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act=act,
+                       out_dtype=torch.float32)
+    if act == "bf16":
+        return y.cpu().numpy().astype(np.float64), O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w), None
+    return (y.cpu().numpy().astype(np.float64), O.moe_w4a8(xb, lay, ids, w), w4a8_tie_bound(xb, lay, ids, w))
+
+
+@pytest.mark.parametrize("H,I", [(512, 256), (512, 384), (256, 128), (768, 256)])
+def test_prefill_q8_down_shapes(H, I):
+    """Every down-GEMM variant: 8 or 4 waves (H % 512), scale groups of 4 or 2 K-blocks
+    (I % 256). Error sources: fp16 h and the fp16(d*q) weights (each within 2^-11)."""
+    got, ref, _ = _small(31, 6, H, I, 300, 4)
+    err = max_row_rel_l2(got, ref)
+    print(f"prefill Q8_0 down H={H} I={I}: max row rel L2 {err:.3e}")
+    assert err < 1e-3
+
+
+def test_prefill_q8_down_tensor_scale_and_w4a8():
+    got, ref, _ = _small(33, 8, 512, 256, 400, 8, gamma=True)
+    assert max_row_rel_l2(got, ref) < 1e-3
+    got, ref, bound = _small(35, 8, 512, 256, 400, 8, act="w4a8_f16")
+    err, ntie = w4a8_check(got, ref, bound)
+    print(f"w4a8 (fp16 MMA) with Q8_0 down: max row rel L2 {err:.3e} ({ntie} rows with a tie allowance)")
+
+
+def test_prefill_q8_down_equals_nvfp4_down_bitwise():
+    """A Q8_0 down projection holding the same real matrix as an NVFP4 one (q = 2*e2m1,
+    d = s/2, both exact in fp16) gives the same output bits: the two B decoders feed
+    identical fp16 operands to identical MFMA sequences."""
+    E, H, I, T, k = 6, 512, 256, 300, 4
+    lay = W.draw_layer(37, E=E, H=H, I=I)
+    rng = np.random.default_rng(38)
+    codes = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+    sb = rng.integers(0x18, 0x59, size=(E, H, I // 32), dtype=np.uint8)
+    lay.down = W.Proj(codes, np.repeat(sb, 2, axis=-1), np.ones(E, np.float32))
+    nib = np.empty((E, H, I), np.int64)
+    nib[..., 0::2], nib[..., 1::2] = codes & 0x0F, codes >> 4
+    mag = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)
+    q = np.where(nib & 8, -mag[nib & 7], mag[nib & 7]).astype(np.int8)
+    e4 = torch.tensor(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    d = (e4[sb] / 2).astype(np.float16)
+    assert np.array_equal(d.astype(np.float64), e4[sb] / 2)
+    dl4 = layer_dev(lay)
+    dl8 = nv.Layer(dl4.gate, dl4.up, nv.Q8Proj(torch.from_numpy(q).to(DEV),
+                                                 torch.from_numpy(d.view(np.int16)).to(DEV), None))
+    xb = W.draw_activations(37, T, H)
+    ids = torch.from_numpy(W.draw_routing_zipf(37, T, E, k)).to(DEV)
+    w = torch.from_numpy(W.draw_router_weights(37, T, k)).to(DEV)
+    for act in ("bf16", "w4a8_f16"):
+        y4 = nv.moe_prefill(bf16_dev(xb), dl4, ids, w, act=act, out_dtype=torch.float32)
+        y8 = nv.moe_prefill(bf16_dev(xb), dl8, ids, w, act=act, out_dtype=torch.float32)
+        assert torch.equal(y4, y8), act
+
+
+def test_prefill_c3_q8_down_full_size_sampled():
+    """The 8192-token workload with a Q8_0 down projection, sampled rows."""
+    lay = W.draw_layer(W.config_seed(3), down_fmt="q8_0")
+    dl = layer_dev(lay)
+    wl = W.draw_workload(3)
+    y = nv.moe_prefill(bf16_dev(wl.x), dl, torch.from_numpy(wl.ids).to(DEV), torch.from_numpy(wl.w).to(DEV))
+    rows = np.sort(np.random.default_rng(3).choice(wl.T, size=16, replace=False))
+    ref = O.moe_grouped(O.bf16_to_f64(wl.x), lay, wl.ids, wl.w, rows=rows)
+    got = bf16_out_to_f64(y[torch.from_numpy(rows).to(DEV)])
+    err = max_row_rel_l2(got, ref)
+    print(f"prefill 8192 tokens, Q8_0 down: max row rel L2 {err:.3e}")
+    assert err < TOL
+    assert torch.isfinite(y.float()).all()
+
+
+def test_q8_format_validation():
+    """A Q8_0 gate projection is unsupported; a Q8_0 linear is unsupported; an unknown
+    format is invalid. Nothing is enqueued on failure."""
+    lay = W.draw_layer(41, E=2, H=256, I=128, down_fmt="q8_0")
+    dl = layer_dev(lay)
+    xb = bf16_dev(W.draw_activations(41, 4, 256))
+    ids = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
+    w = torch.ones((4, 2), dtype=torch.float32, device=DEV)
+    q8_gate = nv.Q8Proj(torch.zeros((2, 128, 256), dtype=torch.int8, device=DEV),
+                        torch.zeros((2, 128, 8), dtype=torch.int16, device=DEV))
+    bad = nv.Layer(q8_gate, dl.up, dl.down)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.moe_prefill(xb, bad, ids, w)
+    assert ei.value.status == -2
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.linear(xb, dl.down)
+    assert ei.value.status == -2
+    import nvfp4_quantized_moe_02_amd.binding as B
+    st = B._Weight(dl.down.codes.data_ptr(), dl.down.scales.data_ptr(), 0, 256, 128, 7)
+    g, u = dl.gate.cstruct(), dl.up.cstruct()
+    import ctypes
+    out = torch.empty((4, 256), dtype=torch.bfloat16, device=DEV)
+    wsz = nv.prefill_workspace_size(4, 256, 128, 2, 2)
+    ws = torch.zeros(wsz, dtype=torch.uint8, device=DEV)
+    r = B.load_library().nvfp4_moe_prefill(xb.data_ptr(), 1, 4, 256, ctypes.byref(g), ctypes.byref(u),
+                                           ctypes.byref(st), 2, ids.data_ptr(), w.data_ptr(), 2, 0,
+                                           out.data_ptr(), 1, ws.data_ptr(), wsz, None)
+    assert r == -1
