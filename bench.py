@@ -26,7 +26,9 @@ PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 PEAK_INT8_TOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 N_LAYERS = 48
-BYTES_PER_EXPERT = 3 * 2048 * 768 * 9 // 16  # codes + scales of gate, up, down
+GATEUP_BYTES = 2 * 768 * 2048 * 9 // 16      # NVFP4 gate + up of one expert (codes + scales)
+DOWN_BYTES_NVFP4 = 2048 * 768 * 9 // 16      # NVFP4 down
+DOWN_BYTES_Q8 = 2048 * 768 + 2048 * 24 * 2   # Q8_0 down: int8 codes + fp16 scales per 32 inputs
 
 
 def log(*a):
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--decode-rounds", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run device-to-device copies of 1 GiB (the plain copy kernel whose HBM "
                          "counter readings scale the GEMM's FETCH_SIZE / WRITE_SIZE)")
@@ -54,7 +56,8 @@ def replicate(layer, n):
     import nvfp4_quantized_moe_02_amd as nv
     out = [layer]
     for _ in range(n - 1):
-        out.append(nv.Layer(*[nv.Proj(p.codes.clone(), p.scales.clone(), p.gamma.clone())
+        out.append(nv.Layer(*[type(p)(p.codes.clone(), p.scales.clone(),
+                                      None if p.gamma is None else p.gamma.clone())
                               for p in (layer.gate, layer.up, layer.down)]))
     return out
 
@@ -115,8 +118,9 @@ def bench_prefill(layers, index, act, steps, warmup):
                 padded_frac=P / (tiles * 128.0), tokens_per_s=wl.T / (ms / 1e3))
 
 
-def bench_decode(layers, index, rounds):
-    """hipGraph of one call per layer (48 layers), replayed `rounds` times."""
+def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4):
+    """hipGraph of one call per layer (48 layers), replayed `rounds` times. down_bytes:
+    bytes of one expert's down projection (NVFP4 or Q8_0)."""
     import numpy as np
     import torch
     import nvfp4_quantized_moe_02_amd as nv
@@ -152,11 +156,11 @@ def bench_decode(layers, index, rounds):
         res[name] = t0.elapsed_time(t1) * 1e3 / (rounds * len(calls))  # us per launch
         del g
     U = len(np.unique(wl.ids))
-    byt = U * BYTES_PER_EXPERT
+    byt = U * (GATEUP_BYTES + down_bytes)
     return dict(T=wl.T, unique_experts=U, bytes=byt, us=res["call"], us_gateup=res["gateup"],
                 us_down=res["down"], gbs=byt / (res["call"] * 1e-6) / 1e9,
                 gbs_gateup=U * 2 * 768 * 2048 * 9 / 16 / (res["gateup"] * 1e-6) / 1e9,
-                gbs_down=U * 768 * 2048 * 9 / 16 / (res["down"] * 1e-6) / 1e9)
+                gbs_down=U * down_bytes / (res["down"] * 1e-6) / 1e9)
 
 
 # Kernel sources whose hash a traffic profile records: counters taken on other sources
@@ -260,6 +264,24 @@ def main():
     if args.only in ("all", "w4a8"):
         w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2)
         log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
+    q8 = None
+    if args.only in ("all", "q8down"):
+        # the mixed pack's layers: NVFP4 gate/up with a Q8_0 down projection
+        del layers, base
+        torch.cuda.empty_cache()
+        t = time.time()
+        lay = W.draw_layer(W.config_seed(3), down_fmt="q8_0")
+        base = nv.Layer.from_numpy(lay, "cuda")
+        del lay
+        layers = replicate(base, args.layers)
+        torch.cuda.synchronize()
+        log(f"{args.layers} Q8_0-down layers on device in {time.time() - t:.1f} s")
+        q8 = {"prefill": bench_prefill(layers, 3, "bf16", max(8, args.steps // 2), args.warmup)}
+        for idx in (1, 2):
+            d = bench_decode(layers, idx, args.decode_rounds, DOWN_BYTES_Q8)
+            q8[f"decode_t{d['T']}"] = d
+        log(f"q8 down: prefill {q8['prefill']['ms']:.3f} ms/step, decode T=1 {q8['decode_t1']['us']:.2f} us, "
+            f"T=4 {q8['decode_t4']['us']:.2f} us")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_sample_tokens)
@@ -322,6 +344,21 @@ def main():
                                                           / 1e12 / PEAK_FP16_TFLOPS, 4),
                           "frac_of_int8_peak_step": round((w4["gu_flops"] + w4["dn_flops"]) / (w4["ms"] * 1e-3)
                                                           / 1e12 / PEAK_INT8_TOPS, 4)}
+    if q8 is not None:
+        pq = q8["prefill"]
+        result["q8_down"] = {
+            "workload": "the same layer shape with a Q8_0 down projection (int8 weights, fp16 scale per 32 "
+                        "inputs); NVFP4 gate/up",
+            "prefill_t8192": {"tokens/s": round(pq["tokens_per_s"], 1), "ms_per_step": round(pq["ms"], 4),
+                              "stage_ms": [round(v, 4) for v in pq["stages_ms"]]},
+            **{k: {"us_per_layer": round(v["us"], 3), "GB/s": round(v["gbs"], 1),
+                   "frac_hbm_peak": round(v["gbs"] / PEAK_HBM_GBS, 4), "weight_bytes": v["bytes"],
+                   "us_down": round(v["us_down"], 3), "GB/s_down": round(v["gbs_down"], 1)}
+               for k, v in q8.items() if k.startswith("decode")},
+        }
+        if dec:
+            result["q8_down"]["decode_time_vs_nvfp4"] = {
+                k: round(q8[f"decode_{k}"]["us"] / dec[k]["us"], 3) for k in dec if f"decode_{k}" in q8}
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
