@@ -26,6 +26,11 @@ Sources (the pages, by title and section):
   [FP4-L]    #2727 "tools: add opt-in FP4-Local CSF checkpoint conversion",
              Validation list: expert tensors stack 512 experts; three-expert
              CUDA parity on relative output error.
+  [S-RT]     "Strata NVFP4" README: the prompt path's BF16 projections (the
+             router among them) take FP32-exact inputs. The routing rule itself
+             is not on the pages; the reading taken: logits = x . Wr^T, the k
+             largest (ties to the lower expert id) in descending order, router
+             weights = softmax over those k logits.
   [S-MIX]    "Strata NVFP4" README, the re-quantized experts pack: in 27 of the
              48 layers the down projection is Q8_0 (more bytes, less error).
              The pages name the format but not its bytes; this oracle takes
@@ -265,6 +270,26 @@ def moe_grouped(x: np.ndarray, layer, ids: np.ndarray, w: np.ndarray,
         for i, p in enumerate(pairs):
             out[p // k] += float(w[rows[p // k], p % k]) * Y[i]
     return out
+
+
+# ----------------------------------------------------------------- router
+def router_topk(x: np.ndarray, w_router_bf16_bits: np.ndarray, k: int):
+    """[S-RT] x float64 [T][H] (exact values of the fp32 or bf16 inputs), Wr bf16 bits
+    [E][H]. Returns (ids int32 [T][k], weights float64 [T][k], logits float64 [T][E]):
+    logits = x Wr^T; ids = the k largest logits in descending order, equal logits
+    ordered by expert id; weights = softmax of the k selected logits."""
+    W_r = bf16_to_f64(np.asarray(w_router_bf16_bits, dtype=np.uint16))
+    logits = np.asarray(x, dtype=np.float64) @ W_r.T
+    T, E = logits.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    wts = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        ids[t] = order
+        sel = logits[t, order]
+        ex = np.exp(sel - sel[0])
+        wts[t] = ex / ex.sum()
+    return ids, wts, logits
 
 
 # ----------------------------------------------------------------- W4A8

@@ -530,3 +530,60 @@ def test_q8_0_negative_controls(monkeypatch):
         with pytest.raises((AssertionError, ValueError)):
             test_q8_0_dequant_bruteforce_all_codes()
         monkeypatch.undo()
+
+
+# ------------------------------------------------------------------ router
+def test_router_hand_example():
+    """T = 1, H = 2, E = 4, k = 2: logits (1, 3, 3, -1) -> ids (1, 2) (equal logits by
+    id), weights softmax(3, 3) = (1/2, 1/2); k = 3 adds expert 0 with weights
+    e^3 : e^3 : e^1 normalized."""
+    x = np.array([[1.0, 2.0]])
+    Wr = np.array([[1.0, 0.0], [1.0, 1.0], [-1.0, 2.0], [1.0, -1.0]], np.float32)
+    bits = W.f32_to_bf16_bits(Wr)
+    ids, w, lg = O.router_topk(x, bits, 2)
+    assert lg.tolist() == [[1.0, 3.0, 3.0, -1.0]]
+    assert ids.tolist() == [[1, 2]] and np.allclose(w, [[0.5, 0.5]], rtol=0, atol=1e-15)
+    ids, w, _ = O.router_topk(x, bits, 3)
+    assert ids.tolist() == [[1, 2, 0]]
+    z = math.exp(3) * 2 + math.exp(1)
+    assert np.allclose(w, [[math.exp(3) / z, math.exp(3) / z, math.exp(1) / z]], rtol=1e-15, atol=0)
+
+
+def test_router_against_sort_and_invariants():
+    rng = np.random.default_rng(6)
+    T, H, E, k = 20, 64, 40, 8
+    x = rng.standard_normal((T, H))
+    bits = W.draw_router(9, E, H)
+    ids, w, lg = O.router_topk(x, bits, k)
+    Wr = O.bf16_to_f64(bits)
+    assert np.allclose(lg, x @ Wr.T, rtol=1e-14, atol=1e-14)
+    for t in range(T):
+        ref = np.argsort(-lg[t], kind="stable")[:k]
+        assert ids[t].tolist() == ref.tolist()
+        assert np.all(np.diff(lg[t, ids[t]]) <= 0) and len(set(ids[t].tolist())) == k
+        assert abs(w[t].sum() - 1.0) < 1e-14 and np.all(np.diff(w[t]) <= 1e-16)
+        # softmax over the selected logits == full softmax renormalized over them
+        p = np.exp(lg[t] - lg[t].max())
+        p /= p.sum()
+        assert np.allclose(w[t], p[ids[t]] / p[ids[t]].sum(), rtol=1e-12)
+    # k = E selects everything in descending order; weights are the full softmax
+    ids_all, w_all, _ = O.router_topk(x[:2], bits, E)
+    assert sorted(ids_all[0].tolist()) == list(range(E))
+
+
+def test_router_bf16_weights_decode_and_negative_controls(monkeypatch):
+    """The router matrix is read as bf16 (not fp16); a sign or tie-order slip fails."""
+    x = np.array([[1.0, 2.0]])
+    bits = np.array([[0x3F80, 0x0000], [0x4000, 0x0000], [0xC000, 0x4040]], np.uint16)  # 1, 2, (-2, 3)
+    ids, _, lg = O.router_topk(x, bits, 2)
+    assert lg.tolist() == [[1.0, 2.0, 4.0]] and ids.tolist() == [[2, 1]]
+    as_fp16 = bits.view(np.float16).astype(np.float64)
+    assert not np.allclose(x @ as_fp16.T, lg)
+    def reversed_ties(x_, b_, k_):
+        W_r = O.bf16_to_f64(b_)
+        lg_ = x_ @ W_r.T
+        ids_ = np.argsort(-lg_, axis=1)[:, ::-1][:, :k_][:, ::-1]
+        return ids_.astype(np.int32), None, lg_
+    monkeypatch.setattr(O, "router_topk", reversed_ties)
+    with pytest.raises(AssertionError):
+        test_router_hand_example()

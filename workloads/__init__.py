@@ -43,6 +43,13 @@ along the inputs with one fp16 scale each):
 Recipe: code bytes uniform over all 256 values; scale = fp16(2^v / 8192) with
 v ~ U[-1, 1] per block (always a normal fp16 value), so weights are of the same
 order as the NVFP4 ones.
+
+Router (the step before the MoE: "Strata NVFP4" README, the prompt path's BF16
+projections, the router among them, fed FP32-exact inputs):
+  w_router uint16 [E][H]  bf16 bit patterns, N(0, 1) / sqrt(H) rounded to bf16, plus a
+                          per-expert bias row direction so that expert popularity is
+                          uneven (expert e's row gets + b_e * u, u a shared unit vector,
+                          b_e ~ N(0, 0.5)).
 """
 from __future__ import annotations
 
@@ -59,7 +66,7 @@ EXPERTS = 512
 TOPK = 8
 GROUP = 16
 
-PROJ_TAG = {"gate": 1, "up": 2, "down": 3, "down_q8": 4}
+PROJ_TAG = {"gate": 1, "up": 2, "down": 3, "down_q8": 4, "router": 5}
 Q8_BLOCK = 32
 _TAG_X, _TAG_IDS, _TAG_W, _TAG_GAMMA, _TAG_OUTLIER, _TAG_PERM = 11, 12, 13, 14, 15, 16
 
@@ -141,6 +148,16 @@ def draw_q8_expert(seed: int, e: int, N: int, K: int):
     v = g.uniform(-1.0, 1.0, size=(N, K // Q8_BLOCK))
     scales = (np.exp2(v) / 8192.0).astype(np.float16).view(np.uint16)
     return codes, scales
+
+
+def draw_router(seed: int, E: int = EXPERTS, H: int = HIDDEN) -> np.ndarray:
+    """bf16 bits [E][H] of a router matrix (see the module recipe)."""
+    g = _rng(seed, PROJ_TAG["router"])
+    w = g.standard_normal((E, H)) / np.sqrt(H)
+    u = g.standard_normal(H)
+    u /= np.linalg.norm(u)
+    w += g.normal(0.0, 0.5, size=(E, 1)) * u[None, :]
+    return f32_to_bf16_bits(w.astype(np.float32))
 
 
 def draw_gammas(seed: int, E: int) -> Dict[str, np.ndarray]:
