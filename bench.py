@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--decode-rounds", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run device-to-device copies of 1 GiB (the plain copy kernel whose HBM "
                          "counter readings scale the GEMM's FETCH_SIZE / WRITE_SIZE)")
@@ -163,6 +163,29 @@ def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4):
                 gbs_down=U * down_bytes / (res["down"] * 1e-6) / 1e9)
 
 
+def bench_router(T, reps=50):
+    """Router (logits -> top-8 -> softmax) on bf16 activations of the 8192-token workload's
+    first T rows: microseconds per call from events on the launch stream."""
+    import numpy as np
+    import torch
+    import nvfp4_quantized_moe_02_amd as nv
+    import workloads as W
+    x = torch.from_numpy(W.draw_activations(W.config_seed(3), T).view(np.int16)).view(torch.bfloat16).cuda()
+    wr = torch.from_numpy(W.draw_router(W.config_seed(3)).view(np.int16)).cuda()
+    ws = torch.empty(nv.router_workspace_size(T, 512), dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        nv.router_topk(x, wr, 8, ws=ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        nv.router_topk(x, wr, 8, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / reps
+
+
 # Kernel sources whose hash a traffic profile records: counters taken on other sources
 # no longer describe the kernel and are not reported.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gateup_t8192_zipf_traffic.md")
@@ -264,6 +287,10 @@ def main():
     if args.only in ("all", "w4a8"):
         w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2)
         log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
+    rt = None
+    if args.only in ("all", "router"):
+        rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
+        log(f"router: {rt}")
     q8 = None
     if args.only in ("all", "q8down"):
         # the mixed pack's layers: NVFP4 gate/up with a Q8_0 down projection
@@ -344,6 +371,10 @@ def main():
                                                           / 1e12 / PEAK_FP16_TFLOPS, 4),
                           "frac_of_int8_peak_step": round((w4["gu_flops"] + w4["dn_flops"]) / (w4["ms"] * 1e-3)
                                                           / 1e12 / PEAK_INT8_TOPS, 4)}
+    if rt is not None:
+        result["router"] = {"workload": "logits of 512 experts (bf16 router matrix, hidden 2048) on bf16 activations, "
+                                        "top-8, softmax over the selected logits; eager calls incl. launch overhead",
+                            **rt}
     if q8 is not None:
         pq = q8["prefill"]
         result["q8_down"] = {

@@ -196,6 +196,24 @@ int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32
                             int32_t act, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* Router (the step before the routed experts): logits[t][e] = sum_h x[t][h] * Wr[e][h] with a
+ * bf16 router matrix Wr [E][H] (raw bf16 bits) and x [T][H] in F32 or BF16. The inputs are
+ * used exactly ("Strata NVFP4" README: FP32-exact inputs to the prompt path's BF16
+ * projections, the router among them): an fp32 x is split into three bf16 parts whose
+ * products with the weights are exact, summed in fp32 on matrix cores. Then, per token,
+ * topk_ids[t][0..topk) = the topk largest logits in descending order (equal logits in
+ * expert-id order; NaN logits rank below every number) and topk_weights[t][j] = softmax of
+ * those topk logits (the rule is this library's reading; the pages do not give it). The
+ * outputs feed nvfp4_moe_decode / nvfp4_moe_prefill directly. ws needs
+ * nvfp4_router_workspace_size() bytes (the fp32 logits). T == 0 is a no-op.
+ * Errors: EINVAL for null or misaligned pointers (x, w_router and ws 16-byte aligned), T < 0,
+ * x_dtype other than F32/BF16, topk < 1 or topk > E; EUNSUPPORTED for H not a multiple of
+ * 64, E not a multiple of 32 or above 2048, topk > 64; EWORKSPACE. */
+size_t nvfp4_router_workspace_size(int32_t T, int32_t E);
+int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const uint16_t* w_router, int32_t E,
+                      int32_t topk, int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* nvfp4_status_string(int status);
 

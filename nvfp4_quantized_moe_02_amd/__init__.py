@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     moe_prefill,
     quant_rows_i8,
     route,
+    router_topk,
+    router_workspace_size,
     decode_workspace_size,
     prefill_workspace_size,
     route_workspace_size,

@@ -58,6 +58,10 @@ _SIGS = {
                                        ctypes.c_void_p]),
     "nvfp4_quant_rows_i8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "nvfp4_router_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 2),
+    "nvfp4_router_topk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4_moe_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 5),
     "nvfp4_moe_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
@@ -248,6 +252,27 @@ def quant_rows_i8(x: torch.Tensor):
     _check("nvfp4_quant_rows_i8", lib.nvfp4_quant_rows_i8(_ptr(x), DTYPE[x.dtype], rows, cols, _ptr(q), _ptr(s),
                                                           _stream(x.device)))
     return q, s
+
+
+def router_workspace_size(T: int, E: int) -> int:
+    return int(load_library().nvfp4_router_workspace_size(T, E))
+
+
+def router_topk(x: torch.Tensor, w_router: torch.Tensor, topk: int, ws: Optional[torch.Tensor] = None):
+    """x [T][H] float32 or bfloat16, w_router bf16 [E][H] (bfloat16 or int16 bits).
+    Returns (topk_ids int32 [T][topk], topk_weights float32 [T][topk])."""
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    E = int(w_router.shape[0])
+    ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    need = router_workspace_size(T, E)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check("nvfp4_router_topk", lib.nvfp4_router_topk(_ptr(x), DTYPE[x.dtype], T, H, _ptr(w_router), E, topk,
+                                                      _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(),
+                                                      _stream(x.device)))
+    return ids, wts
 
 
 def decode_workspace_size(T: int, H: int, I: int, E: int, topk: int) -> int:

@@ -159,6 +159,28 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
   return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, 0, scale, as_stream(stream)));
 }
 
+size_t nvfp4_router_workspace_size(int32_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return align_up((size_t)T * E * 4);
+}
+
+int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const uint16_t* w_router, int32_t E,
+                      int32_t topk, int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (T < 0 || H < 1 || E < 1 || topk < 1 || topk > E || !w_router || !ws) return NVFP4_EINVAL;
+  if (T > 0 && (!x || !topk_ids || !topk_weights)) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(ws, 16) || !aligned(topk_ids, 4) ||
+      !aligned(topk_weights, 4))
+    return NVFP4_EINVAL;
+  if ((H % 64) != 0 || (E % 32) != 0 || E > 2048 || topk > 64) return NVFP4_EUNSUPPORTED;
+  if (ws_bytes < nvfp4_router_workspace_size(T, E)) return NVFP4_EWORKSPACE;
+  if (T == 0) return NVFP4_OK;
+  (void)hipGetLastError();
+  return hip_status(launch_router(x, x_dtype == NVFP4_BF16 ? 1 : 0, T, H, w_router, E, topk,
+                                  reinterpret_cast<float*>(ws), topk_ids, topk_weights, as_stream(stream)));
+}
+
 size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk) {
   (void)H;
   (void)E;

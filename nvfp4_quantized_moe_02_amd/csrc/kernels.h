@@ -65,6 +65,12 @@ hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const We
                          void* out, int out_dtype, float* h, int32_t* hdr, unsigned long long* flags,
                          hipStream_t st);
 
+// router.hip: logits [T][E] fp32 (workspace), then ids/weights [T][k]. x_dtype 1 = bf16,
+// 0 = fp32 (split exactly into three bf16 parts). E % 32 == 0, E <= 2048, k <= 64,
+// H % 16 == 0 (H % 64 == 0 for few tokens).
+hipError_t launch_router(const void* x, int x_dtype, int T, int H, const uint16_t* wr, int E, int k, float* logits,
+                         int32_t* ids, float* wts, hipStream_t st);
+
 // prefill.hip
 constexpr int kTileM = 128;
 hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* sorted_pairs,

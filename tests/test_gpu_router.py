@@ -1,0 +1,111 @@
+"""GPU parity of the router (logits -> top-k -> softmax over the selected logits) through
+the C-ABI, against the float64 oracle. The logits the library leaves in its workspace are
+checked against the oracle's within the fp32 accumulation error bound; the selection and
+the weights are then checked exactly against those logits (so a near-tie between the k-th
+and (k+1)-th expert cannot make the test flaky), and the ids against the oracle's wherever
+no near-tie exists."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import DEV, bf16_dev
+
+pytestmark = pytest.mark.gpu
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+
+
+def _run(x_dev, x_f64, wr_bits, k):
+    T, E = x_dev.shape[0], wr_bits.shape[0]
+    ws = torch.empty(nv.router_workspace_size(T, E), dtype=torch.uint8, device=DEV)
+    ids, wts = nv.router_topk(x_dev, torch.from_numpy(wr_bits.view(np.int16)).to(DEV), k, ws=ws)
+    torch.cuda.synchronize()
+    lg = ws[:T * E * 4].view(torch.float32).view(T, E).cpu().numpy().astype(np.float64)
+    ids, wts = ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64)
+    rids, rw, rlg = O.router_topk(x_f64, wr_bits, k)
+    # fp32 accumulation of exact products: at most (parts * H / 16 + 8) roundings of 2^-24
+    Wr = O.bf16_to_f64(wr_bits)
+    parts = 3 if x_dev.dtype == torch.float32 else 1
+    bound = (parts * x_f64.shape[1] / 16 + 8) * 2.0 ** -24 * (np.abs(x_f64) @ np.abs(Wr).T)
+    assert np.all(np.abs(lg - rlg) <= bound), float(np.max(np.abs(lg - rlg) / np.maximum(bound, 1e-300)))
+    # selection and weights exactly from the GPU logits (float32 values, tie to lower id)
+    for t in range(T):
+        want = sorted(range(E), key=lambda e: (-lg[t, e], e))[:k]
+        assert ids[t].tolist() == want, t
+        sel = lg[t, want]
+        ex = np.exp(sel - sel[0])
+        assert np.allclose(wts[t], ex / ex.sum(), rtol=2e-6, atol=1e-7), t
+    # against the oracle's ids where the k-th and (k+1)-th oracle logits are not within
+    # twice the bound of each other
+    ntie = 0
+    for t in range(T):
+        if ids[t].tolist() == rids[t].tolist():
+            continue
+        srt = np.sort(rlg[t])[::-1]
+        assert k < E and srt[k - 1] - srt[k] <= 2 * bound[t].max() or \
+            sorted(ids[t].tolist()) == sorted(rids[t].tolist()), t
+        ntie += 1
+    return ntie
+
+
+@pytest.mark.parametrize("T", [8192, 1, 4, 100])
+def test_router_bf16_inputs(T):
+    xb = W.draw_activations(W.config_seed(3), T)
+    wr = W.draw_router(W.config_seed(3))
+    ntie = _run(bf16_dev(xb), O.bf16_to_f64(xb), wr, 8)
+    print(f"router T={T} bf16 x: {ntie} tokens with a near-tie at the k-th expert")
+
+
+@pytest.mark.parametrize("T", [4, 64, 300])
+def test_router_fp32_inputs_exact_split(T):
+    """fp32 activations that bf16 cannot hold: the three-part split keeps every product
+    exact (the bound is that of fp32 accumulation only)."""
+    rng = np.random.default_rng(T)
+    x = (rng.standard_normal((T, 512)) * np.exp(rng.uniform(-3, 3, (T, 1)))).astype(np.float32)
+    wr = W.draw_router(5, E=96, H=512)
+    ntie = _run(torch.from_numpy(x).to(DEV), x.astype(np.float64), wr, 6)
+    print(f"router T={T} fp32 x: {ntie} near-ties")
+    # rounding x to bf16 first (what the pages' fix avoids) is measurably different
+    xb = W.f32_to_bf16_bits(x)
+    _, _, lg_b = O.router_topk(O.bf16_to_f64(xb), wr, 6)
+    _, _, lg_x = O.router_topk(x.astype(np.float64), wr, 6)
+    assert np.abs(lg_b - lg_x).max() > 1e-4 * np.abs(lg_x).max()
+
+
+def test_router_ties_and_k_equal_E_and_nan():
+    """Duplicate router rows give equal logits: the lower expert id comes first. k = E
+    returns every expert. A NaN logit ranks last."""
+    H, E = 128, 64
+    wr = W.draw_router(7, E=E, H=H)
+    wr[9] = wr[40]
+    wr[33] = wr[2]
+    xb = W.draw_activations(7, 16, H)
+    _run(bf16_dev(xb), O.bf16_to_f64(xb), wr, 8)
+    ids, _ = nv.router_topk(bf16_dev(xb), torch.from_numpy(wr.view(np.int16)).to(DEV), E)
+    assert all(sorted(r) == list(range(E)) for r in ids.cpu().numpy().tolist())
+    lg = O.bf16_to_f64(xb) @ O.bf16_to_f64(wr).T
+    both = [t for t in range(16) if set([9, 40]) <= set(np.argsort(-lg[t], kind="stable")[:8].tolist())]
+    ids8, _ = nv.router_topk(bf16_dev(xb), torch.from_numpy(wr.view(np.int16)).to(DEV), 8)
+    for t in both:
+        r = ids8[t].cpu().numpy().tolist()
+        assert r.index(9) == r.index(40) - 1
+    wr2 = wr.copy()
+    wr2[5, 0] = 0x7FC0  # NaN weight -> NaN logit for expert 5
+    ids_n, _ = nv.router_topk(bf16_dev(xb), torch.from_numpy(wr2.view(np.int16)).to(DEV), E)
+    assert np.all(ids_n[:, -1].cpu().numpy() == 5)
+
+
+def test_router_validation():
+    x = torch.zeros((4, 96), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((64, 96), dtype=torch.int16, device=DEV)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.router_topk(x, w, 8)                       # H % 64 != 0
+    assert ei.value.status == -2
+    x = torch.zeros((4, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.router_topk(x, torch.zeros((48, 128), dtype=torch.int16, device=DEV), 8)   # E % 32
+    assert ei.value.status == -2
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.router_topk(x, torch.zeros((64, 128), dtype=torch.int16, device=DEV), 65)  # k > E
+    assert ei.value.status == -1
