@@ -10,8 +10,9 @@ layer (65 GB), so no step finds its weights in the 256 MB Infinity Cache.
 Also reported on the same line: per-kernel times from HIP events on the launch stream
 and the roofline of the dominant kernel (the gate/up grouped GEMM against the dense
 fp16 matrix-core peak), decode HBM bandwidth at 1 and 4 tokens (hipGraph of 48
-layer calls, replayed), the W4A8 prefill at 32768 tokens, and the CPU oracle timed on
-a bounded sample of the prefill workload.
+layer calls, replayed), the W4A8 prefill at 32768 tokens, the router, the Q8_0-down
+layer, the host-CPU decode projection, and the CPU oracle timed on a bounded sample of
+the prefill workload.
 """
 import argparse
 import json
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--decode-rounds", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router", "host"], default="all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run device-to-device copies of 1 GiB (the plain copy kernel whose HBM "
                          "counter readings scale the GEMM's FETCH_SIZE / WRITE_SIZE)")
@@ -186,6 +187,60 @@ def bench_router(T, reps=50):
     return t0.elapsed_time(t1) * 1e3 / reps
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_host(reps=24):
+    """The host-CPU expert projection (nvfp4_moe_decode_host) on a full 512-expert layer in
+    host memory: 8 seeded experts tiled to 512 (content does not change the speed), calls
+    rotating over `reps` seeded Zipf routings; GB/s counts the weight bytes of the unique
+    experts each call reads."""
+    import numpy as np
+    import torch
+    import nvfp4_quantized_moe_02_amd as nv
+    import workloads as W
+    E, H, I, k = W.EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    sub = W.draw_layer(W.config_seed(3), E=8, H=H, I=I)
+    gam = W.draw_gammas(W.config_seed(3), E)
+
+    def tiled(p, name):
+        r = E // 8
+        return nv.Proj(torch.from_numpy(np.tile(p.codes, (r, 1, 1))), torch.from_numpy(np.tile(p.scales, (r, 1, 1))),
+                       torch.from_numpy(gam[name]))
+    L = nv.Layer(tiled(sub.gate, "gate"), tiled(sub.up, "up"), tiled(sub.down, "down"))
+    per_expert = GATEUP_BYTES + DOWN_BYTES_NVFP4
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    out = {"cpu": cpu_model(), "isa": nv.host_isa(), "threads": threads,
+           "workload": "decode projection of one layer on the host CPU (512 NVFP4 experts in host memory, "
+                       "top-8 Zipf(1.1) routing, hidden 2048, intermediate 768, FP32 arithmetic)"}
+    for T, nt in ((1, threads), (4, threads), (1, 1)):
+        calls = []
+        for r in range(reps):
+            ids = W.draw_routing_zipf(1000 + r, T, E, k)
+            calls.append((torch.from_numpy(W.draw_activations(1000 + r, T, H).view(np.int16)).view(torch.bfloat16),
+                          torch.from_numpy(ids), torch.from_numpy(W.draw_router_weights(1000 + r, T, k)),
+                          len(np.unique(ids))))
+        for c in calls[:3]:
+            nv.moe_decode_host(c[0], L, c[1], c[2], n_threads=nt)
+        n = reps if nt > 1 else 6
+        t = time.perf_counter()
+        for c in calls[:n]:
+            nv.moe_decode_host(c[0], L, c[1], c[2], n_threads=nt)
+        dt = (time.perf_counter() - t) / n
+        u = sum(c[3] for c in calls[:n]) / n
+        out[f"t{T}" + ("_1thread" if nt == 1 else "")] = {"ms": round(dt * 1e3, 3), "unique_experts": round(u, 2),
+                                                           "GB/s": round(u * per_expert / dt / 1e9, 1)}
+    return out
+
+
 # Kernel sources whose hash a traffic profile records: counters taken on other sources
 # no longer describe the kernel and are not reported.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gateup_t8192_zipf_traffic.md")
@@ -291,6 +346,10 @@ def main():
     if args.only in ("all", "router"):
         rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
         log(f"router: {rt}")
+    hd = None
+    if args.only in ("all", "host"):
+        hd = bench_host()
+        log(f"host decode: {hd}")
     q8 = None
     if args.only in ("all", "q8down"):
         # the mixed pack's layers: NVFP4 gate/up with a Q8_0 down projection
@@ -390,6 +449,8 @@ def main():
         if dec:
             result["q8_down"]["decode_time_vs_nvfp4"] = {
                 k: round(q8[f"decode_{k}"]["us"] / dec[k]["us"], 3) for k in dec if f"decode_{k}" in q8}
+    if hd is not None:
+        result["host_decode"] = hd
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

@@ -26,11 +26,13 @@
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA tensor's
- *     data_ptr()) owned by the caller. The library never allocates, frees or retains
- *     them, and keeps no state between calls: it is safe to call from several host
- *     threads on different streams, provided their workspaces and outputs differ.
+ *     data_ptr()) owned by the caller, except in the *_host entry points, which take
+ *     host pointers. The library never allocates, frees or retains them, and keeps no
+ *     state between calls (the host entry points keep worker threads): it is safe to
+ *     call from several host threads on different streams, provided their workspaces
+ *     and outputs differ.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. All
- *     work is enqueued on it asynchronously; no call synchronizes the host.
+ *     device work is enqueued on it asynchronously; no device call synchronizes the host.
  *   - Arguments are validated completely before anything is enqueued: a call that
  *     returns an error has enqueued nothing and written nothing. A failed kernel
  *     launch returns NVFP4_EHIP.
@@ -66,7 +68,8 @@ typedef enum {
   NVFP4_EINVAL = -1,       /* a null or misaligned pointer, a size out of range */
   NVFP4_EUNSUPPORTED = -2, /* a valid request this build does not implement */
   NVFP4_EWORKSPACE = -3,   /* ws_bytes smaller than the matching *_workspace_size() */
-  NVFP4_EHIP = -4          /* a HIP runtime error while enqueueing */
+  NVFP4_EHIP = -4,         /* a HIP runtime error while enqueueing */
+  NVFP4_ENOMEM = -5        /* a host allocation failed (host entry points only) */
 } nvfp4_status;
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
@@ -213,6 +216,31 @@ size_t nvfp4_router_workspace_size(int32_t T, int32_t E);
 int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const uint16_t* w_router, int32_t E,
                       int32_t topk, int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* Host-CPU share of the experts ("Strata NVFP4" README: AVX-512 NVFP4 kernels compute the
+ * CPU's share of the experts from host DRAM, with an AVX2 path for CPUs without AVX-512).
+ * The decode projection above on HOST memory, run on this process's CPU threads: every
+ * pointer (x, the weight planes and scales, topk_ids, topk_weights, out) is a host pointer
+ * owned by the caller, with the device layout and no alignment requirement. Each weight is
+ * decoded exactly to fp32, dot products and SwiGLU run in FP32, h stays in FP32, and the
+ * routed pairs of an output row are added in a fixed order, so the result does not depend
+ * on n_threads. x [T][H] F32 or BF16, any T >= 0; out float [T][H]. To split a layer's
+ * experts between the GPU and the CPU, give each call the same topk_ids with the other
+ * side's experts replaced by -1 (dropped) and add the two outputs.
+ * n_threads: 0 = one per CPU this process may run on. isa: NVFP4_ISA_AUTO (the widest the
+ * CPU has) or a narrower one to force (results differ only in FP32 summation order).
+ * dropped (may be NULL) receives the number of pairs whose id is outside [0, E).
+ * The call returns when out is written; it makes no HIP call. Concurrent calls run one
+ * after the other on the library's worker threads.
+ * Errors: EINVAL (null pointers, shapes that disagree, K not a multiple of 32, unknown
+ * dtype, format or isa, n_threads < 0); EUNSUPPORTED for a Q8_0 gate or up projection,
+ * an isa the CPU lacks, T * topk above 2^31 - 1; ENOMEM. T == 0 writes nothing. */
+typedef enum { NVFP4_ISA_AUTO = 0, NVFP4_ISA_PORTABLE = 1, NVFP4_ISA_AVX2 = 2, NVFP4_ISA_AVX512 = 3 } nvfp4_isa;
+int32_t nvfp4_host_isa(void); /* the widest nvfp4_isa this CPU supports */
+int nvfp4_moe_decode_host(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                          const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                          const int32_t* topk_ids, const float* topk_weights, int32_t topk, float* out,
+                          int32_t n_threads, int32_t isa, int64_t* dropped);
 
 /* A static, human-readable name for a status code. */
 const char* nvfp4_status_string(int status);

@@ -13,6 +13,9 @@ from .binding import (  # noqa: F401
     Proj,
     Q8Proj,
     FORMAT,
+    ISA,
+    host_isa,
+    moe_decode_host,
     Layer,
     dequant,
     lib_path,

@@ -18,6 +18,7 @@ _LIB_NAME = "libnvfp4moe.so"
 
 DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 ACT = {"bf16": 0, "w4a8": 1, "w4a8_f16": 2}
+ISA = {"auto": 0, "portable": 1, "avx2": 2, "avx512": 3}
 
 _lib = None
 
@@ -79,6 +80,12 @@ _SIGS = {
                                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4_moe_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 6),
+    "nvfp4_host_isa": (ctypes.c_int32, []),
+    "nvfp4_moe_decode_host": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                             ctypes.POINTER(_Weight), ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "nvfp4_moe_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
@@ -305,6 +312,29 @@ def moe_decode(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor
         _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
         _ptr(w), k, _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
     return out
+
+
+def host_isa() -> str:
+    """The widest instruction set the host row kernels can use on this CPU."""
+    code = int(load_library().nvfp4_host_isa())
+    return next(k for k, v in ISA.items() if v == code)
+
+
+def moe_decode_host(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor, n_threads: int = 0,
+                    isa: str = "auto", out: Optional[torch.Tensor] = None):
+    """The routed-expert projection on the host CPU: every tensor (the layer's too) in host
+    memory; x [T][H] float32 or bfloat16; returns (out float32 [T][H], dropped pairs)."""
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    k = int(ids.shape[1])
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32)
+    g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
+    dropped = ctypes.c_int64(0)
+    _check("nvfp4_moe_decode_host", lib.nvfp4_moe_decode_host(
+        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+        _ptr(w), k, _ptr(out), n_threads, ISA[isa], ctypes.byref(dropped)))
+    return out, int(dropped.value)
 
 
 def moe_prefill(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor, act: str = "bf16",

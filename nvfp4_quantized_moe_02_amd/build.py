@@ -1,4 +1,5 @@
-"""Build libnvfp4moe.so in-tree with hipcc for gfx950 (cross-compiles without a GPU)."""
+"""Build libnvfp4moe.so in-tree: the HIP sources with hipcc for gfx950 (cross-compiles
+without a GPU), the host-only sources (*.cpp) with the host C++ compiler."""
 import glob
 import os
 import shutil
@@ -28,10 +29,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall"]
+
+
+def cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), "/opt/rocm/llvm/bin/clang++"):
+        if c and (os.path.exists(c) or shutil.which(c)):
+            return c
+    raise RuntimeError("no host C++ compiler found")
+
+
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    objs = []
+    for src in sorted(glob.glob(os.path.join(PKG, "csrc", "*.cpp"))):
+        obj = os.path.join(PKG, "csrc", os.path.basename(src)[:-4] + ".host.o")
+        cmd = [cxx(), *HOST_FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("host compile failed:\n" + r.stdout + r.stderr)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-x", "none", *objs, "-pthread", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

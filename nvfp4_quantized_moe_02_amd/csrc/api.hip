@@ -1,7 +1,10 @@
 // The C ABI (include/nvfp4moe.h): argument validation, workspace layout and launch
 // order. Every entry point validates all of its arguments before enqueueing anything.
 #include "../../include/nvfp4moe.h"
+#include "host.h"
 #include "kernels.h"
+
+#include <new>
 
 using namespace nvfp4;
 
@@ -104,6 +107,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_EUNSUPPORTED: return "unsupported configuration";
     case NVFP4_EWORKSPACE: return "workspace too small";
     case NVFP4_EHIP: return "HIP runtime error";
+    case NVFP4_ENOMEM: return "host memory allocation failed";
     default: return "unknown status";
   }
 }
@@ -317,6 +321,46 @@ int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32
   if (stage < 0 || stage > 3) return NVFP4_EINVAL;
   return prefill_impl(stage, stage, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, act, out,
                       out_dtype, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ host-CPU share
+static bool host_weight_ok(const nvfp4_weight* w) {
+  if (!w || (w->format != NVFP4_FMT_NVFP4 && w->format != NVFP4_FMT_Q8_0)) return false;
+  return w->codes && w->scales && (w->global || w->format == NVFP4_FMT_Q8_0) && w->N > 0 && w->K > 0 &&
+         (w->K % 32) == 0;
+}
+
+static host::Weight host_args(const nvfp4_weight* w) {
+  return host::Weight{w->codes, w->scales, w->global, w->N, w->K, w->format == NVFP4_FMT_Q8_0 ? 1 : 0};
+}
+
+int32_t nvfp4_host_isa(void) { return host::best_isa(); }
+
+int nvfp4_moe_decode_host(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                          const nvfp4_weight* up, const nvfp4_weight* down, int32_t E, const int32_t* topk_ids,
+                          const float* topk_weights, int32_t topk, float* out, int32_t n_threads, int32_t isa,
+                          int64_t* dropped) {
+  if (T < 0 || H < 1 || E < 1 || topk < 1 || n_threads < 0) return NVFP4_EINVAL;
+  if (T > 0 && (!x || !topk_ids || !topk_weights || !out)) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (isa < NVFP4_ISA_AUTO || isa > NVFP4_ISA_AVX512) return NVFP4_EINVAL;
+  if (!host_weight_ok(gate) || !host_weight_ok(up) || !host_weight_ok(down)) return NVFP4_EINVAL;
+  const int I = gate->N;
+  if (gate->K != H || up->K != H || up->N != I || down->N != H || down->K != I) return NVFP4_EINVAL;
+  if (gate->format != NVFP4_FMT_NVFP4 || up->format != NVFP4_FMT_NVFP4) return NVFP4_EUNSUPPORTED;
+  if (isa > host::best_isa()) return NVFP4_EUNSUPPORTED;
+  if ((int64_t)T * topk > 0x7fffffff) return NVFP4_EUNSUPPORTED;
+  int64_t d = 0;
+  if (T > 0) {
+    try {
+      d = host::moe_decode(x, x_dtype, T, H, I, host_args(gate), host_args(up), host_args(down), E, topk_ids,
+                           topk_weights, topk, out, n_threads, isa);
+    } catch (const std::bad_alloc&) {
+      return NVFP4_ENOMEM;
+    }
+  }
+  if (dropped) *dropped = d;
+  return NVFP4_OK;
 }
 
 }  // extern "C"

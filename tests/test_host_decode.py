@@ -1,0 +1,163 @@
+"""The host-CPU expert projection (nvfp4_moe_decode_host) against the float64 oracle.
+It runs on this machine's CPU, so these tests need the built library but no GPU.
+
+Bar: FP32 arithmetic over exactly decoded weights, so the max per-row relative L2 error
+against the oracle is held to 1e-5 (the GPU's fp16-operand paths are held to 2e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+
+TOL = 1e-5
+
+
+def isas():
+    order = ["portable", "avx2", "avx512"]
+    return order[: order.index(nv.host_isa()) + 1]
+
+
+def host_layer(lay):
+    return nv.Layer.from_numpy(lay, "cpu")
+
+
+def bf16_cpu(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def case(seed, T, E=16, H=512, I=256, k=4, down_fmt="nvfp4"):
+    lay = W.draw_layer(seed, E=E, H=H, I=I, down_fmt=down_fmt)
+    xb = W.draw_activations(seed, T, H)
+    ids = W.draw_routing_zipf(seed, T, E, k)
+    w = W.draw_router_weights(seed, T, k)
+    return lay, xb, ids, w
+
+
+def run(lay, xb, ids, w, **kw):
+    return nv.moe_decode_host(bf16_cpu(xb), host_layer(lay), torch.from_numpy(ids), torch.from_numpy(w), **kw)
+
+
+@pytest.mark.parametrize("isa", isas())
+@pytest.mark.parametrize("T", [1, 3, 8, 21])
+def test_parity_nvfp4(isa, T):
+    lay, xb, ids, w = case(11 + T, T)
+    y, dropped = run(lay, xb, ids, w, isa=isa, n_threads=3)
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    err = float(np.max(O.rel_l2_rows(y.numpy(), ref)))
+    assert dropped == 0
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("isa", isas())
+def test_parity_q8_down(isa):
+    lay, xb, ids, w = case(5, 6, down_fmt="q8_0")
+    y, _ = run(lay, xb, ids, w, isa=isa)
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    assert float(np.max(O.rel_l2_rows(y.numpy(), ref))) < TOL
+
+
+def test_full_width_layer():
+    """H = 2048, I = 768 (the decode layer's widths) for 8 experts, one token routed to all."""
+    E, H, I = 8, W.HIDDEN, W.INTER
+    lay = W.draw_layer(3, E=E, H=H, I=I)
+    xb = W.draw_activations(3, 2, H)
+    ids = np.array([[3, 0, 7, 1, 5, 2, 6, 4], [1, 1, 6, 0, 2, 2, 7, 3]], dtype=np.int32)
+    w = W.draw_router_weights(3, 2, 8)
+    y, _ = run(lay, xb, ids, w)
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    assert float(np.max(O.rel_l2_rows(y.numpy(), ref))) < TOL
+
+
+@pytest.mark.parametrize("isa", isas())
+def test_thread_count_does_not_change_bits(isa):
+    lay, xb, ids, w = case(7, 8, k=8)
+    outs = [run(lay, xb, ids, w, isa=isa, n_threads=n)[0] for n in (1, 2, 5, 0)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_f32_input_equals_bf16_input():
+    lay, xb, ids, w = case(9, 5)
+    x32 = bf16_cpu(xb).float()  # the same values, exactly
+    L = host_layer(lay)
+    a, _ = nv.moe_decode_host(bf16_cpu(xb), L, torch.from_numpy(ids), torch.from_numpy(w))
+    b, _ = nv.moe_decode_host(x32, L, torch.from_numpy(ids), torch.from_numpy(w))
+    assert torch.equal(a, b)
+
+
+def test_dropped_and_duplicate_ids():
+    E, T, k = 16, 4, 4
+    lay, xb, ids, w = case(13, T, E=E, k=k)
+    ids = ids.copy()
+    ids[0, 1] = -1
+    ids[2, 3] = E          # out of range: dropped
+    ids[1, 2] = ids[1, 0]  # duplicate within a token: summed
+    y, dropped = run(lay, xb, ids, w)
+    assert dropped == 2
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    assert float(np.max(O.rel_l2_rows(y.numpy(), ref))) < TOL
+    # a token whose every id is dropped gets zeros
+    ids[3, :] = -5
+    y, dropped = run(lay, xb, ids, w)
+    assert dropped == 2 + k
+    assert torch.count_nonzero(y[3]) == 0
+
+
+def test_expert_split_adds_up():
+    """Splitting the experts between two calls (the other side's ids set to -1) and adding
+    the outputs gives the one-call result up to FP32 summation order."""
+    E, T = 16, 6
+    lay, xb, ids, w = case(17, T, E=E, k=4)
+    full, _ = run(lay, xb, ids, w)
+    a_ids = np.where(ids % 2 == 0, ids, -1).astype(np.int32)
+    b_ids = np.where(ids % 2 == 1, ids, -1).astype(np.int32)
+    ya, da = run(lay, xb, a_ids, w)
+    yb, db = run(lay, xb, b_ids, w)
+    assert da + db == ids.size
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    assert float(np.max(O.rel_l2_rows((ya + yb).numpy(), ref))) < TOL
+    assert float(np.max(O.rel_l2_rows((ya + yb).numpy(), full.numpy().astype(np.float64)))) < TOL
+
+
+def test_nan_scale_poisons_only_its_expert():
+    lay, xb, ids, w = case(19, 4, E=16, k=2)
+    L = host_layer(lay)
+    used = set(int(e) for e in ids.ravel())
+    unused = [e for e in range(16) if e not in used]
+    assert unused
+    for p in (L.gate, L.up, L.down):
+        p.scales[unused] = 0x7F  # E4M3 NaN
+    y, _ = nv.moe_decode_host(bf16_cpu(xb), L, torch.from_numpy(ids), torch.from_numpy(w))
+    assert torch.isfinite(y).all()
+    e = next(iter(used))
+    L.down.scales[e, 0, 0] = 0x7F
+    y, _ = nv.moe_decode_host(bf16_cpu(xb), L, torch.from_numpy(ids), torch.from_numpy(w))
+    hit = [t for t in range(ids.shape[0]) if e in ids[t]]
+    assert torch.isnan(y[hit, 0]).all()
+    assert torch.isfinite(y[:, 1:]).all()
+
+
+def test_empty_and_validation():
+    lay, xb, ids, w = case(23, 2)
+    L = host_layer(lay)
+    y, d = nv.moe_decode_host(bf16_cpu(xb[:0]), L, torch.from_numpy(ids[:0]), torch.from_numpy(w[:0]))
+    assert y.shape == (0, lay.H) and d == 0
+    x = bf16_cpu(xb)
+    ti, tw = torch.from_numpy(ids), torch.from_numpy(w)
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.moe_decode_host(x, nv.Layer(L.gate, L.up, L.gate), ti, tw)  # down has the wrong shape
+    assert e.value.status == -1
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.moe_decode_host(x, L, ti, tw, n_threads=-1)
+    assert e.value.status == -1
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.moe_decode_host(x.half(), L, ti, tw)  # fp16 activations are not accepted
+    assert e.value.status == -1
+    q8 = W.draw_layer(23, E=16, H=lay.I, I=lay.H, down_fmt="q8_0").down  # [E][I][H] Q8_0
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.moe_decode_host(x, nv.Layer(nv.Q8Proj.from_numpy(q8, "cpu"), L.up, L.down), ti, tw)
+    assert e.value.status == -2
