@@ -36,7 +36,7 @@ constexpr int kUB = 4;            // down units (one expert x 4 rows) a wave loa
 
 struct DecodeSmem {
   int ids[64];    // each pair's expert id, or -1 when dropped
-  int uniq[64];   // unique experts in order of first appearance
+  int uniq[64];   // unique experts in ascending id order
   int list[64];   // pairs grouped by unique expert, each group in pair order
   int start[65];  // group boundaries in list
   float wp[64];   // router weight of each pair
@@ -82,8 +82,8 @@ constexpr int kVmcnt0 = (7 << 4) | (0xF << 8);
 
 // Setup, called by every thread of the block (it holds barriers). The loads of the
 // routing ids, the router weights and the activations are issued together; wave 0 then
-// forms the unique-expert list with cross-lane shuffles (order of first appearance)
-// and the pair list of each unique expert.
+// forms the unique-expert list (ascending ids) and the pair list of each unique expert
+// with one ballot per id bit.
 __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x) {
   const int tid = threadIdx.x;
   int e = -1;
@@ -103,28 +103,40 @@ __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x)
     const int ev = valid ? e : -1;
     sm.ids[tid] = ev;
     sm.wp[tid] = wv;
-    // Group the pairs by expert, experts in order of first appearance: the lowest lane
-    // not yet grouped names the next expert (scalar bit scan + readlane, no LDS reads),
-    // a ballot finds all lanes holding it, ranks in lane order give the pair order.
+    // Group the pairs by expert, experts in ascending id order, pairs in pair order, with
+    // no loop over the experts: from the top bit of the id down, one ballot per bit
+    // narrows each lane's mask of lanes with the same id and collects the lanes with a
+    // smaller id. A pair's list position is the count of smaller-id pairs plus its rank
+    // among its expert's pairs; the lowest lane of an expert writes the group entry.
     const uint64_t lt = (1ull << tid) - 1ull;
-    uint64_t rem = __ballot(valid);
+    const uint64_t vm = __ballot(valid);
     const uint64_t dm = __ballot(tid < a.P && !valid);
-    int start = 0, nu = 0;
-    while (rem) {
-      const int eu = __builtin_amdgcn_readlane(ev, __builtin_ctzll(rem));
-      const bool m = ev == eu;
-      const uint64_t mm = __ballot(m);
-      if (m) sm.list[start + __popcll(mm & lt)] = tid;
-      if (tid == 0) {
-        sm.uniq[nu] = eu;
-        sm.start[nu] = start;
-      }
-      start += __popcll(mm);
-      ++nu;
-      rem &= ~mm;
+    uint64_t less = 0ull, same = valid ? vm : 0ull;
+    // One token: its valid slots are taken in slot order, each as its own group (an
+    // expert named twice is read twice); this skips the ballots, the slowest part of the
+    // set-up at one token.
+    const int nbits = a.T == 1 ? 0 : 32 - __builtin_clz((unsigned)(a.E > 1 ? a.E - 1 : 1));
+    if (a.T == 1) {
+      same = valid ? (1ull << tid) : 0ull;
+      less = vm & lt;
+    }
+    for (int b = nbits - 1; b >= 0; --b) {
+      const bool bit = (ev >> b) & 1;
+      const uint64_t mb = __ballot(bit);
+      less |= bit ? (same & ~mb) : 0ull;
+      same &= bit ? mb : ~mb;
+    }
+    const bool first = valid && (same & lt) == 0ull;
+    const uint64_t fm = __ballot(first);
+    if (valid) sm.list[__popcll(less) + __popcll(same & lt)] = tid;
+    if (first) {
+      const int g = __popcll(fm & less);  // distinct smaller ids
+      sm.uniq[g] = ev;
+      sm.start[g] = __popcll(less);
     }
     if (tid == 0) {
-      sm.start[nu] = start;
+      const int nu = __popcll(fm);
+      sm.start[nu] = __popcll(vm);
       sm.nu = nu;
       sm.drop = __popcll(dm);
     }
