@@ -197,6 +197,27 @@ def test_decode_edge_cases():
     assert int(ws[:4].view(torch.int32).item()) == 2
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_grouping_duplicates_and_dropped(T):
+    """The pair grouping at both set-up paths (one token: slots in slot order; more:
+    experts in id order by ballots): duplicate ids, dropped ids, ids 0 and E-1 (the id
+    bits at both ends), all slots of a token dropped."""
+    E, H, I, k = 33, 256, 128, 8
+    lay = W.draw_layer(29, E=E, H=H, I=I)
+    dl = layer_dev(lay)
+    xb = W.draw_activations(29, T, H)
+    ids = np.array([[E - 1, 0, 7, 7, -1, E, 31, 0], [-3, -3, -3, -3, -3, -3, -3, -3]], dtype=np.int32)[:T]
+    w = np.random.default_rng(29).random((T, k)).astype(np.float32)
+    ws = torch.zeros(nv.decode_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=DEV)
+    y = nv.moe_decode(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), ws=ws)
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    yn = y.cpu().numpy()
+    assert max_row_rel_l2(yn[:1], ref[:1]) < 1e-5
+    if T == 2:
+        assert np.count_nonzero(yn[1]) == 0
+    assert int(ws[:4].view(torch.int32).item()) == int(np.sum((ids < 0) | (ids >= E)))
+
+
 # ------------------------------------------------------------------ prefill
 def _prefill_small(act, seed=21, E=8, H=512, I=256, T=600, k=8, out_dtype=torch.bfloat16, routing="zipf"):
     lay = W.draw_layer(seed, E=E, H=H, I=I)
