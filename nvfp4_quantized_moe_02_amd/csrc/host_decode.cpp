@@ -251,7 +251,8 @@ inline void row_ptrs(const Weight& w, int e, int r, const uint8_t** c, const uin
 // Persistent workers, created on first use and kept for the life of the process (a
 // forked child starts a pool of its own). One job at a time; the calling thread works too.
 // A job is published as one atomic word (generation << 16 | helper count), so a worker
-// decides from a single snapshot whether it takes part. Idle workers spin for a short
+// decides from a single snapshot whether it takes part; workers take the caller's MXCSR
+// (denormal and rounding modes), so every unit is computed the same way on any thread. Idle workers spin for a short
 // while before they sleep, since decode calls come back to back and a sleeping thread
 // takes tens of microseconds to wake.
 class Pool {
@@ -269,6 +270,7 @@ class Pool {
     }
     job_.store(&f, std::memory_order_relaxed);
     n_.store(n, std::memory_order_relaxed);
+    csr_.store(_mm_getcsr(), std::memory_order_relaxed);  // the caller's denormal and rounding modes
     next_.store(0, std::memory_order_relaxed);
     busy_.store(threads - 1, std::memory_order_relaxed);
     {
@@ -305,6 +307,7 @@ class Pool {
       }
       seen = st;
       if (id >= (int)(st & 0xFFFF)) continue;  // not a helper of this job
+      _mm_setcsr(csr_.load(std::memory_order_relaxed));
       drain(*job_.load(std::memory_order_relaxed), n_.load(std::memory_order_relaxed));
       busy_.fetch_sub(1, std::memory_order_release);
     }
@@ -315,6 +318,7 @@ class Pool {
   std::atomic<uint64_t> state_{0};
   std::atomic<const std::function<void(int)>*> job_{nullptr};
   std::atomic<int> n_{0}, next_{0}, busy_{0}, sleepers_{0};
+  std::atomic<unsigned> csr_{0};
   int started_ = 0;
 };
 

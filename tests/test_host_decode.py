@@ -161,3 +161,27 @@ def test_empty_and_validation():
     with pytest.raises(nv.NVFP4Error) as e:
         nv.moe_decode_host(x, nv.Layer(nv.Q8Proj.from_numpy(q8, "cpu"), L.up, L.down), ti, tw)
     assert e.value.status == -2
+
+
+def test_worker_threads_follow_callers_denormal_mode():
+    """Workers take the calling thread's MXCSR: with denormals-are-zero set by the caller,
+    subnormal activations read as zero on every thread. Large gate/up global scales lift
+    what the subnormals would otherwise contribute into the normal range, so a worker
+    that kept the default mode would give a nonzero output."""
+    lay, xb, ids, w = case(31, 4)
+    x = bf16_cpu(xb).float() * 1e-39  # subnormal fp32 inputs
+    L = host_layer(lay)
+    L.gate.gamma.fill_(1e30)
+    L.up.gamma.fill_(1e30)
+    ti, tw = torch.from_numpy(ids), torch.from_numpy(w)
+    free, _ = nv.moe_decode_host(x, L, ti, tw, n_threads=4)
+    assert torch.count_nonzero(free) > 0  # the subnormals do reach the output normally
+    if not torch.set_flush_denormal(True):
+        pytest.skip("this CPU has no flush-to-zero control")
+    try:
+        one, _ = nv.moe_decode_host(x, L, ti, tw, n_threads=1)
+        many, _ = nv.moe_decode_host(x, L, ti, tw, n_threads=4)
+    finally:
+        torch.set_flush_denormal(False)
+    assert torch.count_nonzero(one) == 0  # every input read as zero
+    assert torch.equal(one, many)
