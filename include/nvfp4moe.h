@@ -208,7 +208,11 @@ int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32
  * expert-id order; NaN logits rank below every number) and topk_weights[t][j] = softmax of
  * those topk logits (the rule is this library's reading; the pages do not give it). The
  * outputs feed nvfp4_moe_decode / nvfp4_moe_prefill directly. ws needs
- * nvfp4_router_workspace_size() bytes (the fp32 logits). T == 0 is a no-op.
+ * nvfp4_router_workspace_size() bytes: a 256-byte header, then the fp32 logits [T][E]. The
+ * header holds a completion counter (up to 8 tokens run as one launch whose last block to
+ * finish ranks the logits): zero-fill the workspace once before first use; every call
+ * leaves the counter at zero, and calls sharing a workspace must not overlap. T == 0 is
+ * a no-op.
  * Errors: EINVAL for null or misaligned pointers (x, w_router and ws 16-byte aligned), T < 0,
  * x_dtype other than F32/BF16, topk < 1 or topk > E; EUNSUPPORTED for H not a multiple of
  * 64, E not a multiple of 32 or above 2048, topk > 64; EWORKSPACE. */

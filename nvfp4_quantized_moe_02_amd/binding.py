@@ -273,9 +273,7 @@ def router_topk(x: torch.Tensor, w_router: torch.Tensor, topk: int, ws: Optional
     E = int(w_router.shape[0])
     ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
     wts = torch.empty((T, topk), dtype=torch.float32, device=x.device)
-    need = router_workspace_size(T, E)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ws = _ws(ws, router_workspace_size(T, E), x.device)  # zero-filled when new (completion counter)
     _check("nvfp4_router_topk", lib.nvfp4_router_topk(_ptr(x), DTYPE[x.dtype], T, H, _ptr(w_router), E, topk,
                                                       _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(),
                                                       _stream(x.device)))

@@ -163,9 +163,13 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
   return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, 0, scale, as_stream(stream)));
 }
 
+// Router workspace: a 256-byte header (the completion counter of the single-launch path,
+// zero before first use and left zero by every call), then the fp32 logits [T][E].
+constexpr size_t kRouterHeader = 256;
+
 size_t nvfp4_router_workspace_size(int32_t T, int32_t E) {
   if (T < 0 || E < 1) return 0;
-  return align_up((size_t)T * E * 4);
+  return kRouterHeader + align_up((size_t)T * E * 4);
 }
 
 int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, const uint16_t* w_router, int32_t E,
@@ -182,7 +186,8 @@ int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
   if (T == 0) return NVFP4_OK;
   (void)hipGetLastError();
   return hip_status(launch_router(x, x_dtype == NVFP4_BF16 ? 1 : 0, T, H, w_router, E, topk,
-                                  reinterpret_cast<float*>(ws), topk_ids, topk_weights, as_stream(stream)));
+                                  at<float>(ws, kRouterHeader), topk_ids, topk_weights, at<unsigned>(ws, 0),
+                                  as_stream(stream)));
 }
 
 size_t nvfp4_moe_decode_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk) {

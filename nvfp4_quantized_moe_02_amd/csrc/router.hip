@@ -24,6 +24,20 @@ __device__ __forceinline__ int dpp_movi(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
+// The value of lane (lane ^ 16) / (lane ^ 32), by the row-swap moves (VALU, no LDS trip).
+// A swap of v with itself leaves in its first result the lower row (half) copied over the
+// upper one and in its second the upper copied over the lower.
+__device__ __forceinline__ int xor16i(int v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane & 16) ? (int)r[0] : (int)r[1];
+}
+__device__ __forceinline__ int xor32i(int v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane & 32) ? (int)r[0] : (int)r[1];
+}
+__device__ __forceinline__ float xor16f(float v, int lane) { return __int_as_float(xor16i(__float_as_int(v), lane)); }
+__device__ __forceinline__ float xor32f(float v, int lane) { return __int_as_float(xor32i(__float_as_int(v), lane)); }
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -132,18 +146,16 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 
 // One wave per token: k rounds of a wave-wide argmax (larger logit first, then the lower
 // expert id; NaN logits rank below every number), then the softmax over the k selected
-// logits (expf of the differences to the largest, IEEE division by their sum).
-template <int NPL>  // logits per lane (E <= 64 * NPL)
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                          int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+// logits (expf of the differences to the largest, IEEE division by their sum). `load(e)`
+// reads the token's logit of expert e.
+template <int NPL, class Load>  // logits per lane (E <= 64 * NPL)
+__device__ __forceinline__ void topk_token(int lane, int E, int k, Load load, int32_t* __restrict__ ids,
+                                           float* __restrict__ wts) {
   float v[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
-    const float f = e < E ? logits[(size_t)t * E + e] : -__builtin_inff();
+    const float f = e < E ? load(e) : -__builtin_inff();
     v[j] = f == f ? f : -__builtin_inff();  // NaN ranks lowest
   }
   uint64_t taken = 0;  // bit j: this lane's value j is selected
@@ -167,28 +179,42 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
         bi = oi;
       }
     };
-    // within each row of 16 lanes by DPP moves, then across the 4 rows
+    // within each row of 16 lanes by DPP moves, then across the 4 rows by row swaps
     take(dpp_mov<0xB1>(bv), dpp_movi<0xB1>(bi));
     take(dpp_mov<0x4E>(bv), dpp_movi<0x4E>(bi));
     take(dpp_mov<0x124>(bv), dpp_movi<0x124>(bi));
     take(dpp_mov<0x128>(bv), dpp_movi<0x128>(bi));
-    take(__shfl_xor(bv, 16, 64), __shfl_xor(bi, 16, 64));
-    take(__shfl_xor(bv, 32, 64), __shfl_xor(bi, 32, 64));
+    take(xor16f(bv, lane), xor16i(bi, lane));
+    take(xor32f(bv, lane), xor32i(bi, lane));
     if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
     if (lane == r) {
       my_id = bi;
       my_l = bv;
     }
   }
-  const float top = __shfl(my_l, 0, 64);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
   const float ez = lane < k ? expf(my_l - top) : 0.f;
-  float s = ez;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  float s = ez;  // sum over the wave: rows by DPP, then the row swaps
+  s += dpp_mov<0xB1>(s);
+  s += dpp_mov<0x4E>(s);
+  s += dpp_mov<0x124>(s);
+  s += dpp_mov<0x128>(s);
+  s += xor16f(s, lane);
+  s += xor32f(s, lane);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = ez / s;
+    ids[lane] = my_id;
+    wts[lane] = ez / s;
   }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  topk_token<NPL>(lane, E, k, [row](int e) { return row[e]; }, ids + (size_t)t * k, wts + (size_t)t * k);
 }
 
 // Many tokens: a block covers 32*RB tokens x 128 experts; wave w computes the 32 experts
@@ -289,17 +315,31 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const void* __r
 // its row share (8 bf16 per 16-byte load) before the arithmetic: products in FP32 FMAs
 // (each product exact inside the FMA), each lane's sum in input order, then a fixed
 // 16-lane reduction.
-template <int XT>  // 1: bf16 x, 0: fp32 x
-__global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict__ x, int T, int H,
+//
+// The same launch also ranks: logits are stored through to memory (agent scope), each
+// block counts itself done on a counter in the workspace once its stores have completed,
+// and the block that completes the count reads every logit back with agent-coherent loads
+// and runs the top-k (one wave per token), then sets the counter back to zero.
+// s_waitcnt immediate: no vector-memory operation of this wave outstanding.
+constexpr int kRouterVmcnt0 = (7 << 4) | (0xF << 8);
+#ifndef ROUTER_GEMV_WAVES
+#define ROUTER_GEMV_WAVES 4
+#endif
+constexpr int kRouterGemvWaves = ROUTER_GEMV_WAVES;  // waves per block: 4 expert rows each
+
+template <int XT, int NPL, int WAVES>  // XT 1: bf16 x, 0: fp32 x; NPL: logits per lane in the top-k
+__global__ __launch_bounds__(64 * WAVES) void router_gemv_kernel(const void* __restrict__ x, int T, int H,
                                                           const uint16_t* __restrict__ wr, int E,
-                                                          float* __restrict__ logits) {
+                                                          float* __restrict__ logits, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                          unsigned* __restrict__ done) {
   extern __shared__ __attribute__((aligned(16))) char xl[];
   const int tid = threadIdx.x;
   const int n16 = T * H * (XT ? 2 : 4) / 16;
-  for (int i = tid; i < n16; i += 256) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(x)[i];
+  for (int i = tid; i < n16; i += 64 * WAVES) reinterpret_cast<uint4*>(xl)[i] = reinterpret_cast<const uint4*>(x)[i];
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15;
-  const int e = blockIdx.x * 16 + wave * 4 + (lane >> 4);  // E % 16 == 0
+  const int e = (blockIdx.x * WAVES + wave) * 4 + (lane >> 4);  // E % (4 * WAVES) == 0
   const uint16_t* row = wr + (size_t)e * H;
   const int nch = H >> 3;  // 8-input chunks; this lane takes l16, l16 + 16, ...
   float acc[kDecodeMaxT];
@@ -354,23 +394,49 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   for (int t = 0; t < kDecodeMaxT; ++t) {
     if (t < T) {
       const float v = sum16(acc[t]);
-      if (l16 == 0) logits[(size_t)t * E + e] = v;
+      if (l16 == 0) __hip_atomic_store(logits + (size_t)t * E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  __builtin_amdgcn_s_waitcnt(kRouterVmcnt0);
+  __syncthreads();
+  __shared__ int last;
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == gridDim.x - 1;
+    if (last) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  for (int t = wave; t < T; t += WAVES) {
+    const float* row = logits + (size_t)t * E;
+    topk_token<NPL>(
+        lane, E, k, [row](int e) { return __hip_atomic_load(row + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+        ids + (size_t)t * k, wts + (size_t)t * k);
   }
 }
 
+template <int XT, int NPL>
+static hipError_t launch_gemv(const void* x, int T, int H, const uint16_t* wr, int E, int k, float* logits,
+                              int32_t* ids, float* wts, unsigned* done, size_t xbytes, hipStream_t st) {
+  constexpr int W = kRouterGemvWaves;
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(router_gemv_kernel<XT, NPL, W>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
+  if (ea != hipSuccess) return ea;
+  router_gemv_kernel<XT, NPL, W><<<dim3((unsigned)(E / (4 * W))), 64 * W, xbytes, st>>>(x, T, H, wr, E, logits, k,
+                                                                                          ids, wts, done);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const void* x, int x_dtype, int T, int H, const uint16_t* wr, int E, int k, float* logits,
-                         int32_t* ids, float* wts, hipStream_t st) {
+                         int32_t* ids, float* wts, unsigned* done, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const size_t xbytes = (size_t)T * H * (x_dtype == 1 ? 2 : 4);
-  if (T <= kDecodeMaxT && xbytes <= 64 * 1024) {
-    const dim3 g1((unsigned)(E / 16));
-    const void* k = x_dtype == 1 ? reinterpret_cast<const void*>(router_gemv_kernel<1>)
-                                 : reinterpret_cast<const void*>(router_gemv_kernel<0>);
-    hipError_t ea = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
-    if (ea != hipSuccess) return ea;
-    if (x_dtype == 1) router_gemv_kernel<1><<<g1, 256, xbytes, st>>>(x, T, H, wr, E, logits);
-    else router_gemv_kernel<0><<<g1, 256, xbytes, st>>>(x, T, H, wr, E, logits);
+  if (T <= kDecodeMaxT && xbytes <= 64 * 1024) {  // one launch: logits and top-k
+    if (x_dtype == 1)
+      return E <= 512 ? launch_gemv<1, 8>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
+                      : launch_gemv<1, 32>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
+    return E <= 512 ? launch_gemv<0, 8>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
+                    : launch_gemv<0, 32>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
   } else if (T <= 64) {
     const dim3 g1((unsigned)((T + 31) / 32), (unsigned)(E / 32));
     if (x_dtype == 1) router_logits_kernel<1, true><<<g1, 256, 0, st>>>(x, T, H, wr, E, logits);

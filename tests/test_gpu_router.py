@@ -18,10 +18,11 @@ nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
 
 def _run(x_dev, x_f64, wr_bits, k):
     T, E = x_dev.shape[0], wr_bits.shape[0]
-    ws = torch.empty(nv.router_workspace_size(T, E), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nv.router_workspace_size(T, E), dtype=torch.uint8, device=DEV)
     ids, wts = nv.router_topk(x_dev, torch.from_numpy(wr_bits.view(np.int16)).to(DEV), k, ws=ws)
     torch.cuda.synchronize()
-    lg = ws[:T * E * 4].view(torch.float32).view(T, E).cpu().numpy().astype(np.float64)
+    lg = ws[256:256 + T * E * 4].view(torch.float32).view(T, E).cpu().numpy().astype(np.float64)
+    assert int(ws[:4].view(torch.int32).item()) == 0  # the completion counter is left at zero
     ids, wts = ids.cpu().numpy(), wts.cpu().numpy().astype(np.float64)
     rids, rw, rlg = O.router_topk(x_f64, wr_bits, k)
     # fp32 accumulation of exact products: at most (parts * H / 16 + 8) roundings of 2^-24
@@ -109,3 +110,20 @@ def test_router_validation():
     with pytest.raises(nv.NVFP4Error) as ei:
         nv.router_topk(x, torch.zeros((64, 128), dtype=torch.int16, device=DEV), 65)  # k > E
     assert ei.value.status == -1
+
+
+def test_router_workspace_reused_across_calls():
+    """One workspace for a sequence of calls (single-launch and two-launch paths, both x
+    dtypes, growing and shrinking T): every call gives what a call on a fresh workspace
+    gives, and leaves the completion counter at zero."""
+    wr = W.draw_router(W.config_seed(3))
+    wr_dev = torch.from_numpy(wr.view(np.int16)).to(DEV)
+    ws = torch.zeros(nv.router_workspace_size(300, 512), dtype=torch.uint8, device=DEV)
+    xb = W.draw_activations(W.config_seed(3), 300)
+    for T, f32 in [(4, False), (1, False), (300, False), (8, True), (2, False), (64, True), (1, True)]:
+        x = bf16_dev(xb[:T])
+        x = x.float() if f32 else x
+        ids, wts = nv.router_topk(x, wr_dev, 8, ws=ws)
+        fids, fwts = nv.router_topk(x, wr_dev, 8)  # fresh workspace
+        assert torch.equal(ids, fids) and torch.equal(wts, fwts), (T, f32)
+        assert int(ws[:4].view(torch.int32).item()) == 0, (T, f32)
