@@ -209,7 +209,7 @@ int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32
  * those topk logits (the rule is this library's reading; the pages do not give it). The
  * outputs feed nvfp4_moe_decode / nvfp4_moe_prefill directly. ws needs
  * nvfp4_router_workspace_size() bytes: a 256-byte header, then the fp32 logits [T][E]. The
- * header holds a completion counter (up to 8 tokens run as one launch whose last block to
+ * header holds a completion counter (up to 4 tokens run as one launch whose last block to
  * finish ranks the logits): zero-fill the workspace once before first use; every call
  * leaves the counter at zero, and calls sharing a workspace must not overlap. T == 0 is
  * a no-op.

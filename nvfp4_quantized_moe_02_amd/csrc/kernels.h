@@ -68,7 +68,7 @@ hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const We
 // router.hip: logits [T][E] fp32 (workspace), then ids/weights [T][k]. x_dtype 1 = bf16,
 // 0 = fp32 (split exactly into three bf16 parts). E % 32 == 0, E <= 2048, k <= 64,
 // H % 16 == 0 (H % 64 == 0 for few tokens). done: a completion counter, zero on entry
-// and left zero (the single-launch path for up to 8 tokens counts its blocks on it).
+// and left zero (the single-launch path for up to 4 tokens counts its blocks on it).
 hipError_t launch_router(const void* x, int x_dtype, int T, int H, const uint16_t* wr, int E, int k, float* logits,
                          int32_t* ids, float* wts, unsigned* done, hipStream_t st);
 

@@ -148,9 +148,79 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 // expert id; NaN logits rank below every number), then the softmax over the k selected
 // logits (expf of the differences to the largest, IEEE division by their sum). `load(e)`
 // reads the token's logit of expert e.
+//
+// Up to 512 experts (8 per lane) each lane first sorts its 8 candidates once, as 64-bit
+// keys (the logit's order-preserving bits above, 2^32 - 1 - id below, so a larger key is a
+// larger logit or, on equal logits, the lower id), and every round is one wave-wide max of
+// the lanes' heads, after which the winning lane drops its head.
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t v) {
+  return ((uint64_t)(uint32_t)dpp_movi<CTRL>((int)(v >> 32)) << 32) | (uint32_t)dpp_movi<CTRL>((int)(uint32_t)v);
+}
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v, int lane) {
+  v = key_max(v, dpp_key<0xB1>(v));
+  v = key_max(v, dpp_key<0x4E>(v));
+  v = key_max(v, dpp_key<0x124>(v));
+  v = key_max(v, dpp_key<0x128>(v));
+  v = key_max(v, ((uint64_t)(uint32_t)xor16i((int)(v >> 32), lane) << 32) | (uint32_t)xor16i((int)(uint32_t)v, lane));
+  v = key_max(v, ((uint64_t)(uint32_t)xor32i((int)(v >> 32), lane) << 32) | (uint32_t)xor32i((int)(uint32_t)v, lane));
+  return v;
+}
+
 template <int NPL, class Load>  // logits per lane (E <= 64 * NPL)
 __device__ __forceinline__ void topk_token(int lane, int E, int k, Load load, int32_t* __restrict__ ids,
                                            float* __restrict__ wts) {
+  if constexpr (NPL == 8) {
+    uint64_t key[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + 64 * j;
+      float f = e < E ? load(e) : 0.f;
+      f = f == f ? (f == 0.f ? 0.f : f) : -__builtin_inff();  // NaN ranks lowest; -0 ties +0
+      const uint32_t u = __float_as_uint(f);
+      const uint32_t ou = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      key[j] = e < E ? ((uint64_t)ou << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;  // 0: no expert
+    }
+    auto cas = [&](int i, int j) {
+      const uint64_t a = key[i], b = key[j];
+      key[i] = a > b ? a : b;
+      key[j] = a > b ? b : a;
+    };
+    // 19-comparator sorting network for 8, descending
+    cas(0, 2); cas(1, 3); cas(4, 6); cas(5, 7);
+    cas(0, 4); cas(1, 5); cas(2, 6); cas(3, 7);
+    cas(0, 1); cas(2, 3); cas(4, 5); cas(6, 7);
+    cas(2, 4); cas(3, 5);
+    cas(1, 4); cas(3, 6);
+    cas(1, 2); cas(3, 4); cas(5, 6);
+    uint64_t mine = 0;
+    for (int r = 0; r < k; ++r) {
+      const uint64_t m = wave_max_key(key[0], lane);
+      if (lane == r) mine = m;
+      const bool won = key[0] == m;  // keys are distinct: one lane
+#pragma unroll
+      for (int j = 0; j < 7; ++j) key[j] = won ? key[j + 1] : key[j];
+      key[7] = won ? 0ull : key[7];
+    }
+    const uint32_t hi = (uint32_t)(mine >> 32);
+    const float my_l = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+    const int my_id = (int)(0xFFFFFFFFu - (uint32_t)mine);
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+    const float ez = lane < k ? expf(my_l - top) : 0.f;
+    float s = ez;  // sum over the wave: rows by DPP, then the row swaps
+    s += dpp_mov<0xB1>(s);
+    s += dpp_mov<0x4E>(s);
+    s += dpp_mov<0x124>(s);
+    s += dpp_mov<0x128>(s);
+    s += xor16f(s, lane);
+    s += xor32f(s, lane);
+    if (lane < k) {
+      ids[lane] = my_id;
+      wts[lane] = ez / s;
+    }
+    return;
+  }
   float v[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
@@ -316,10 +386,11 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const void* __r
 // (each product exact inside the FMA), each lane's sum in input order, then a fixed
 // 16-lane reduction.
 //
-// The same launch also ranks: logits are stored through to memory (agent scope), each
-// block counts itself done on a counter in the workspace once its stores have completed,
-// and the block that completes the count reads every logit back with agent-coherent loads
-// and runs the top-k (one wave per token), then sets the counter back to zero.
+// Up to one token per wave of a block (RANK), the same launch also ranks: logits are
+// stored through to memory (agent scope), each block counts itself done on a counter in
+// the workspace once its stores have completed, and the block that completes the count
+// reads every logit back with agent-coherent loads and runs the top-k (one wave per
+// token), then sets the counter back to zero. More tokens rank in a second launch.
 // s_waitcnt immediate: no vector-memory operation of this wave outstanding.
 constexpr int kRouterVmcnt0 = (7 << 4) | (0xF << 8);
 #ifndef ROUTER_GEMV_WAVES
@@ -327,7 +398,8 @@ constexpr int kRouterVmcnt0 = (7 << 4) | (0xF << 8);
 #endif
 constexpr int kRouterGemvWaves = ROUTER_GEMV_WAVES;  // waves per block: 4 expert rows each
 
-template <int XT, int NPL, int WAVES>  // XT 1: bf16 x, 0: fp32 x; NPL: logits per lane in the top-k
+template <int XT, int NPL, int WAVES, bool RANK>  // XT 1: bf16 x, 0: fp32 x; NPL: logits per lane in the
+                                                  // top-k; RANK: this launch also ranks (T <= WAVES)
 __global__ __launch_bounds__(64 * WAVES) void router_gemv_kernel(const void* __restrict__ x, int T, int H,
                                                           const uint16_t* __restrict__ wr, int E,
                                                           float* __restrict__ logits, int k,
@@ -397,6 +469,7 @@ __global__ __launch_bounds__(64 * WAVES) void router_gemv_kernel(const void* __r
       if (l16 == 0) __hip_atomic_store(logits + (size_t)t * E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if constexpr (!RANK) return;
   __builtin_amdgcn_s_waitcnt(kRouterVmcnt0);
   __syncthreads();
   __shared__ int last;
@@ -415,15 +488,15 @@ __global__ __launch_bounds__(64 * WAVES) void router_gemv_kernel(const void* __r
   }
 }
 
-template <int XT, int NPL>
+template <int XT, int NPL, bool RANK>
 static hipError_t launch_gemv(const void* x, int T, int H, const uint16_t* wr, int E, int k, float* logits,
                               int32_t* ids, float* wts, unsigned* done, size_t xbytes, hipStream_t st) {
   constexpr int W = kRouterGemvWaves;
-  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(router_gemv_kernel<XT, NPL, W>),
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(router_gemv_kernel<XT, NPL, W, RANK>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
   if (ea != hipSuccess) return ea;
-  router_gemv_kernel<XT, NPL, W><<<dim3((unsigned)(E / (4 * W))), 64 * W, xbytes, st>>>(x, T, H, wr, E, logits, k,
-                                                                                          ids, wts, done);
+  router_gemv_kernel<XT, NPL, W, RANK><<<dim3((unsigned)(E / (4 * W))), 64 * W, xbytes, st>>>(
+      x, T, H, wr, E, logits, k, ids, wts, done);
   return hipGetLastError();
 }
 
@@ -431,12 +504,16 @@ hipError_t launch_router(const void* x, int x_dtype, int T, int H, const uint16_
                          int32_t* ids, float* wts, unsigned* done, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const size_t xbytes = (size_t)T * H * (x_dtype == 1 ? 2 : 4);
-  if (T <= kDecodeMaxT && xbytes <= 64 * 1024) {  // one launch: logits and top-k
+  if (T <= kRouterGemvWaves && xbytes <= 64 * 1024) {  // one launch: logits, then one wave per token ranks
     if (x_dtype == 1)
-      return E <= 512 ? launch_gemv<1, 8>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
-                      : launch_gemv<1, 32>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
-    return E <= 512 ? launch_gemv<0, 8>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
-                    : launch_gemv<0, 32>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
+      return E <= 512 ? launch_gemv<1, 8, true>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
+                      : launch_gemv<1, 32, true>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
+    return E <= 512 ? launch_gemv<0, 8, true>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
+                    : launch_gemv<0, 32, true>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
+  } else if (T <= kDecodeMaxT && xbytes <= 64 * 1024) {
+    hipError_t eg = x_dtype == 1 ? launch_gemv<1, 8, false>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st)
+                                 : launch_gemv<0, 8, false>(x, T, H, wr, E, k, logits, ids, wts, done, xbytes, st);
+    if (eg != hipSuccess) return eg;
   } else if (T <= 64) {
     const dim3 g1((unsigned)((T + 31) / 32), (unsigned)(E / 32));
     if (x_dtype == 1) router_logits_kernel<1, true><<<g1, 256, 0, st>>>(x, T, H, wr, E, logits);
