@@ -69,7 +69,7 @@ typedef enum {
   NVFP4_EUNSUPPORTED = -2, /* a valid request this build does not implement */
   NVFP4_EWORKSPACE = -3,   /* ws_bytes smaller than the matching *_workspace_size() */
   NVFP4_EHIP = -4,         /* a HIP runtime error while enqueueing */
-  NVFP4_ENOMEM = -5        /* a host allocation failed (host entry points only) */
+  NVFP4_ENOMEM = -5        /* a host allocation or worker thread could not be created (host entry points) */
 } nvfp4_status;
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;

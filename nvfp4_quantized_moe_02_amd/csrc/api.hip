@@ -107,7 +107,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_EUNSUPPORTED: return "unsupported configuration";
     case NVFP4_EWORKSPACE: return "workspace too small";
     case NVFP4_EHIP: return "HIP runtime error";
-    case NVFP4_ENOMEM: return "host memory allocation failed";
+    case NVFP4_ENOMEM: return "host memory or thread allocation failed";
     default: return "unknown status";
   }
 }
@@ -360,7 +360,7 @@ int nvfp4_moe_decode_host(const void* x, int32_t x_dtype, int32_t T, int32_t H, 
     try {
       d = host::moe_decode(x, x_dtype, T, H, I, host_args(gate), host_args(up), host_args(down), E, topk_ids,
                            topk_weights, topk, out, n_threads, isa);
-    } catch (const std::bad_alloc&) {
+    } catch (...) {  // std::bad_alloc, or std::system_error from creating a worker thread
       return NVFP4_ENOMEM;
     }
   }

@@ -264,9 +264,9 @@ class Pool {
       for (int i = 0; i < n; ++i) f(i);
       return;
     }
-    while (started_ < threads - 1) {
-      const int id = started_++;
-      std::thread([this, id] { loop(id); }).detach();
+    while (started_ < threads - 1) {  // counted only once running (creation may throw)
+      std::thread([this, id = started_] { loop(id); }).detach();
+      ++started_;
     }
     job_.store(&f, std::memory_order_relaxed);
     n_.store(n, std::memory_order_relaxed);
