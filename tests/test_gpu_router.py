@@ -127,3 +127,14 @@ def test_router_workspace_reused_across_calls():
         fids, fwts = nv.router_topk(x, wr_dev, 8)  # fresh workspace
         assert torch.equal(ids, fids) and torch.equal(wts, fwts), (T, f32)
         assert int(ws[:4].view(torch.int32).item()) == 0, (T, f32)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1024, 8), (3, 1024, 16), (8, 1024, 8), (40, 1024, 8), (2, 2048, 64),
+                                   (2, 64, 64), (4, 96, 33)])
+def test_router_expert_counts_and_k(T, E, k):
+    """More than 512 experts (32 candidates per lane, the per-round scan), k up to 64 and
+    k = E on the one-launch path (up to 4 tokens), the two-launch path and the tiles."""
+    H = 256
+    wr = W.draw_router(11, E=E, H=H)
+    xb = W.draw_activations(11, T, H)
+    _run(bf16_dev(xb), O.bf16_to_f64(xb), wr, k)
