@@ -246,6 +246,22 @@ def bench_host(reps=24):
         u = sum(c[3] for c in calls[:n]) / n
         out[f"t{T}" + ("_1thread" if nt == 1 else "")] = {"ms": round(dt * 1e3, 3), "unique_experts": round(u, 2),
                                                            "GB/s": round(u * per_expert / dt / 1e9, 1)}
+    # then the host's plain streaming read rate on as many threads (torch's multithreaded sum
+    # of 2 GiB of float32; measured last, as torch's idle workers spin for a while): the
+    # ceiling the projection's byte rate is compared with
+    buf = torch.ones(1 << 29, dtype=torch.float32)
+    nt0 = torch.get_num_threads()
+    torch.set_num_threads(threads)
+    buf.sum()
+    t = time.perf_counter()
+    for _ in range(3):
+        buf.sum()
+    read_gbs = buf.numel() * 4 * 3 / (time.perf_counter() - t) / 1e9
+    torch.set_num_threads(nt0)
+    del buf
+    out["read_GB/s"] = round(read_gbs, 1)
+    for key in ("t1", "t4", "t1_1thread"):
+        out[key]["frac_of_read"] = round(out[key]["GB/s"] / read_gbs, 3)
     return out
 
 
