@@ -17,7 +17,8 @@
 //            traffic overlaps phase 1 and the wait.
 //
 // The same device code also runs as two ordinary launches (phase 1, then phase 2) for
-// the staged entry point and for shapes whose grid cannot be co-resident; both forms
+// the staged entry point and for shapes whose grid cannot be co-resident or whose h does
+// not fit in LDS (the launch boundary then makes h visible); both forms
 // give bit-identical results. Both derive the unique-expert list from topk_ids
 // themselves (no host synchronization).
 //
