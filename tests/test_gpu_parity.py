@@ -197,24 +197,26 @@ def test_decode_edge_cases():
     assert int(ws[:4].view(torch.int32).item()) == 2
 
 
-@pytest.mark.parametrize("T", [1, 2])
-def test_decode_grouping_duplicates_and_dropped(T):
+@pytest.mark.parametrize("T,E", [(1, 33), (2, 33), (3, 8192), (2, 1)])
+def test_decode_grouping_duplicates_and_dropped(T, E):
     """The pair grouping at both set-up paths (one token: slots in slot order; more:
-    experts in id order by ballots): duplicate ids, dropped ids, ids 0 and E-1 (the id
-    bits at both ends), all slots of a token dropped."""
-    E, H, I, k = 33, 256, 128, 8
+    experts in id order by ballots, one per id bit: 13 at 8192 experts): duplicate ids,
+    dropped ids, ids 0 and E-1 (the id bits at both ends), all slots of a token dropped."""
+    H, I, k = (256, 128, 8) if E < 1000 else (64, 32, 8)
     lay = W.draw_layer(29, E=E, H=H, I=I)
     dl = layer_dev(lay)
     xb = W.draw_activations(29, T, H)
-    ids = np.array([[E - 1, 0, 7, 7, -1, E, 31, 0], [-3, -3, -3, -3, -3, -3, -3, -3]], dtype=np.int32)[:T]
+    ids = np.array([[E - 1, 0, 7 % E, 7 % E, -1, E, 31 % E, 0], [-3, -3, -3, -3, -3, -3, -3, -3],
+                    [E // 2, E - 1, 4095 % E, 4096 % E, E - 2, 1 % E, 0, E - 1]], dtype=np.int32)[:T]
     w = np.random.default_rng(29).random((T, k)).astype(np.float32)
     ws = torch.zeros(nv.decode_workspace_size(T, H, I, E, k), dtype=torch.uint8, device=DEV)
     y = nv.moe_decode(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), ws=ws)
     ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
     yn = y.cpu().numpy()
-    assert max_row_rel_l2(yn[:1], ref[:1]) < 1e-5
-    if T == 2:
-        assert np.count_nonzero(yn[1]) == 0
+    live = [t for t in range(T) if np.any((ids[t] >= 0) & (ids[t] < E))]
+    assert max_row_rel_l2(yn[live], ref[live]) < 1e-5
+    for t in set(range(T)) - set(live):
+        assert np.count_nonzero(yn[t]) == 0
     assert int(ws[:4].view(torch.int32).item()) == int(np.sum((ids < 0) | (ids >= E)))
 
 
