@@ -393,10 +393,9 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const void* __r
 // token), then sets the counter back to zero. More tokens rank in a second launch.
 // s_waitcnt immediate: no vector-memory operation of this wave outstanding.
 constexpr int kRouterVmcnt0 = (7 << 4) | (0xF << 8);
-#ifndef ROUTER_GEMV_WAVES
-#define ROUTER_GEMV_WAVES 4
-#endif
-constexpr int kRouterGemvWaves = ROUTER_GEMV_WAVES;  // waves per block: 4 expert rows each
+// Waves per GEMV block (4 expert rows each). 1 and 2 measured slower: the ranking block then
+// ranks several tokens per wave one after another.
+constexpr int kRouterGemvWaves = 4;
 
 template <int XT, int NPL, int WAVES, bool RANK>  // XT 1: bf16 x, 0: fp32 x; NPL: logits per lane in the
                                                   // top-k; RANK: this launch also ranks (T <= WAVES)
