@@ -222,7 +222,7 @@ int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
                       void* stream);
 
 /* Host-CPU share of the experts ("Strata NVFP4" README: AVX-512 NVFP4 kernels compute the
- * CPU's share of the experts from host DRAM, with an AVX2 path for CPUs without AVX-512).
+ * CPU's share of the experts from host DRAM; a CPU without AVX-512 takes an AVX2 path).
  * The decode projection above on HOST memory, run on this process's CPU threads: every
  * pointer (x, the weight planes and scales, topk_ids, topk_weights, out) is a host pointer
  * owned by the caller, with the device layout and no alignment requirement. Each weight is
@@ -231,7 +231,9 @@ int nvfp4_router_topk(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
  * on n_threads. x [T][H] F32 or BF16, any T >= 0; out float [T][H]. To split a layer's
  * experts between the GPU and the CPU, give each call the same topk_ids with the other
  * side's experts replaced by -1 (dropped) and add the two outputs.
- * n_threads: 0 = one per CPU this process may run on. isa: NVFP4_ISA_AUTO (the widest the
+ * n_threads: 0 = one per CPU this process may run on (more than that is clamped to it).
+ * Worker threads are started on first use and kept; they take the calling thread's
+ * floating-point modes (MXCSR) for each call. isa: NVFP4_ISA_AUTO (the widest the
  * CPU has) or a narrower one to force (results differ only in FP32 summation order).
  * dropped (may be NULL) receives the number of pairs whose id is outside [0, E).
  * The call returns when out is written; it makes no HIP call. Concurrent calls run one
