@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     DTYPE,
     NVFP4Error,
     PreparedCall,
+    PreparedHostCall,
     Proj,
     Q8Proj,
     FORMAT,

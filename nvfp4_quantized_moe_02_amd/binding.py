@@ -379,3 +379,22 @@ class PreparedCall:
 
     def stage(self, i: int) -> None:
         _check(self.kind + "_stage", self.staged(i, *self.args, _stream(self.device)))
+
+
+class PreparedHostCall:
+    """A host-CPU decode call (nvfp4_moe_decode_host) with its arguments marshalled once,
+    for call loops: run() runs the call on the CPU threads and returns the dropped count."""
+
+    def __init__(self, x, layer: Layer, ids, w, out, n_threads: int = 0, isa: str = "auto"):
+        self.lib = load_library()
+        self.keep = (x, layer, ids, w, out)
+        self._w = (layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct())
+        self._dropped = ctypes.c_int64(0)
+        g, u, d = (ctypes.byref(v) for v in self._w)
+        T, H = int(x.shape[0]), int(x.shape[1])
+        self.args = [_ptr(x), DTYPE[x.dtype], T, H, g, u, d, layer.E, _ptr(ids), _ptr(w), int(ids.shape[1]),
+                     _ptr(out), n_threads, ISA[isa], ctypes.byref(self._dropped)]
+
+    def run(self) -> int:
+        _check("nvfp4_moe_decode_host", self.lib.nvfp4_moe_decode_host(*self.args))
+        return int(self._dropped.value)

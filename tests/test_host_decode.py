@@ -185,3 +185,17 @@ def test_worker_threads_follow_callers_denormal_mode():
         torch.set_flush_denormal(False)
     assert torch.count_nonzero(one) == 0  # every input read as zero
     assert torch.equal(one, many)
+
+
+def test_prepared_host_call_matches():
+    lay, xb, ids, w = case(37, 5)
+    L = host_layer(lay)
+    x, ti, tw = bf16_cpu(xb), torch.from_numpy(ids), torch.from_numpy(w)
+    ref, d0 = nv.moe_decode_host(x, L, ti, tw)
+    out = torch.empty_like(ref)
+    call = nv.PreparedHostCall(x, L, ti, tw, out)
+    assert call.run() == d0
+    assert torch.equal(out, ref)
+    out.fill_(7.0)
+    call.run()  # a second run overwrites the output
+    assert torch.equal(out, ref)
