@@ -53,7 +53,8 @@ Readings where the pages are silent (each listed in the design notes):
   * W4A8: per row s = fp32(absmax / 127) by an fp32 division, q = clamp(
     rint_even(fp32(x / s)), -127, 127), s = q = 0 for an all-zero row; the
     down projection's input h is quantized per (token, slot) row the same
-    way, from h rounded to fp32.
+    way, from h rounded to fp32; a row holding a NaN (an infinity) gets a NaN
+    (+inf) scale and all-zero codes, so its non-finite value propagates.
 """
 from __future__ import annotations
 
@@ -296,14 +297,26 @@ def router_topk(x: np.ndarray, w_router_bf16_bits: np.ndarray, k: int):
 def quant_rows_i8(x32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Per-row symmetric int8: s = fp32(absmax / 127) (float32 division),
     q = clamp(round_half_even(fp32(x / s)), -127, 127); an all-zero row gives
-    s = 0, q = 0. [S-NVFP4] W4A8 prompt path with 8-bit activations."""
+    s = 0, q = 0. [S-NVFP4] W4A8 prompt path with 8-bit activations.
+
+    Non-finite rows (a reading; the pages are silent): if a row holds a NaN, its
+    absmax and so its scale are NaN; else if it holds an infinity, its scale is +inf.
+    Either way every code of the row is 0, so the dequantized row q * s is NaN
+    everywhere (0 * NaN, 0 * inf) and the non-finite value propagates to every output
+    that row touches, as a NaN or infinite activation does in float64."""
     x32 = np.asarray(x32, dtype=np.float32)
-    absmax = np.max(np.abs(x32), axis=-1)
-    s = (absmax / np.float32(127.0)).astype(np.float32)
-    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-    r = np.rint((x32 / safe[..., None]).astype(np.float32))
+    a = np.abs(x32)
+    has_nan = np.isnan(a).any(axis=-1)
+    absmax = np.where(has_nan, np.float32(np.nan), np.max(np.where(np.isnan(a), 0, a), axis=-1))
+    absmax = absmax.astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        s = (absmax / np.float32(127.0)).astype(np.float32)
+    finite = np.isfinite(s) & (s > 0)
+    safe = np.where(finite, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = np.rint((np.where(finite[..., None], x32, 0) / safe[..., None]).astype(np.float32))
     q = np.clip(r, -127, 127)
-    q = np.where(s[..., None] > 0, q, 0).astype(np.int8)
+    q = np.where(finite[..., None], q, 0).astype(np.int8)
     return q, s
 
 
@@ -355,6 +368,30 @@ def w4a8_pair_hidden(x_bf16_bits: np.ndarray, layer, ids, rows=None):
         h = w4a8_hidden(xh[rows[pairs // k]], Wg, gg, Wu, gu)
         _, s = quant_rows_i8(h)
         out.append((e, pairs, h, s))
+    return out
+
+
+def w4a8_down_from_codes(qh: np.ndarray, sh: np.ndarray, pairs: np.ndarray, layer, ids: np.ndarray,
+                         w: np.ndarray) -> np.ndarray:
+    """The W4A8 down projection and combine on given int8 hidden rows: for each listed
+    pair p = t*k + j (row i of qh, sh), out[t] += w[t][j] * gamma_d * (qh[i] * sh[i]) .
+    Wd_e^T with e = ids[t][j]. This is the last step of moe_w4a8 with the hidden codes
+    supplied by the caller (the configuration text's "the oracle uses the same int8
+    activations" read literally for the requantized h). Returns float64 [T][H]."""
+    T, k = ids.shape
+    pairs = np.asarray(pairs, dtype=np.int64)
+    hh = np.asarray(qh, dtype=np.int8).astype(np.float64) * np.asarray(sh, dtype=np.float32).astype(np.float64)[:, None]
+    out = np.zeros((T, layer.H), dtype=np.float64)
+    ex = ids.reshape(-1)[pairs]
+    for e in np.unique(ex):
+        if e < 0 or e >= layer.E:
+            continue
+        sel = np.nonzero(ex == e)[0]
+        _, _, _, _, Wd, gd = _expert(layer, int(e))
+        Y = (hh[sel] @ Wd.T) * gd
+        for i, r in enumerate(sel):
+            p = int(pairs[r])
+            out[p // k] += float(w[p // k, p % k]) * Y[i]
     return out
 
 

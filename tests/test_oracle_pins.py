@@ -294,7 +294,8 @@ def test_quant_i8_fixture():
         xs, s, q = [f.strip() for f in ln.split("|")]
         x = np.array([[float(v) for v in xs.split(",")]], dtype=np.float32)
         qq, ss = O.quant_rows_i8(x)
-        assert ss[0] == np.float32(float(s)), (xs, ss[0])
+        want = np.float32(float(s))
+        assert ss[0] == want or (np.isnan(want) and np.isnan(ss[0])), (xs, ss[0])
         assert list(qq[0]) == [int(v) for v in q.split(",")], (xs, qq[0])
 
 
@@ -340,6 +341,93 @@ def test_w4a8_exact_int8_inputs():
     x32 = (q * 0.0625).astype(np.float32)
     qq, s = O.quant_rows_i8(x32)
     assert np.all(s == np.float32(0.0625)) and np.array_equal(qq.astype(int), q)
+
+
+def test_w4a8_nonfinite_rows_propagate():
+    """A NaN or infinite activation makes its whole token row of the W4A8 output NaN
+    (the quantizer's reading for non-finite rows); every other row stays finite."""
+    lay = _small_layer(E=2)
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((4, lay.H)).astype(np.float32)
+    x[1, 5] = np.nan
+    x[2, 0] = np.inf
+    xb = W.f32_to_bf16_bits(x)
+    ids = np.array([[0, 1], [1, 0], [0, 1], [1, 0]], np.int32)
+    w = np.full((4, 2), 0.5, np.float32)
+    with np.errstate(invalid="ignore"):
+        y = O.moe_w4a8(xb, lay, ids, w)
+    assert np.isnan(y[1]).all() and np.isnan(y[2]).all()
+    assert np.isfinite(y[0]).all() and np.isfinite(y[3]).all()
+
+
+def test_w4a8_down_from_codes_reproduces_moe_w4a8():
+    """The down step on supplied int8 hidden codes, fed the oracle's own codes (from
+    w4a8_pair_hidden, quantized), reproduces the pinned W4A8 composition; pinned the
+    other way too: one flipped code moves exactly one output row, by w * s * gamma_d
+    times one down column."""
+    lay = _small_layer(seed=5, E=4)
+    rng = np.random.default_rng(29)
+    T, k = 6, 2
+    xb = W.f32_to_bf16_bits(rng.standard_normal((T, lay.H)).astype(np.float32))
+    ids = np.array([[0, 3], [3, 1], [2, 0], [1, 1], [0, -1], [3, 2]], np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    ref = O.moe_w4a8(xb, lay, ids, w)
+    pairs, qs, ss = [], [], []
+    for e, pe, h, s in O.w4a8_pair_hidden(xb, lay, ids):
+        q, s2 = O.quant_rows_i8(h)
+        assert np.array_equal(s2.view(np.uint32), s.view(np.uint32))
+        pairs.append(pe)
+        qs.append(q)
+        ss.append(s2)
+    pairs, qs, ss = np.concatenate(pairs), np.concatenate(qs), np.concatenate(ss)
+    assert sorted(pairs.tolist()) == [p for p in range(T * k) if 0 <= ids.reshape(-1)[p] < lay.E]
+    got = O.w4a8_down_from_codes(qs, ss, pairs, lay, ids, w)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    i, j = 3, 7
+    qs2 = qs.copy()
+    qs2[i, j] = qs2[i, j] + (1 if qs2[i, j] < 127 else -1)
+    moved = O.w4a8_down_from_codes(qs2, ss, pairs, lay, ids, w) - got
+    p = int(pairs[i])
+    e = int(ids.reshape(-1)[p])
+    Wd = O.dequant(lay.down.codes[e], lay.down.scales[e])
+    expect = float(w.reshape(-1)[p]) * float(ss[i]) * float(lay.down.gamma[e]) * (qs2[i, j] - qs[i, j]) * Wd[:, j]
+    assert np.allclose(moved[p // k], expect, rtol=1e-12, atol=1e-15)
+    assert np.count_nonzero(np.delete(moved, p // k, axis=0)) == 0
+
+
+# ------------------------------------------------------------------ comparison measure
+def _rows(field):
+    return np.array([[float(v) for v in r.split(",")] for r in field.split(";")])
+
+
+def test_rel_l2_rows_fixture():
+    for ln in read_golden("rel_l2_cases.txt"):
+        y, ref, want = [f.strip() for f in ln.split("|")]
+        got = O.rel_l2_rows(_rows(y), _rows(ref))
+        assert np.allclose(got, [float(v) for v in want.split(",")], rtol=1e-15, atol=0), (ln, got)
+
+
+# ------------------------------------------------------------------ dequant roundings
+def test_dequant_double_rounding_fixture():
+    """bf16 / fp16 dequantization with a global scale rounds twice (exact -> fp32 ->
+    narrow); the hand-derived ties make a single rounding give other bits."""
+    for ln in read_golden("dequant_double_rounding.txt"):
+        dt, code, sb, gbits, want, single = [f.strip() for f in ln.split("|")]
+        codes = np.full((1, 16), int(code) * 0x11, np.uint8)  # every nibble = code
+        scales = np.full((1, 2), int(sb, 16), np.uint8)
+        gamma = np.array([int(gbits, 16)], np.uint32).view(np.float32)[0]
+        got = (O.dequant_bf16(codes, scales, gamma) if dt == "bf16"
+               else O.dequant_f16(codes, scales, gamma).view(np.uint16))
+        assert np.all(got == int(want, 16)), (ln, hex(int(got[0, 0])))
+        assert int(want, 16) != int(single, 16)
+        # the single rounding of the exact float64 product, done by hand (ties are
+        # impossible here): it lands on the other neighbour
+        exact = float(O.dequant(codes, scales, gamma)[0, 0])
+        lo = float(np.array([int(want, 16) << (16 if dt == "bf16" else 0)], np.uint32).view(np.float32)[0]) \
+            if dt == "bf16" else float(np.array([int(want, 16)], np.uint16).view(np.float16)[0])
+        hi = float(np.array([int(single, 16) << 16], np.uint32).view(np.float32)[0]) if dt == "bf16" \
+            else float(np.array([int(single, 16)], np.uint16).view(np.float16)[0])
+        assert lo < exact < hi and exact - lo > hi - exact
 
 
 # ------------------------------------------------------------------ slicing (TF-906)
@@ -427,6 +515,32 @@ def test_negative_controls_are_caught(monkeypatch):
     s = np.float32(12.7) / np.float32(127)
     q64 = np.rint(x.astype(np.float64) / float(s))
     assert q64[0, 1] == -63 and O.quant_rows_i8(x)[0][0, 1] == -64
+
+    # 7) the comparison measure normalized by ||y||, or summed over the wrong axis,
+    #    fails its hand fixture
+    def rel_by_y(y, ref):
+        y, ref = np.asarray(y, float), np.asarray(ref, float)
+        return np.sqrt(((y - ref) ** 2).sum(-1)) / np.sqrt((y ** 2).sum(-1))
+
+    def rel_cols(y, ref):
+        y, ref = np.asarray(y, float), np.asarray(ref, float)
+        return np.sqrt(((y - ref) ** 2).sum(0)) / np.sqrt((ref ** 2).sum(0))
+    for bad in (rel_by_y, rel_cols):
+        monkeypatch.setattr(O, "rel_l2_rows", bad)
+        with pytest.raises(AssertionError):
+            test_rel_l2_rows_fixture()
+        monkeypatch.undo()
+
+    # 8) a single rounding of the exact product to bf16 fails the double-rounding fixture
+    def dequant_bf16_single(codes, scales, gamma=None):
+        v = O.dequant(codes, scales, gamma)
+        m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+        r = np.ldexp(np.rint(m * 256.0), e - 8)  # 8 significant bits, ties to even
+        return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    monkeypatch.setattr(O, "dequant_bf16", dequant_bf16_single)
+    with pytest.raises(AssertionError):
+        test_dequant_double_rounding_fixture()
+    monkeypatch.undo()
 
 
 # ------------------------------------------------------------------ Q8_0 down projection
