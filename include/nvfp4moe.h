@@ -76,11 +76,13 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
 
 /* Activation handling of the prefill path.
  *   NVFP4_ACT_BF16      bf16 activations; both expert GEMMs run on fp16 matrix cores
- *                       (x is converted to fp16, h is kept in fp16).
+ *                       (x is staged in fp16 with a power-of-two exponent per row, h is
+ *                       kept in fp16 with one per block; see nvfp4_moe_prefill).
  *   NVFP4_ACT_W4A8      x and h quantized per row to int8 (scale absmax/127); the GEMMs
  *                       run on int8 matrix cores with an FP32 rescale per 16-input group.
  *   NVFP4_ACT_W4A8_F16  the same int8 activations and the same result, computed on fp16
- *                       matrix cores (int8 values are exact in fp16). */
+ *                       matrix cores (int8 values are exact in fp16; x and h are stored
+ *                       as 1-byte codes and widened while staged). */
 typedef enum { NVFP4_ACT_BF16 = 0, NVFP4_ACT_W4A8 = 1, NVFP4_ACT_W4A8_F16 = 2 } nvfp4_act;
 
 /* Weight format of a projection: NVFP4 (every projection) or Q8_0 (down only). */
@@ -131,7 +133,9 @@ int nvfp4_moe_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
 
 /* Per-row int8 quantization (the W4A8 activation rule): s[r] = fp32(absmax_r / 127) by
  * an fp32 division, q[r][c] = clamp(round_half_even(fp32(x[r][c] / s[r])), -127, 127);
- * an all-zero row gives s = 0 and q = 0. x [rows][cols] in x_dtype (F32 or BF16).
+ * an all-zero row gives s = 0 and q = 0. A row holding a NaN gets s = NaN, else a row
+ * holding an infinity s = +inf, and either gets q = 0 (so q * s is NaN and the non-finite
+ * value propagates). x [rows][cols] in x_dtype (F32 or BF16).
  * ("Strata NVFP4" README: the W4A8 prompt path keeps 8-bit activations.)
  * Errors: EINVAL for null pointers, rows < 0, cols < 1. */
 int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, int8_t* q,
@@ -147,7 +151,13 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
  * flags that every successful call leaves ready for the next; zero it again if H changes
  * or after an error). Bytes
  * 4..7 of ws hold an error word: bit 0 is set if a call's grid barrier timed out (the
- * output of that call is then invalid). The result does not depend on scheduling: every
+ * output of that call is then invalid; the bit stays set until the caller clears it, and
+ * the barrier state stays consistent, so the next call may proceed once it is cleared).
+ * A timeout can only happen if other work keeps some of the grid's blocks from starting
+ * while the rest wait; the caller must check the word after calls whose result it uses.
+ * Bytes 8..11 (int32), when positive, replace the barrier's spin limit (default 2^22
+ * polls); when negative, waiting blocks do not poll at all and give up at once (for
+ * testing the error path). The result does not depend on scheduling: every
  * output element is summed in a fixed order. Calls sharing one workspace must not
  * overlap. The whole call is one persistent launch when its grid (H/8 blocks) fits on the
  * device at once, else two launches with identical results.
@@ -168,18 +178,61 @@ int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const
  * chunks up to 32K tokens, where every chunk streams every layer's experts once.)
  * Each pair's down output is kept in fp32 and the slots of a token are summed in slot
  * order, so the result is deterministic. T == 0 is a no-op and may pass null tensors.
+ * Range (act BF16): the fp16 matrix-core operands carry a power-of-two exponent per row:
+ * each token row of x is scaled so that its largest magnitude lies in [2^14, 2^15) before
+ * it is narrowed to fp16, and h is stored in fp16 the same way per (routed pair, block of
+ * 256 intermediate indices), brought to the pair's common exponent when the down GEMM
+ * stages it; every exponent is undone exactly (ldexp) at the FP32 accumulator. So any
+ * finite bf16 activations are accepted, none overflows fp16, and an operand loses bits
+ * only where it is below 2^-31 of its row's (block's) largest magnitude ("Strata NVFP4"
+ * README, "How it differs from upstream Strata": the scale fold that left hidden
+ * activations in FP16 subnormals). NaN and infinite activations or scale bytes give NaN
+ * or infinite outputs where the float64 definition does.
  * The down projection may be Q8_0: its weights enter the fp16 matrix cores as
  * fp16(d * q), one rounding per weight (relative error at most 2^-11), the only
  * operand of the path that is not exact.
  * Errors: EINVAL (null pointers, shapes that disagree, unknown act or format,
- * out_dtype F16); EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128,
- * E > 8192, x_dtype other than BF16, a Q8_0 gate or up projection; EWORKSPACE. */
+ * out_dtype F16); EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128 or
+ * above 8192, E > 8192, x_dtype other than BF16, a Q8_0 gate or up projection, act W4A8
+ * (the int8 matrix-core variant is not in this build); EWORKSPACE. */
 size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                         int32_t act);
 int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
                       const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
                       const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act,
                       void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Where a prefill call keeps its intermediate results in its workspace, for callers
+ * that inspect them (tests, debugging) after running the stages: *offset receives the
+ * region's byte offset from the start of ws and *bytes its size (0 when the region does
+ * not exist for `act`). The contents are valid after the stage that writes them.
+ *   EXPERT_OFFSETS  int32 [E+1]            stage 0 (the routing of nvfp4_moe_route)
+ *   SORTED_PAIRS    int32 [T*topk]         stage 0
+ *   PAIR_POSITION   int32 [T*topk]         stage 0: sorted position of pair p, -1 if dropped
+ *   X_STAGED        BF16: fp16 [T][H] (x * 2^xexp[t]); W4A8*: int8 codes [T][H]  stage 0
+ *   X_ROWSCALE      BF16: int32 xexp [T];  W4A8*: fp32 row scales [T]           stage 0
+ *   H               BF16: fp16 [P][I] in sorted order, h * 2^hexp[pos][I-block]; W4A8*:
+ *                   fp32 [P][I]                                                   stage 1
+ *   H_EXP           BF16: int32 [P][I/256] (I/128 when I % 256 != 0); W4A8*: none stage 1
+ *   H_Q             W4A8*: int8 codes of h [P][I] (the per-row rule of
+ *                   nvfp4_quant_rows_i8 applied to the fp32 H); BF16: none         stage 1
+ *   H_SCALE         W4A8*: fp32 [P]; BF16: none                                    stage 1
+ *   Y               fp32 [P][H], each pair's down row times gamma_down and its weight stage 2
+ * Errors: EINVAL for null outputs, bad sizes, unknown act or region. */
+typedef enum {
+  NVFP4_WS_EXPERT_OFFSETS = 0,
+  NVFP4_WS_SORTED_PAIRS = 1,
+  NVFP4_WS_PAIR_POSITION = 2,
+  NVFP4_WS_X_STAGED = 3,
+  NVFP4_WS_X_ROWSCALE = 4,
+  NVFP4_WS_H = 5,
+  NVFP4_WS_H_EXP = 6,
+  NVFP4_WS_H_Q = 7,
+  NVFP4_WS_H_SCALE = 8,
+  NVFP4_WS_Y = 9
+} nvfp4_ws_region;
+int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act,
+                                       int32_t region, size_t* offset, size_t* bytes);
 
 /* One stage of the same sequence, for callers that interleave or time the stages.
  * Arguments, validation and workspace are those of the full call; running the stages

@@ -31,4 +31,9 @@ from .binding import (  # noqa: F401
     decode_workspace_size,
     prefill_workspace_size,
     route_workspace_size,
+    prefill_workspace_region,
+    check_decode_workspace,
+    DECODE_ERROR_WORD,
+    DECODE_SPIN_WORD,
+    WS_REGION,
 )

@@ -80,6 +80,7 @@ _SIGS = {
                                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4_moe_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 6),
+    "nvfp4_moe_prefill_workspace_region": (ctypes.c_int, [ctypes.c_int32] * 7 + [ctypes.POINTER(ctypes.c_size_t)] * 2),
     "nvfp4_host_isa": (ctypes.c_int32, []),
     "nvfp4_moe_decode_host": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
@@ -288,6 +289,32 @@ def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str =
     return int(load_library().nvfp4_moe_prefill_workspace_size(T, H, I, E, topk, ACT[act]))
 
 
+WS_REGION = {"expert_offsets": 0, "sorted_pairs": 1, "pair_position": 2, "x_staged": 3, "x_rowscale": 4,
+             "h": 5, "h_exp": 6, "h_q": 7, "h_scale": 8, "y": 9}
+
+
+def prefill_workspace_region(T: int, H: int, I: int, E: int, topk: int, act: str, region: str):
+    """(byte offset, bytes) of an intermediate result inside a prefill workspace."""
+    off, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("nvfp4_moe_prefill_workspace_region", load_library().nvfp4_moe_prefill_workspace_region(
+        T, H, I, E, topk, ACT[act], WS_REGION[region], ctypes.byref(off), ctypes.byref(nb)))
+    return int(off.value), int(nb.value)
+
+
+DECODE_ERROR_WORD = slice(4, 8)       # bytes of the decode workspace's error flags
+DECODE_SPIN_WORD = slice(8, 12)       # bytes of its grid-barrier spin-limit override
+
+
+def check_decode_workspace(ws: torch.Tensor) -> None:
+    """Raise NVFP4Error if a decode call on this workspace reported a grid-barrier timeout
+    (its output is then invalid); clears the flag. Synchronizes with the device."""
+    word = ws[DECODE_ERROR_WORD].view(torch.int32)
+    flags = int(word.item())
+    if flags & 1:
+        word.zero_()
+        raise NVFP4Error("nvfp4_moe_decode", flags, "grid barrier timed out: the output is invalid")
+
+
 def _ws(ws: Optional[torch.Tensor], need: int, dev) -> torch.Tensor:
     """A workspace of at least `need` bytes; new ones are zero-filled (the decode
     workspace holds a grid-barrier counter that must start at zero)."""
@@ -298,7 +325,10 @@ def _ws(ws: Optional[torch.Tensor], need: int, dev) -> torch.Tensor:
 
 def moe_decode(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor,
                out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
-               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+               ws: Optional[torch.Tensor] = None, check: bool = True) -> torch.Tensor:
+    """check: read the workspace's error word after the call (a device synchronization)
+    and raise if the grid barrier timed out; launch loops pass False and call
+    check_decode_workspace() when they use a result."""
     lib = load_library()
     T, H = int(x.shape[0]), int(x.shape[1])
     k = int(ids.shape[1])
@@ -309,7 +339,26 @@ def moe_decode(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor
     _check("nvfp4_moe_decode", lib.nvfp4_moe_decode(
         _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
         _ptr(w), k, _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    if check and T > 0:
+        check_decode_workspace(ws)
     return out
+
+
+def _host_args(x, ids, w, out):
+    """The host entry point reads x, ids and w and writes T*H floats to out as host memory:
+    check devices, dtypes and shapes before handing it the pointers."""
+    T = int(x.shape[0])
+    for name, t in (("x", x), ("ids", ids), ("w", w), ("out", out)):
+        if t is not None and t.device.type != "cpu":
+            raise ValueError(f"{name} must be a CPU tensor for the host decode path (got {t.device})")
+    if x.dim() != 2 or x.dtype not in DTYPE:
+        raise ValueError("x must be a [T][H] tensor of a library dtype")
+    if ids.dim() != 2 or ids.dtype != torch.int32 or int(ids.shape[0]) != T:
+        raise ValueError("ids must be an int32 [T][topk] tensor")
+    if w.dtype != torch.float32 or tuple(w.shape) != tuple(ids.shape):
+        raise ValueError("w must be a float32 [T][topk] tensor")
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (T, int(x.shape[1]))):
+        raise ValueError("out must be a float32 [T][H] tensor")
 
 
 def host_isa() -> str:
@@ -323,6 +372,7 @@ def moe_decode_host(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.T
     """The routed-expert projection on the host CPU: every tensor (the layer's too) in host
     memory; x [T][H] float32 or bfloat16; returns (out float32 [T][H], dropped pairs)."""
     lib = load_library()
+    _host_args(x, ids, w, out)
     T, H = int(x.shape[0]), int(x.shape[1])
     k = int(ids.shape[1])
     if out is None:
@@ -380,6 +430,11 @@ class PreparedCall:
     def stage(self, i: int) -> None:
         _check(self.kind + "_stage", self.staged(i, *self.args, _stream(self.device)))
 
+    def check(self) -> None:
+        """Decode: raise if a call since the last check reported a grid-barrier timeout."""
+        if self.kind == "decode":
+            check_decode_workspace(self.keep[5])
+
 
 class PreparedHostCall:
     """A host-CPU decode call (nvfp4_moe_decode_host) with its arguments marshalled once,
@@ -387,6 +442,9 @@ class PreparedHostCall:
 
     def __init__(self, x, layer: Layer, ids, w, out, n_threads: int = 0, isa: str = "auto"):
         self.lib = load_library()
+        _host_args(x, ids, w, out)
+        if out is None:
+            raise ValueError("out must be given")
         self.keep = (x, layer, ids, w, out)
         self._w = (layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct())
         self._dropped = ctypes.c_int64(0)

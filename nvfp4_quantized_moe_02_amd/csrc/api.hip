@@ -56,9 +56,14 @@ RouteLayout route_layout(int64_t P, int E, bool with_tiles, Carver& c) {
   return l;
 }
 
+// Prefill workspace regions (act BF16 | W4A8): staged x (fp16 | int8) and its per-row
+// exponents (int32) | scales (fp32); h in sorted-pair order (fp16 scaled per gate/up block
+// | fp32) with the block exponents (int32 [P][blocks] | absent); the requantized h (absent |
+// int8 [P][I] and fp32 [P] scales); y, each pair's scaled down row (fp32 [P][H]).
 struct PrefillLayout {
   RouteLayout r;
-  size_t a16, sx, h, qh16, sh, y, end;
+  size_t xa, xs, h, hexp, qh, sh, y, end;
+  size_t xa_b, xs_b, h_b, hexp_b, qh_b, sh_b, y_b;
 };
 
 PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
@@ -67,12 +72,20 @@ PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
   const int64_t P = (int64_t)T * topk;
   l.r = route_layout(P, E, true, c);
   const bool w4a8 = act != NVFP4_ACT_BF16;
-  l.a16 = c.take((size_t)T * H * 2);
-  l.sx = c.take(w4a8 ? (size_t)T * 4 : 0);
-  l.h = c.take((size_t)P * I * (w4a8 ? 4 : 2));
-  l.qh16 = c.take(w4a8 ? (size_t)P * I * 2 : 0);
-  l.sh = c.take(w4a8 ? (size_t)P * 4 : 0);
-  l.y = c.take((size_t)P * H * 4);
+  l.xa_b = (size_t)T * H * (w4a8 ? 1 : 2);
+  l.xs_b = (size_t)T * 4;
+  l.h_b = (size_t)P * I * (w4a8 ? 4 : 2);
+  l.hexp_b = w4a8 ? 0 : (size_t)P * gateup_blocks(I) * 4;
+  l.qh_b = w4a8 ? (size_t)P * I : 0;
+  l.sh_b = w4a8 ? (size_t)P * 4 : 0;
+  l.y_b = (size_t)P * H * 4;
+  l.xa = c.take(l.xa_b);
+  l.xs = c.take(l.xs_b);
+  l.h = c.take(l.h_b);
+  l.hexp = c.take(l.hexp_b);
+  l.qh = c.take(l.qh_b);
+  l.sh = c.take(l.sh_b);
+  l.y = c.take(l.y_b);
   l.end = c.off;
   return l;
 }
@@ -160,7 +173,7 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (rows > 0x7fffffff) return NVFP4_EUNSUPPORTED;
   (void)hipGetLastError();
-  return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, 0, scale, as_stream(stream)));
+  return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, scale, as_stream(stream)));
 }
 
 // Router workspace: a 256-byte header (the completion counter of the single-launch path,
@@ -267,7 +280,7 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   if (act == NVFP4_ACT_W4A8) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
-  if ((H % 256) != 0 || (I % 128) != 0 || E > kMaxExperts) return NVFP4_EUNSUPPORTED;
+  if ((H % 256) != 0 || (I % 128) != 0 || I > 8192 || E > kMaxExperts) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * topk > (int64_t)1 << 30) return NVFP4_EUNSUPPORTED;
   const PrefillLayout l = prefill_layout(T, H, I, E, topk, act);
   if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
@@ -280,33 +293,57 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   int32_t* sorted = at<int32_t>(ws, l.r.sorted);
   int32_t* hdr = at<int32_t>(ws, l.r.hdr);
   TileDesc* tiles = at<TileDesc>(ws, l.r.tiles);
-  void* a16 = at<void>(ws, l.a16);
-  float* sx = at<float>(ws, l.sx);
-  float* sh = at<float>(ws, l.sh);
+  void* xa = at<void>(ws, l.xa);
   const int mode = act == NVFP4_ACT_BF16 ? 0 : 1;
+  float* xscale = mode == 1 ? at<float>(ws, l.xs) : nullptr;
+  int32_t* xexp = mode == 0 ? at<int32_t>(ws, l.xs) : nullptr;
+  int32_t* hexp = mode == 0 ? at<int32_t>(ws, l.hexp) : nullptr;
+  float* sh = mode == 1 ? at<float>(ws, l.sh) : nullptr;
   for (int stage = first; stage <= last; ++stage) {
     hipError_t e = hipSuccess;
     if (stage == 0) {  // route, stage the activations
       RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles, at<int32_t>(ws, l.r.inv)};
-      if (act == NVFP4_ACT_BF16) {
-        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s, x, a16, (int64_t)T * H);
+      if (mode == 0) {
+        e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s, x, xa, xexp, T, H);
       } else {
         e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
-        if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, a16, 1, sx, s);
+        if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, static_cast<int8_t*>(xa), xscale, s);
       }
     } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
-      e = launch_gemm_gateup(mode, a16, sx, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
-                             to_args(gate), to_args(up), at<void>(ws, l.h), s);
+      e = launch_gemm_gateup(mode, xa, xscale, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+                             to_args(gate), to_args(up), at<void>(ws, l.h), hexp, s);
       if (e == hipSuccess && mode == 1)
-        e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<void>(ws, l.qh16), 1, sh, s);
+        e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<int8_t>(ws, l.qh), sh, s);
     } else if (stage == 2) {  // down, scaled by gamma_d and the router weight, per pair
-      const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh16);
-      e = launch_gemm_down(mode, hA, sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+      const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh);
+      e = launch_gemm_down(mode, hA, sh, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
                            to_args(down), topk_weights, y, s);
     } else {  // top-k combine in slot order, one rounding to the output dtype
       e = launch_combine(y, at<int32_t>(ws, l.r.inv), T, topk, H, out, out_dtype, s);
     }
     if (e != hipSuccess) return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
+}
+
+int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act,
+                                       int32_t region, size_t* offset, size_t* bytes) {
+  if (!offset || !bytes || T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return NVFP4_EINVAL;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
+  const PrefillLayout l = prefill_layout(T, H, I, E, topk, act);
+  const size_t P = (size_t)T * topk;
+  switch (region) {
+    case NVFP4_WS_EXPERT_OFFSETS: *offset = l.r.offsets; *bytes = (size_t)(E + 1) * 4; break;
+    case NVFP4_WS_SORTED_PAIRS: *offset = l.r.sorted; *bytes = P * 4; break;
+    case NVFP4_WS_PAIR_POSITION: *offset = l.r.inv; *bytes = P * 4; break;
+    case NVFP4_WS_X_STAGED: *offset = l.xa; *bytes = l.xa_b; break;
+    case NVFP4_WS_X_ROWSCALE: *offset = l.xs; *bytes = l.xs_b; break;
+    case NVFP4_WS_H: *offset = l.h; *bytes = l.h_b; break;
+    case NVFP4_WS_H_EXP: *offset = l.hexp; *bytes = l.hexp_b; break;
+    case NVFP4_WS_H_Q: *offset = l.qh; *bytes = l.qh_b; break;
+    case NVFP4_WS_H_SCALE: *offset = l.sh; *bytes = l.sh_b; break;
+    case NVFP4_WS_Y: *offset = l.y; *bytes = l.y_b; break;
+    default: return NVFP4_EINVAL;
   }
   return NVFP4_OK;
 }

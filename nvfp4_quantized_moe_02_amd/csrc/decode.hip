@@ -47,7 +47,7 @@ struct DecodeSmem {
   int list[64];   // pairs grouped by unique expert, each group in pair order
   int start[65];  // group boundaries in list
   float wp[64];   // router weight of each pair
-  int nu, drop, ok, last;
+  int nu, drop, ok, last, spin;
   unsigned long long target;
   float part[kDecWaves][kRowsPerBlock][kDecodeMaxT];
 };
@@ -75,7 +75,7 @@ struct DecodeArgs {
   float* h;
   void* out;
   int out_dtype;
-  int32_t* hdr;                  // [0] dropped pairs, [1] error flags
+  int32_t* hdr;                  // [0] dropped pairs, [1] error flags, [2] spin-limit override
   unsigned long long* barrier;   // grid barrier counter
   unsigned long long* flags;     // grid barrier release flags, one 128-byte line per block
   int spin_limit;
@@ -154,6 +154,10 @@ __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x)
       sm.start[nu] = __popcll(vm);
       sm.nu = nu;
       sm.drop = __popcll(dm);
+      // grid-barrier spin limit: the workspace header's override word when nonzero
+      // (negative: no polling, every waiting block gives up at once)
+      const int ov = a.hdr[2];
+      sm.spin = ov > 0 ? ov : ov < 0 ? 0 : a.spin_limit;
     }
   }
   __syncthreads();
@@ -457,7 +461,7 @@ __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
     const unsigned long long* f = a.flags + (size_t)blockIdx.x * 16;
     int n = 0;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++n > a.spin_limit) {
+      if (++n > sm.spin) {
         sm.ok = 0;
         __hip_atomic_fetch_or(a.hdr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;

@@ -137,42 +137,54 @@ hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes
 }
 
 // ------------------------------------------------------------------ int8 row quantization
-// One block per row. s = absmax / 127 (IEEE fp32 division), q = rint(x / s) clamped to
-// +-127 (IEEE fp32 division, round half to even); all-zero rows give s = 0, q = 0.
-// OUTQ: 0 -> int8 codes, 1 -> the same integers as fp16 (exact), for the fp16 GEMMs.
-template <int XT, int OUTQ>
+// s = absmax / 127 (IEEE fp32 division), q = rint(x / s) clamped to +-127 (IEEE fp32
+// division, round half to even); all-zero rows give s = 0, q = 0. A row holding a NaN
+// gets s = NaN, else a row holding an infinity s = +inf; both get q = 0, so q * s is NaN
+// and the non-finite activation propagates.
+__device__ __forceinline__ float quant_scale(float absmax, bool has_nan) {
+  return has_nan ? __builtin_nanf("") : absmax / 127.0f;
+}
+__device__ __forceinline__ bool quant_scale_ok(float s) { return s > 0.f && s <= 3.402823466e38f; }
+__device__ __forceinline__ float quant_code(float v, float s, bool ok) {
+  return ok ? fminf(fmaxf(rintf(v / s), -127.f), 127.f) : 0.f;
+}
+
+// One block per row (any cols).
+template <int XT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int cols,
-                                                         void* __restrict__ q, float* __restrict__ scale) {
+                                                         int8_t* __restrict__ q, float* __restrict__ scale) {
   const int64_t r = blockIdx.x;
   __shared__ float red[4];
+  __shared__ int nan_any;
   auto load = [&](int c) -> float {
     if (XT == 1) return bf16_lo(reinterpret_cast<const uint16_t*>(x)[r * cols + c]);
     return reinterpret_cast<const float*>(x)[r * cols + c];
   };
+  if (threadIdx.x == 0) nan_any = 0;
+  __syncthreads();
   float m = 0.f;
-  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(load(c)));
+  bool nan = false;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    const float a = fabsf(load(c));
+    m = fmaxf(m, a);
+    nan |= a != a;
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if (nan) nan_any = 1;
   __syncthreads();
-  const float absmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = absmax / 127.0f;
-  for (int c = threadIdx.x; c < cols; c += 256) {
-    float v = 0.f;
-    if (s > 0.f) v = fminf(fmaxf(rintf(load(c) / s), -127.f), 127.f);
-    if (OUTQ == 0)
-      reinterpret_cast<int8_t*>(q)[r * cols + c] = (int8_t)(int)v;
-    else
-      reinterpret_cast<uint16_t*>(q)[r * cols + c] = f32_to_f16_bits(v);
-  }
+  const float s = quant_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), nan_any != 0);
+  const bool ok = quant_scale_ok(s);
+  for (int c = threadIdx.x; c < cols; c += 256) q[r * cols + c] = (int8_t)(int)quant_code(load(c), s, ok);
   if (threadIdx.x == 0) scale[r] = s;
 }
 
 // The same quantization with one wave per row and 8 elements per access (16-byte loads of
-// bf16, two of fp32; 16-byte fp16 or 8-byte int8 stores): cols % 8 == 0 and aligned rows.
-// The row is read twice; the second read comes from cache.
-template <int XT, int OUTQ>
+// bf16, two of fp32; 8-byte int8 stores): cols % 8 == 0 and aligned rows. The row is
+// read twice; the second read comes from cache.
+template <int XT>
 __global__ __launch_bounds__(256) void quant_rows_vec_kernel(const void* __restrict__ x, int64_t rows, int cols,
-                                                             void* __restrict__ q, float* __restrict__ scale) {
+                                                             int8_t* __restrict__ q, float* __restrict__ scale) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int lane = threadIdx.x & 63, nch = cols >> 3;
@@ -193,64 +205,48 @@ __global__ __launch_bounds__(256) void quant_rows_vec_kernel(const void* __restr
     }
   };
   float m = 0.f;
+  bool nan = false;
   for (int ch = lane; ch < nch; ch += 64) {
     float v[8];
     load8(ch, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(v[j]);
+      m = fmaxf(m, a);
+      nan |= a != a;
+    }
   }
   m = wave_max(m);
-  const float s = m / 127.0f;
+  const float s = quant_scale(m, __ballot(nan) != 0ull);
+  const bool ok = quant_scale_ok(s);
   for (int ch = lane; ch < nch; ch += 64) {
     float v[8];
     load8(ch, v);
+    uint32_t w[2] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = s > 0.f ? fminf(fmaxf(rintf(v[j] / s), -127.f), 127.f) : 0.f;
-    if (OUTQ == 0) {
-      uint32_t w[2] = {0, 0};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[j >> 2] |= ((uint32_t)(int)v[j] & 0xFFu) << (8 * (j & 3));
-      reinterpret_cast<uint2*>(reinterpret_cast<int8_t*>(q) + r * cols)[ch] = make_uint2(w[0], w[1]);
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)f32_to_f16_bits(v[2 * j]) | ((uint32_t)f32_to_f16_bits(v[2 * j + 1]) << 16);
-      reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(q) + r * cols)[ch] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int j = 0; j < 8; ++j) w[j >> 2] |= ((uint32_t)(int)quant_code(v[j], s, ok) & 0xFFu) << (8 * (j & 3));
+    reinterpret_cast<uint2*>(q + r * cols)[ch] = make_uint2(w[0], w[1]);
   }
   if (lane == 0) scale[r] = s;
 }
 
-hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
-                             float* scale, hipStream_t st) {
+hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, int8_t* q, float* scale,
+                             hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const bool vec = cols % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(q) % (q_f16 ? 16 : 8) == 0;
+  const bool vec = cols % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 8 == 0;
   if (vec) {
     const dim3 g((unsigned)((rows + 3) / 4));
-    if (x_dtype == 1) {
-      if (q_f16) quant_rows_vec_kernel<1, 1><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
-      else quant_rows_vec_kernel<1, 0><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
-    } else {
-      if (q_f16) quant_rows_vec_kernel<0, 1><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
-      else quant_rows_vec_kernel<0, 0><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
-    }
+    if (x_dtype == 1) quant_rows_vec_kernel<1><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
+    else quant_rows_vec_kernel<0><<<g, 256, 0, st>>>(x, rows, cols, q, scale);
     return hipGetLastError();
   }
   dim3 grid((unsigned)rows);
-  if (x_dtype == 1) {
-    if (q_f16) quant_rows_kernel<1, 1><<<grid, 256, 0, st>>>(x, cols, q, scale);
-    else quant_rows_kernel<1, 0><<<grid, 256, 0, st>>>(x, cols, q, scale);
-  } else {
-    if (q_f16) quant_rows_kernel<0, 1><<<grid, 256, 0, st>>>(x, cols, q, scale);
-    else quant_rows_kernel<0, 0><<<grid, 256, 0, st>>>(x, cols, q, scale);
-  }
+  if (x_dtype == 1) quant_rows_kernel<1><<<grid, 256, 0, st>>>(x, cols, q, scale);
+  else quant_rows_kernel<0><<<grid, 256, 0, st>>>(x, cols, q, scale);
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ activation staging
-// bf16 -> fp16 (round to nearest even; exact for |x| in the fp16 normal range).
+// ------------------------------------------------------------------ top-k combine
 // Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic. All
 // slot loads are issued before the first add (an absent slot reads row 0 and adds nothing);
 // y is read once, so its loads are non-temporal.

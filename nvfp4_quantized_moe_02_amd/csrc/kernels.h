@@ -27,8 +27,8 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
                           int K, int out_dtype, void* out, hipStream_t st);
 hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes, const uint8_t* scales,
                          const float* global, int N, int K, float* out, hipStream_t st);
-hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, void* q, int q_f16,
-                             float* scale, hipStream_t st);
+hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, int8_t* q, float* scale,
+                             hipStream_t st);
 // out[t][n] = sum over slots j (in order) of y[inv[t*topk + j]][n]; dropped slots skipped.
 hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, int H, void* out, int out_dtype,
                           hipStream_t st);
@@ -44,11 +44,12 @@ struct RouteWs {
   int32_t* inv;       // [P] sorted position of each pair, -1 if dropped (optional)
 };
 int route_blocks(int64_t P);
-// cvt_src (optional): n bf16 values converted to fp16 into cvt_dst by extra blocks of the
-// first launch (n a multiple of 8).
+// cvt_src (optional): bf16 activations [cvt_rows][cvt_cols] staged as fp16 into cvt_dst by
+// extra blocks of the first launch, each row scaled by 2^cvt_exp[row] (cvt_cols a multiple
+// of 8, rows 16-byte aligned).
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const RouteWs& ws, int tile_m, hipStream_t st, const void* cvt_src = nullptr,
-                        void* cvt_dst = nullptr, int64_t cvt_n = 0);
+                        void* cvt_dst = nullptr, int32_t* cvt_exp = nullptr, int cvt_rows = 0, int cvt_cols = 0);
 
 // decode.hip
 constexpr int kDecodeMaxT = 8;
@@ -56,7 +57,7 @@ constexpr int kDecodeMaxPairs = 64;
 constexpr int kDecodeMaxTH = 40960;  // T * H: the bf16 activations of a block live in LDS
 // stage 0: gate/up + SwiGLU; 1: down + combine; 2: both in one persistent launch (falls
 // back to 0 then 1 when the grid cannot be co-resident). hdr: [0] dropped pairs,
-// [1] error flags, [4..5] the grid-barrier counter; flags: decode_flag_bytes(H) of
+// [1] error flags, [2] grid-barrier spin limit when positive, [4..5] the grid-barrier counter; flags: decode_flag_bytes(H) of
 // per-block release flags (counter and flags zero before first use).
 constexpr int kDecodeRowsPerBlock = 8;
 inline size_t decode_flag_bytes(int H) { return (size_t)((H + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock) * 128; }
@@ -74,14 +75,20 @@ hipError_t launch_router(const void* x, int x_dtype, int T, int H, const uint16_
 
 // prefill.hip
 constexpr int kTileM = 128;
-hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* sorted_pairs,
-                              const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
-                              int max_tiles, int topk, int H, int I, const WeightArgs& gate,
-                              const WeightArgs& up, void* h, hipStream_t st);
+// act 0: fp16 activations with power-of-two row exponents (a_exp: x per token; h written
+// as fp16 with one exponent per (sorted pair, gate/up block) into hexp); act 1: int8
+// activations with fp32 row scales (a_scale), fp32 h.
+hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* a_exp,
+                              const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
+                              const int32_t* tile_count, int max_tiles, int topk, int H, int I,
+                              const WeightArgs& gate, const WeightArgs& up, void* h, int32_t* hexp,
+                              hipStream_t st);
+// gate/up blocks along I (the number of h exponents per sorted pair in act 0)
+int gateup_blocks(int I);
 // y[pos][n] = gamma_down * w[pair] * (h[pos] . Wdown[n]) for every sorted position pos
-hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* sorted_pairs,
-                            const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
-                            int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
-                            float* y, hipStream_t st);
+hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* hexp,
+                            const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
+                            const int32_t* tile_count, int max_tiles, int topk, int H, int I,
+                            const WeightArgs& down, const float* w, float* y, hipStream_t st);
 
 }  // namespace nvfp4

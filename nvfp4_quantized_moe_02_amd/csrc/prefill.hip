@@ -64,21 +64,32 @@ __device__ __forceinline__ f16x8_t bfrag(uint32_t word, _Float16 sc) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Q8_0 fragment: 8 int8 weights (two words) -> fp16 exactly (each byte with its sign bit
-// flipped, q + 128, becomes the mantissa of the fp16 value 1024 + q + 128 by a byte
-// permute; subtracting 1152 is exact), then one fp16 multiply by the block scale d: the
-// one rounding of the path's operands (relative error at most 2^-11).
-__device__ __forceinline__ f16x8_t bfrag_q8(uint32_t lo, uint32_t hi, _Float16 d) {
+// 8 int8 values (two words) -> 8 fp16 exactly: each byte with its sign bit flipped,
+// q + 128, becomes the mantissa of the fp16 value 1024 + q + 128 by a byte permute, and
+// subtracting 1152 is exact.
+__device__ __forceinline__ f16x8_t i8x8_f16(uint32_t lo, uint32_t hi) {
   const uint32_t u0 = lo ^ 0x80808080u, u1 = hi ^ 0x80808080u;
   const f16x2_t k = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2_t dd = {d, d};
-  const f16x2_t o0 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - k) * dd;
-  const f16x2_t o1 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - k) * dd;
-  const f16x2_t o2 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - k) * dd;
-  const f16x2_t o3 = (__builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - k) * dd;
+  const f16x2_t o0 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - k;
+  const f16x2_t o1 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - k;
+  const f16x2_t o2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - k;
+  const f16x2_t o3 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - k;
   const f16x4_t lo4 = __builtin_shufflevector(o0, o1, 0, 1, 2, 3);
   const f16x4_t hi4 = __builtin_shufflevector(o2, o3, 0, 1, 2, 3);
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Q8_0 fragment: 8 int8 weights -> fp16 exactly, then one fp16 multiply by the block
+// scale d: the one rounding of the path's operands (relative error at most 2^-11).
+__device__ __forceinline__ f16x8_t bfrag_q8(uint32_t lo, uint32_t hi, _Float16 d) {
+  const f16x8_t v = i8x8_f16(lo, hi);
+  const f16x8_t dd = {d, d, d, d, d, d, d, d};
+  return v * dd;
+}
+
+// fp16 bits of 2^-d for a right shift by d >= 0 bits (subnormal for d > 14, zero past 24).
+__device__ __forceinline__ uint32_t f16_pow2_neg(int d) {
+  return d <= 14 ? (uint32_t)(15 - d) << 10 : d <= 24 ? 1u << (24 - d) : 0u;
 }
 
 // SiLU for the fp16/fp32 h of the prefill path: exp and reciprocal from the hardware
@@ -117,12 +128,26 @@ struct BTile {
   __device__ static int slot(int row, int ch) { return row * ROWB + ((ch ^ ((row >> SHIFT) & (CPR - 1))) << 4); }
 };
 
-template <bool GATEUP, bool ASCALE, bool HOUT32, int NRB, int KQ, int WPB, int GK, bool Q8>
-__device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __restrict__ A, int K,
+// Activation modes. A_F16: fp16 activations staged with a power-of-two exponent per row
+// (gate/up: the token row's, from the staging launch; down: h stored per gate/up block
+// with that block's exponent, brought to the row's smallest exponent while A is staged into
+// LDS); the epilogue multiplies by 2^-exponent with ldexp, so no operand overflows or
+// underflows fp16 whatever the activations' range. A_I8: int8 activations (1 byte each,
+// converted to fp16 exactly when staged) with an fp32 scale per row (the W4A8 path).
+constexpr int A_F16 = 0, A_I8 = 1;
+constexpr int kMaxHSeg = 64;  // gate/up blocks along I that the down GEMM can rescale (I <= 8192)
+
+template <bool GATEUP, int AM, int NRB, int KQ, int WPB, int GK, bool Q8>
+__device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restrict__ A, int K,
                                           const uint8_t* b0row, const uint8_t* b1row,
                                           const uint8_t* const* bs, const WeightArgs& w0,
                                           const WeightArgs& w1, void* __restrict__ out, int ldo, char* lds,
-                                          const int* s_src, const float* s_coef) {
+                                          const int* s_src, const float* s_coef, const int* s_exp,
+                                          const uint8_t* s_hd, int seg_shift, float* s_red,
+                                          int32_t* __restrict__ hexp_out, int NB) {
+  constexpr bool HOUT32 = GATEUP && AM == A_I8;
+  constexpr int ES = AM == A_I8 ? 1 : 2;  // bytes per activation in memory
+  typedef typename std::conditional<AM == A_I8, uint2, uint4>::type ARaw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nkb = K / KBLK;
@@ -134,9 +159,10 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   constexpr int RPR = WPB * 8;
   constexpr int NA = (NRB * 32 + RPR - 1) / RPR;
   const int arow = tid >> 3, achunk = tid & 7;
-  const uint16_t* asrc[NA];
+  const char* asrc[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) asrc[i] = A + (size_t)s_src[arow + RPR * i] * K + achunk * 8;
+  for (int i = 0; i < NA; ++i)
+    asrc[i] = reinterpret_cast<const char*>(A) + ((size_t)s_src[arow + RPR * i] * K + achunk * 8) * ES;
   const int aslot = ((achunk ^ (arow & 7)) << 4);
 
   // B codes: the block's NCB weight rows, GK K-blocks (GK*32 bytes of each row) per
@@ -182,9 +208,26 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
       c[0] = __builtin_amdgcn_perm(r.y, r.x, psel);
     }
   };
-  auto load_a = [&](int kb, int i) -> uint4 {
+  auto load_a = [&](int kb, int i) -> ARaw {
     const int kc = kb < nkb ? kb : nkb - 1;
-    return *reinterpret_cast<const uint4*>(asrc[i] + kc * KBLK);
+    return *reinterpret_cast<const ARaw*>(asrc[i] + kc * KBLK * ES);
+  };
+  // the 8 fp16 values a thread stores for row arow + RPR*i of K-block kb
+  auto a_fp16 = [&](const ARaw& v, int kb, int i) -> uint4 {
+    if constexpr (AM == A_I8) {
+      return __builtin_bit_cast(uint4, i8x8_f16(v.x, v.y));
+    } else if constexpr (!GATEUP) {
+      const uint32_t m = f16_pow2_neg(s_hd[(arow + RPR * i) * kMaxHSeg + (kb >> seg_shift)]);
+      const f16x2_t mm = __builtin_bit_cast(f16x2_t, m | (m << 16));
+      return make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * mm),
+                        __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * mm),
+                        __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.z) * mm),
+                        __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.w) * mm));
+    } else {
+      (void)kb;
+      (void)i;
+      return v;
+    }
   };
 
   f32x16_t acc[NRB][2];
@@ -202,7 +245,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
   // The scales of the next group are loaded two K-blocks before the end of a scale group
   // and compacted at its end, inside the same loop iteration (a value carried across the
   // back-edge while loads are in flight makes the compiler drain every load there).
-  uint4 aq[2][NA];
+  ARaw aq[2][NA];
   uint4 bg[BT::CH];
   SRaw sq[2] = {load_s(0, 0), load_s(0, 1)};
   __builtin_amdgcn_sched_barrier(0);
@@ -224,7 +267,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     constexpr int R = Q & 1;                  // LDS stage / register ring slot
     char* st = lds + R * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = aq[R][i];
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = a_fp16(aq[R][i], kb, i);
     // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
     // finished those reads before passing the barrier of iteration kb-1.
     __syncthreads();
@@ -342,36 +385,76 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
     // 16-byte (fp32) piece straight to memory.
     const float gg = w0.global[tc.e], gu = w1.global[tc.e];
     const int col0 = tc.nb * (WPB * 32) + wave * 32 + 4 * half;
+    float hv[NRB][16];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = rb * 32 + l32;
-      const float xs = s_coef[r];
-      const float cg = xs * gg, cu = xs * gu;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if constexpr (AM == A_I8) {
+          const float xs = s_coef[r];
+          hv[rb][v] = silu_fast(acc[rb][0][v] * (xs * gg)) * (acc[rb][1][v] * (xs * gu));
+        } else {
+          // g = gamma_g * 2^-e * acc: the gamma product rounds once, the power of two is exact
+          const int ex = -s_exp[r];
+          hv[rb][v] = silu_fast(__builtin_amdgcn_ldexpf(acc[rb][0][v] * gg, ex)) *
+                      __builtin_amdgcn_ldexpf(acc[rb][1][v] * gu, ex);
+        }
+      }
+    }
+    // fp16 h (A_F16): each row of the block's WPB*32 intermediate indices is stored times
+    // 2^eb, eb chosen so that the row's largest magnitude in this block lands in
+    // [2^14, 2^15) (zero, infinite or NaN maxima take eb = 0); eb goes to hexp_out. The
+    // block maximum is reduced over the two lane halves and then over the waves in LDS.
+    int eb[NRB];
+    if constexpr (!HOUT32) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float m = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) m = fmaxf(m, fabsf(hv[rb][v]));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (half == 0) s_red[wave * BM + rb * 32 + l32] = m;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int r = rb * 32 + l32;
+        float m = s_red[r];
+#pragma unroll
+        for (int w = 1; w < WPB; ++w) m = fmaxf(m, s_red[w * BM + r]);
+        eb[rb] = (m > 0.f && m <= 3.402823466e38f) ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+        if (wave == 0 && half == 0 && r < tc.rows) hexp_out[(size_t)(tc.base + tc.m0 + r) * NB + tc.nb] = eb[rb];
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = rb * 32 + l32;
       const size_t rowoff = (size_t)(tc.base + tc.m0 + r) * ldo + col0;
+      if (r < tc.rows) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float hv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          hv[v] = silu_fast(acc[rb][0][4 * g + v] * cg) * (acc[rb][1][4 * g + v] * cu);
-        if (r < tc.rows) {
+        for (int g = 0; g < 4; ++g) {
           if constexpr (HOUT32) {
             *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + rowoff + 8 * g) =
-                f32x4_t{hv[0], hv[1], hv[2], hv[3]};
+                f32x4_t{hv[rb][4 * g], hv[rb][4 * g + 1], hv[rb][4 * g + 2], hv[rb][4 * g + 3]};
           } else {
-            const uint2 pk = {(uint32_t)f32_to_f16_bits(hv[0]) | ((uint32_t)f32_to_f16_bits(hv[1]) << 16),
-                              (uint32_t)f32_to_f16_bits(hv[2]) | ((uint32_t)f32_to_f16_bits(hv[3]) << 16)};
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + rowoff + 8 * g) = pk;
+            uint32_t pk[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              pk[j] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(hv[rb][4 * g + 2 * j], eb[rb])) |
+                      ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(hv[rb][4 * g + 2 * j + 1], eb[rb])) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + rowoff + 8 * g) = make_uint2(pk[0], pk[1]);
           }
         }
       }
     }
   } else {
-    // y[pos][n] = gamma_d * coef[pos] * acc, fp32, in sorted order; the combine kernel sums
-    // each token's slots. One row block at a time goes through LDS ([32][NCOL] fp32, 16-byte
-    // chunks XOR-swizzled by row), so every store is a full 16 bytes and a wave writes whole
-    // 1 KB row segments; the stores are non-temporal (y is read once, by the combine). The
-    // kernel's LDS holds 32 * NCOL * 4 bytes.
+    // y[pos][n] = gamma_d * coef[pos] * acc (A_F16: times 2^-e of the row, by ldexp), fp32,
+    // in sorted order; the combine kernel sums each token's slots. One row block at a time
+    // goes through LDS ([32][NCOL] fp32, 16-byte chunks XOR-swizzled by row), so every
+    // store is a full 16 bytes and a wave writes whole 1 KB row segments; the stores are
+    // non-temporal (y is read once, by the combine). The kernel's LDS holds
+    // 32 * NCOL * 4 bytes.
     constexpr int NCOL = WPB * 64;
     const float gd = w0.global ? w0.global[tc.e] : 1.0f;  // a Q8_0 down may have no tensor scale
     float* y = reinterpret_cast<float*>(out);
@@ -383,10 +466,13 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
       for (int i = 0; i < 16; ++i) {
         const int rr = (i >> 2) * 8 + half * 4 + (i & 3);
         const float c = s_coef[rb * 32 + rr] * gd;
+        const int ex = AM == A_F16 ? -s_exp[rb * 32 + rr] : 0;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           const int col = wave * 64 + cb * 32 + l32;
-          yl[rr * NCOL + (((col >> 2) ^ (rr & 7)) << 2) + (col & 3)] = acc[rb][cb][i] * c;
+          float v = acc[rb][cb][i] * c;
+          if constexpr (AM == A_F16) v = __builtin_amdgcn_ldexpf(v, ex);
+          yl[rr * NCOL + (((col >> 2) ^ (rr & 7)) << 2) + (col & 3)] = v;
         }
       }
       __syncthreads();
@@ -404,21 +490,30 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const uint16_t* __r
 }
 
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
-// ASCALE: multiply by a per-row activation scale (the W4A8 int8 scales).
-// HOUT32: gate/up writes fp32 h (for the int8 requantization), else fp16 h.
-template <bool GATEUP, bool ASCALE, bool HOUT32, int KQ, int WPB, int GK, bool Q8 = false>
+// AM: the activation mode (A_F16 or A_I8, above).
+// a_scale: A_I8 row scales (gate/up: per token; down: per sorted position).
+// a_exp: A_F16 exponents (gate/up: per token; down: per sorted position and gate/up block,
+// [P][nbh], whose blocks span 2^seg_shift K-blocks of the down GEMM).
+// hexp_out: gate/up A_F16 only, the exponents of the fp16 h it writes ([P][NB]).
+template <bool GATEUP, int AM, int KQ, int WPB, int GK, bool Q8 = false>
 __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
-    const uint16_t* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ sorted_pairs,
-    const int32_t* __restrict__ offsets, const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count,
-    int topk, int K, int NB, WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w,
-    void* __restrict__ out, int ldo) {
+    const void* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ a_exp, int nbh,
+    int seg_shift, const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ offsets,
+    const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count, int topk, int K, int NB,
+    WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w, void* __restrict__ out, int ldo,
+    int32_t* __restrict__ hexp_out) {
   // A stages and the B tile; the down epilogue reuses them (32 rows x WPB*64 fp32)
   constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, Q8 ? 2 : GK>::BYTES;
   constexpr int kEpi = GATEUP ? 0 : 32 * WPB * 64 * 4;
   constexpr int kLds = kMain > kEpi ? kMain : kEpi;
+  constexpr bool kHd = !GATEUP && AM == A_F16;    // down rescales A per gate/up block
+  constexpr bool kRed = GATEUP && AM == A_F16;    // gate/up reduces the row maxima of h
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   __shared__ int s_src[BM];
   __shared__ float s_coef[BM];
+  __shared__ int s_exp[BM];
+  __shared__ uint8_t s_hd[kHd ? BM * kMaxHSeg : 1];
+  __shared__ float s_red[kRed ? WPB * BM : 1];
 
   // XCD-aware order: consecutive logical tiles (the N blocks of one row tile, then the
   // row tiles of one expert) run on the same XCD and share its L2.
@@ -446,10 +541,21 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const int p = sorted_pairs[pos];
     if (GATEUP) {
       s_src[tid] = p / topk;
-      s_coef[tid] = ASCALE ? a_scale[p / topk] : 1.0f;
+      s_coef[tid] = AM == A_I8 ? a_scale[p / topk] : 1.0f;
+      s_exp[tid] = AM == A_F16 ? a_exp[p / topk] : 0;
     } else {
       s_src[tid] = pos;
-      s_coef[tid] = route_w[p] * (ASCALE ? a_scale[pos] : 1.0f);
+      s_coef[tid] = route_w[p] * (AM == A_I8 ? a_scale[pos] : 1.0f);
+      if constexpr (kHd) {
+        // the row's smallest exponent (its largest block), and each block's shift down to it
+        const int32_t* ex = a_exp + (size_t)pos * nbh;
+        int emin = ex[0];
+        for (int b = 1; b < nbh; ++b) emin = min(emin, ex[b]);
+        for (int b = 0; b < nbh; ++b) s_hd[tid * kMaxHSeg + b] = (uint8_t)min(ex[b] - emin, 31);
+        s_exp[tid] = emin;
+      } else {
+        s_exp[tid] = 0;
+      }
     }
   }
 
@@ -473,14 +579,18 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
   __syncthreads();
 
   const int nrb = (tc.rows + 31) >> 5;
+#define NVFP4_TILE(R)                                                                                            \
+  gemm_tile<GATEUP, AM, R, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef, \
+                                            s_exp, s_hd, seg_shift, s_red, hexp_out, NB)
   if (nrb == 4)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 4, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    NVFP4_TILE(4);
   else if (nrb == 3)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 3, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    NVFP4_TILE(3);
   else if (nrb == 2)
-    gemm_tile<GATEUP, ASCALE, HOUT32, 2, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    NVFP4_TILE(2);
   else
-    gemm_tile<GATEUP, ASCALE, HOUT32, 1, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef);
+    NVFP4_TILE(1);
+#undef NVFP4_TILE
 }
 
 static inline unsigned grid_for(int max_tiles, int NB) {
@@ -488,68 +598,76 @@ static inline unsigned grid_for(int max_tiles, int NB) {
   return (unsigned)(((g + 7) / 8) * 8);
 }
 
-hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* sorted_pairs,
-                              const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
-                              int max_tiles, int topk, int H, int I, const WeightArgs& gate,
-                              const WeightArgs& up, void* h, hipStream_t st) {
+hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* a_exp,
+                              const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
+                              const int32_t* tile_count, int max_tiles, int topk, int H, int I,
+                              const WeightArgs& gate, const WeightArgs& up, void* h, int32_t* hexp,
+                              hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(a);
   // 8 waves (256 intermediate indices per block) when I allows, else 4 (128); H is a
   // multiple of 256, so scale groups of 4 K-blocks; B groups of 2 K-blocks.
-#define NVFP4_GU(ASC, H32, WPB, GK)                                                                      \
-  moe_gemm_f16_kernel<true, ASC, H32, 4, WPB, GK><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>( \
-      A, a_scale, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, nullptr, h, I)
+#define NVFP4_GU(AM, WPB)                                                                                  \
+  moe_gemm_f16_kernel<true, AM, 4, WPB, 2><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>(      \
+      a, a_scale, a_exp, 0, 0, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, \
+      nullptr, h, I, hexp)
   const bool w8 = I % 256 == 0;
   if (act == 0) {
     if (w8)
-      NVFP4_GU(false, false, 8, 2);
+      NVFP4_GU(A_F16, 8);
     else
-      NVFP4_GU(false, false, 4, 2);
+      NVFP4_GU(A_F16, 4);
   } else {
     if (w8)
-      NVFP4_GU(true, true, 8, 2);
+      NVFP4_GU(A_I8, 8);
     else
-      NVFP4_GU(true, true, 4, 2);
+      NVFP4_GU(A_I8, 4);
   }
 #undef NVFP4_GU
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* sorted_pairs,
-                            const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
-                            int max_tiles, int topk, int H, int I, const WeightArgs& down, const float* w,
-                            float* y, hipStream_t st) {
+int gateup_blocks(int I) { return I % 256 == 0 ? I / 256 : I / 128; }
+
+hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* hexp,
+                            const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
+                            const int32_t* tile_count, int max_tiles, int topk, int H, int I,
+                            const WeightArgs& down, const float* w, float* y, hipStream_t st) {
   if (max_tiles == 0) return hipSuccess;
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(h);
+  // fp16 h: one exponent per gate/up block of 256 (or 128) intermediate indices, i.e. per
+  // 4 (or 2) K-blocks of this GEMM
+  const int nbh = gateup_blocks(I);
+  const int seg_shift = I % 256 == 0 ? 2 : 1;
   // 8 waves (512 outputs per block) when H allows, else 4 (256); scale groups of 4
   // K-blocks when I is a multiple of 256, else 2; B groups of 2 K-blocks.
-#define NVFP4_DOWN(ASC, KQ, WPB)                                                                           \
-  do {                                                                                                     \
-    const dim3 grid = grid_for(max_tiles, H / (WPB * 64));                                                 \
-    if (down.fmt == 1)                                                                                     \
-      moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2, true><<<grid, WPB * 64, 0, st>>>(                 \
-          A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), down, down, w, y, H); \
-    else                                                                                                   \
-      moe_gemm_f16_kernel<false, ASC, false, KQ, WPB, 2><<<grid, WPB * 64, 0, st>>>(                       \
-          A, h_scale, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), down, down, w, y, H); \
+#define NVFP4_DOWN(AM, KQ, WPB)                                                                             \
+  do {                                                                                                      \
+    const dim3 grid = grid_for(max_tiles, H / (WPB * 64));                                                  \
+    if (down.fmt == 1)                                                                                      \
+      moe_gemm_f16_kernel<false, AM, KQ, WPB, 2, true><<<grid, WPB * 64, 0, st>>>(                          \
+          h, h_scale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), \
+          down, down, w, y, H, nullptr);                                                                    \
+    else                                                                                                    \
+      moe_gemm_f16_kernel<false, AM, KQ, WPB, 2><<<grid, WPB * 64, 0, st>>>(                                \
+          h, h_scale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), \
+          down, down, w, y, H, nullptr);                                                                    \
   } while (0)
-#define NVFP4_DOWN_W(ASC, KQ) \
-  if (H % 512 == 0)           \
-    NVFP4_DOWN(ASC, KQ, 8);   \
-  else                        \
-    NVFP4_DOWN(ASC, KQ, 4);
+#define NVFP4_DOWN_W(AM, KQ) \
+  if (H % 512 == 0)          \
+    NVFP4_DOWN(AM, KQ, 8);   \
+  else                       \
+    NVFP4_DOWN(AM, KQ, 4);
   const bool q4 = I % 256 == 0;
   if (act == 0) {
     if (q4) {
-      NVFP4_DOWN_W(false, 4)
+      NVFP4_DOWN_W(A_F16, 4)
     } else {
-      NVFP4_DOWN_W(false, 2)
+      NVFP4_DOWN_W(A_F16, 2)
     }
   } else {
     if (q4) {
-      NVFP4_DOWN_W(true, 4)
+      NVFP4_DOWN_W(A_I8, 4)
     } else {
-      NVFP4_DOWN_W(true, 2)
+      NVFP4_DOWN_W(A_I8, 2)
     }
   }
 #undef NVFP4_DOWN_W

@@ -11,26 +11,51 @@ namespace nvfp4 {
 int route_blocks(int64_t P) { return (int)((P + kRouteChunk - 1) / kRouteChunk); }
 
 // Blocks [0, nblk): expert histogram of one chunk of kRouteChunk pairs. Blocks after that
-// (optional) convert the bf16 activations to fp16 for the prefill GEMMs, 2048 values per
-// block: the routing grid is small, so the conversion runs beside it in the same launch.
+// (optional) stage the bf16 activations as fp16 for the prefill GEMMs, one wave per token
+// row: the row is scaled by 2^e, e chosen so that its largest magnitude lands in
+// [2^14, 2^15), so every bf16 value of the row above 2^-17 of that magnitude is exact in
+// fp16 and nothing overflows, whatever the row's range; e goes to cvt_exp[row] and the
+// gate/up epilogue multiplies by 2^-e (exact). Rows holding an infinity or a NaN, and
+// all-zero rows, take e = 0. The routing grid is small, so the staging runs beside it in
+// the same launch.
+__device__ __forceinline__ int f16_stage_exponent(float absmax) {
+  if (!(absmax > 0.f) || !(absmax <= 3.402823466e38f)) return 0;  // zero, inf or NaN
+  return 15 - __builtin_amdgcn_frexp_expf(absmax);  // absmax in [2^(x-1), 2^x) -> [2^14, 2^15)
+}
+
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
                                                           int nblk, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ dropped,
                                                           const uint4* __restrict__ cvt_src,
-                                                          uint4* __restrict__ cvt_dst, int64_t cvt_n8) {
+                                                          uint4* __restrict__ cvt_dst, int32_t* __restrict__ cvt_exp,
+                                                          int cvt_rows, int cvt_row8) {
   extern __shared__ int32_t hist[];
   __shared__ int32_t drop;
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b >= nblk) {
-    const int64_t i = (int64_t)(b - nblk) * 256 + tid;
-    if (i >= cvt_n8) return;
-    const uint4 v = cvt_src[i];
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
+    const int row = (b - nblk) * 4 + (tid >> 6), lane = tid & 63;
+    if (row >= cvt_rows) return;
+    const uint4* src = cvt_src + (size_t)row * cvt_row8;
+    float m = 0.f;
+    for (int i = lane; i < cvt_row8; i += 64) {
+      const uint4 v = src[i];
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = (uint32_t)f32_to_f16_bits(bf16_lo(in[j])) | ((uint32_t)f32_to_f16_bits(bf16_hi(in[j])) << 16);
-    cvt_dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(in[j])), fabsf(bf16_hi(in[j]))));
+    }
+    const int e = f16_stage_exponent(wave_max(m));
+    uint4* dst = cvt_dst + (size_t)row * cvt_row8;
+    for (int i = lane; i < cvt_row8; i += 64) {
+      const uint4 v = src[i];
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(bf16_lo(in[j]), e)) |
+               ((uint32_t)f32_to_f16_bits(__builtin_amdgcn_ldexpf(bf16_hi(in[j]), e)) << 16);
+      dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (lane == 0) cvt_exp[row] = e;
     return;
   }
   for (int e = tid; e < E; e += 256) hist[e] = 0;
@@ -179,14 +204,14 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __res
 
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const RouteWs& ws, int tile_m, hipStream_t st, const void* cvt_src, void* cvt_dst,
-                        int64_t cvt_n) {
+                        int32_t* cvt_exp, int cvt_rows, int cvt_cols) {
   const int nblk = route_blocks(P);
-  const int64_t cvt_n8 = cvt_src != nullptr ? cvt_n / 8 : 0;
-  const int64_t cvt_blocks = (cvt_n8 + 255) / 256;
+  const int rows = cvt_src != nullptr ? cvt_rows : 0;
+  const int64_t cvt_blocks = (rows + 3) / 4;
   if (nblk + cvt_blocks > 0) {
     route_count_kernel<<<dim3((unsigned)(nblk + cvt_blocks)), 256, (size_t)E * sizeof(int32_t), st>>>(
         ids, P, E, nblk, ws.counts, ws.dropped, reinterpret_cast<const uint4*>(cvt_src),
-        reinterpret_cast<uint4*>(cvt_dst), cvt_n8);
+        reinterpret_cast<uint4*>(cvt_dst), cvt_exp, rows, cvt_cols / 8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -372,16 +372,18 @@ def w4a8_pair_hidden(x_bf16_bits: np.ndarray, layer, ids, rows=None):
 
 
 def w4a8_down_from_codes(qh: np.ndarray, sh: np.ndarray, pairs: np.ndarray, layer, ids: np.ndarray,
-                         w: np.ndarray) -> np.ndarray:
+                         w: np.ndarray, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """The W4A8 down projection and combine on given int8 hidden rows: for each listed
     pair p = t*k + j (row i of qh, sh), out[t] += w[t][j] * gamma_d * (qh[i] * sh[i]) .
     Wd_e^T with e = ids[t][j]. This is the last step of moe_w4a8 with the hidden codes
     supplied by the caller (the configuration text's "the oracle uses the same int8
-    activations" read literally for the requantized h). Returns float64 [T][H]."""
+    activations" read literally for the requantized h). Returns float64 [T][H], or only the
+    given token rows (every listed pair must belong to one of them)."""
     T, k = ids.shape
     pairs = np.asarray(pairs, dtype=np.int64)
     hh = np.asarray(qh, dtype=np.int8).astype(np.float64) * np.asarray(sh, dtype=np.float32).astype(np.float64)[:, None]
-    out = np.zeros((T, layer.H), dtype=np.float64)
+    row_of = {t: t for t in range(T)} if rows is None else {int(t): i for i, t in enumerate(rows)}
+    out = np.zeros((len(row_of), layer.H), dtype=np.float64)
     ex = ids.reshape(-1)[pairs]
     for e in np.unique(ex):
         if e < 0 or e >= layer.E:
@@ -391,7 +393,7 @@ def w4a8_down_from_codes(qh: np.ndarray, sh: np.ndarray, pairs: np.ndarray, laye
         Y = (hh[sel] @ Wd.T) * gd
         for i, r in enumerate(sel):
             p = int(pairs[r])
-            out[p // k] += float(w[p // k, p % k]) * Y[i]
+            out[row_of[p // k]] += float(w[p // k, p % k]) * Y[i]
     return out
 
 

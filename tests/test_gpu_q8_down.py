@@ -7,8 +7,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import (DEV, TOL, bf16_dev, bf16_out_to_f64, layer_dev, max_row_rel_l2, sparse_layer,
-                      w4a8_check, w4a8_tie_bound)
+from gpu_util import (DEV, TOL, bf16_dev, bf16_out_to_f64, cover_rows, layer_dev, max_row_rel_l2, sparse_layer,
+                      w4a8_strict)
 
 pytestmark = pytest.mark.gpu
 nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
@@ -44,11 +44,13 @@ def _small(seed, E, H, I, T, k, act="bf16", gamma=False):
     xb = W.draw_activations(seed, T, H, outlier_frac=0.001)
     ids = W.draw_routing_zipf(seed, T, E, k, s=1.1)
     w = W.draw_router_weights(seed, T, k)
+    ws = torch.zeros(nv.prefill_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device=DEV)
     y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act=act,
-                       out_dtype=torch.float32)
+                       out_dtype=torch.float32, ws=ws)
+    got = y.cpu().numpy().astype(np.float64)
     if act == "bf16":
-        return y.cpu().numpy().astype(np.float64), O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w), None
-    return (y.cpu().numpy().astype(np.float64), O.moe_w4a8(xb, lay, ids, w), w4a8_tie_bound(xb, lay, ids, w))
+        return got, O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w), None
+    return got, None, w4a8_strict(xb, lay, ids, w, np.arange(T), ws, got, act=act)
 
 
 @pytest.mark.parametrize("H,I", [(512, 256), (512, 384), (256, 128), (768, 256)])
@@ -64,9 +66,8 @@ def test_prefill_q8_down_shapes(H, I):
 def test_prefill_q8_down_tensor_scale_and_w4a8():
     got, ref, _ = _small(33, 8, 512, 256, 400, 8, gamma=True)
     assert max_row_rel_l2(got, ref) < 1e-3
-    got, ref, bound = _small(35, 8, 512, 256, 400, 8, act="w4a8_f16")
-    err, ntie = w4a8_check(got, ref, bound)
-    print(f"w4a8 (fp16 MMA) with Q8_0 down: max row rel L2 {err:.3e} ({ntie} rows with a tie allowance)")
+    _, _, stats = _small(35, 8, 512, 256, 400, 8, act="w4a8_f16")
+    print(f"w4a8 (fp16 MMA) with Q8_0 down: {stats}")
 
 
 def test_prefill_q8_down_equals_nvfp4_down_bitwise():
@@ -98,13 +99,14 @@ def test_prefill_q8_down_equals_nvfp4_down_bitwise():
         assert torch.equal(y4, y8), act
 
 
-def test_prefill_c3_q8_down_full_size_sampled():
-    """The 8192-token workload with a Q8_0 down projection, sampled rows."""
+def test_prefill_c3_q8_down_full_size_cover():
+    """The 8192-token workload with a Q8_0 down projection: >= 1024 rows covering every
+    routed expert and its last tile."""
     lay = W.draw_layer(W.config_seed(3), down_fmt="q8_0")
     dl = layer_dev(lay)
     wl = W.draw_workload(3)
     y = nv.moe_prefill(bf16_dev(wl.x), dl, torch.from_numpy(wl.ids).to(DEV), torch.from_numpy(wl.w).to(DEV))
-    rows = np.sort(np.random.default_rng(3).choice(wl.T, size=16, replace=False))
+    rows = cover_rows(wl.ids, lay.E, n=1024, seed=3)
     ref = O.moe_grouped(O.bf16_to_f64(wl.x), lay, wl.ids, wl.w, rows=rows)
     got = bf16_out_to_f64(y[torch.from_numpy(rows).to(DEV)])
     err = max_row_rel_l2(got, ref)

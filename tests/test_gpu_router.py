@@ -38,10 +38,14 @@ def _run(x_dev, x_f64, wr_bits, k):
         ex = np.exp(sel - sel[0])
         assert np.allclose(wts[t], ex / ex.sum(), rtol=2e-6, atol=1e-7), t
     # against the oracle's ids where the k-th and (k+1)-th oracle logits are not within
-    # twice the bound of each other
+    # twice the bound of each other; where the ids agree, the weights against the oracle's
+    # softmax: a logit error of at most d moves each weight by a factor within exp(+-2d),
+    # plus a few fp32 roundings of the exponentials, the sum and the division
     ntie = 0
     for t in range(T):
         if ids[t].tolist() == rids[t].tolist():
+            d = float(bound[t, ids[t]].max())
+            assert np.all(np.abs(wts[t] - rw[t]) <= rw[t] * (np.expm1(2 * d) + 2e-6) + 1e-30), t
             continue
         srt = np.sort(rlg[t])[::-1]
         assert k < E and srt[k - 1] - srt[k] <= 2 * bound[t].max() or \

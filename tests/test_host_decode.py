@@ -157,6 +157,20 @@ def test_empty_and_validation():
     with pytest.raises(nv.NVFP4Error) as e:
         nv.moe_decode_host(x.half(), L, ti, tw)  # fp16 activations are not accepted
     assert e.value.status == -1
+    # caller tensors the C side would read or write as host memory of the wrong size or
+    # type are refused by the binding before the call
+    for bad in (dict(out=torch.empty((2, lay.H), dtype=torch.bfloat16)),
+                dict(out=torch.empty((1, lay.H), dtype=torch.float32))):
+        with pytest.raises(ValueError):
+            nv.moe_decode_host(x, L, ti, tw, **bad)
+        with pytest.raises(ValueError):
+            nv.PreparedHostCall(x, L, ti, tw, bad["out"])
+    with pytest.raises(ValueError):
+        nv.moe_decode_host(x, L, ti.long(), tw)
+    with pytest.raises(ValueError):
+        nv.moe_decode_host(x, L, ti, tw[:, :1].contiguous())
+    with pytest.raises(ValueError):
+        nv.PreparedHostCall(x, L, ti, tw, None)
     q8 = W.draw_layer(23, E=16, H=lay.I, I=lay.H, down_fmt="q8_0").down  # [E][I][H] Q8_0
     with pytest.raises(nv.NVFP4Error) as e:
         nv.moe_decode_host(x, nv.Layer(nv.Q8Proj.from_numpy(q8, "cpu"), L.up, L.down), ti, tw)
