@@ -147,12 +147,11 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
  * x [T][H] bf16; gate/up: N = I, K = H, NVFP4; down: N = H, K = I, NVFP4 or Q8_0
  * (Q8_0 dot products in FP32, each 32-input block scaled once); out [T][H] in out_dtype
  * (F32 or BF16). ws needs nvfp4_moe_decode_workspace_size() bytes and must be
- * zero-filled before its first use (it holds a grid-barrier counter and per-block release
- * flags that every successful call leaves ready for the next; zero it again if H changes
- * or after an error). Bytes
+ * zero-filled before its first use (it holds a grid-barrier counter, epoch and per-block
+ * release flags that every call leaves ready for the next, whatever the shapes). Bytes
  * 4..7 of ws hold an error word: bit 0 is set if a call's grid barrier timed out (the
- * output of that call is then invalid; the bit stays set until the caller clears it, and
- * the barrier state stays consistent, so the next call may proceed once it is cleared).
+ * output rows of the blocks that gave up are then NaN; the bit stays set until the
+ * caller clears it, and the barrier state stays consistent for the next call).
  * A timeout can only happen if other work keeps some of the grid's blocks from starting
  * while the rest wait; the caller must check the word after calls whose result it uses.
  * Bytes 8..11 (int32), when positive, replace the barrier's spin limit (default 2^22
@@ -170,6 +169,24 @@ int nvfp4_moe_decode(const void* x, int32_t x_dtype, int32_t T, int32_t H, const
                      const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
                      const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
                      int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode that allocates nothing, for callers that cannot allocate or pass device memory
+ * between calls: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. The same computation, kernels and results as nvfp4_moe_decode, with the
+ * workspace taken from a static device array of 1 MiB (one copy per GPU, held until the
+ * process ends) instead of the caller's ws. The caller still passes x, the weights, the
+ * routing and out. The first call on a device looks up that device's array and clears
+ * its barrier state with a fill kernel on `stream`, ahead of the call; the call itself
+ * makes no allocation. Every call on one GPU shares its array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialized by the caller.
+ * A grid-barrier timeout (see nvfp4_moe_decode) leaves NaN in the affected output rows.
+ * Errors: those of nvfp4_moe_decode, and EUNSUPPORTED when the call would need more than
+ * the 1 MiB (nvfp4_moe_decode_workspace_size() above 1048576 bytes: 131,328 bytes of
+ * header and flag lines plus T * topk * I * 4 bytes of h). */
+int nvfp4_moe_decode_noalloc(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                             const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                             const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
+                             int32_t out_dtype, void* stream);
 
 /* Prefill (any T >= 0): the same projection as grouped GEMMs on matrix cores, one
  * launch per stage for all experts. x [T][H] bf16; out [T][H] bf16 or f32 (accumulated

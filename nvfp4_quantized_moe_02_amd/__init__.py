@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     linear,
     load_library,
     moe_decode,
+    moe_decode_noalloc,
     moe_prefill,
     quant_rows_i8,
     route,

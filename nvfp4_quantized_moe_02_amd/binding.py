@@ -81,6 +81,11 @@ _SIGS = {
                                                ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4_moe_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 6),
     "nvfp4_moe_prefill_workspace_region": (ctypes.c_int, [ctypes.c_int32] * 7 + [ctypes.POINTER(ctypes.c_size_t)] * 2),
+    "nvfp4_moe_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
+                                                ctypes.POINTER(_Weight), ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_void_p]),
     "nvfp4_host_isa": (ctypes.c_int32, []),
     "nvfp4_moe_decode_host": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(_Weight), ctypes.POINTER(_Weight),
@@ -359,6 +364,19 @@ def _host_args(x, ids, w, out):
         raise ValueError("w must be a float32 [T][topk] tensor")
     if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != (T, int(x.shape[1]))):
         raise ValueError("out must be a float32 [T][H] tensor")
+
+
+def moe_decode_noalloc(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor,
+                       out: torch.Tensor) -> torch.Tensor:
+    """nvfp4_moe_decode_noalloc: the decode with the library's static device scratch as its
+    workspace (no workspace argument; out must be given)."""
+    lib = load_library()
+    T, H = int(x.shape[0]), int(x.shape[1])
+    g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
+    _check("nvfp4_moe_decode_noalloc", lib.nvfp4_moe_decode_noalloc(
+        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+        _ptr(w), int(ids.shape[1]), _ptr(out), DTYPE[out.dtype], _stream(x.device)))
+    return out
 
 
 def host_isa() -> str:

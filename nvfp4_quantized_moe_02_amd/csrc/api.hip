@@ -4,6 +4,7 @@
 #include "host.h"
 #include "kernels.h"
 
+#include <mutex>
 #include <new>
 
 using namespace nvfp4;
@@ -94,11 +95,14 @@ struct DecodeLayout {
   size_t hdr, flags, h, end;
 };
 
+// The flag lines are reserved for the largest supported H, so calls with different H on
+// one workspace never place h where an earlier call's flag lines are.
 DecodeLayout decode_layout(int T, int H, int I, int topk) {
+  (void)H;
   Carver c;
   DecodeLayout l;
   l.hdr = c.take(64);
-  l.flags = c.take(decode_flag_bytes(H));
+  l.flags = c.take(decode_flag_bytes(kDecodeMaxH));
   l.h = c.take((size_t)T * topk * I * 4);
   l.end = c.off;
   return l;
@@ -223,20 +227,21 @@ static int check_moe_common(const void* x, int32_t T, int32_t H, const nvfp4_wei
   return NVFP4_OK;
 }
 
+// dry: validate only (nothing is enqueued).
 static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int32_t T, int32_t H,
                        const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
                        const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
-                       int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t out_dtype, void* ws, size_t ws_bytes, void* stream, bool dry = false) {
   int st = check_moe_common(x, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, ws);
   if (st != NVFP4_OK) return st;
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
-  if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > 8192 || I > 8192) return NVFP4_EUNSUPPORTED;
+  if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > kDecodeMaxH || I > 8192) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * H > kDecodeMaxTH) return NVFP4_EUNSUPPORTED;  // activations are staged in LDS
   const DecodeLayout l = decode_layout(T, H, I, topk);
   if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
-  if (T == 0) return NVFP4_OK;
+  if (T == 0 || dry) return NVFP4_OK;
   (void)hipGetLastError();
   // the full call runs as one persistent launch (mode 2); a single stage as mode 0 or 1
   const int mode = (first == 0 && last == 1) ? 2 : first;
@@ -261,6 +266,68 @@ int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_
   if (stage < 0 || stage > 1) return NVFP4_EINVAL;
   return decode_impl(stage, stage, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out,
                      out_dtype, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ decode without allocation
+// Device scratch of nvfp4_moe_decode_noalloc: the decode workspace (header, barrier flag
+// lines, h) in a static device array, one copy per GPU, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until set up
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The device address of this device's scratch (taken with the device current, once per
+// device; the array's name in host code is only a stand-in). On that first set-up the
+// header and the flag lines, the barrier state that must start at zero, are cleared by a
+// fill kernel on the caller's stream (ahead of the call's own launch).
+int scratch_for_device(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return NVFP4_EHIP;
+    const DecodeLayout l = decode_layout(1, 1, 1, 1);  // header and flags sit first, for any shape
+    zero_fill_kernel<<<dim3(16), 256, 0, s>>>(static_cast<uint4*>(p), l.h / 16);
+    if (hipGetLastError() != hipSuccess) return NVFP4_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int nvfp4_moe_decode_noalloc(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                             const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                             const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
+                             int32_t out_dtype, void* stream) {
+  if (!gate || T < 0 || topk < 1) return NVFP4_EINVAL;
+  const size_t need = nvfp4_moe_decode_workspace_size(T, H, gate->N, E, topk);
+  if (need > kNoAllocScratchBytes) return NVFP4_EUNSUPPORTED;
+  // every argument is checked before the set-up enqueues anything (a stand-in aligned,
+  // non-null workspace pointer: validation never dereferences it)
+  void* const probe = reinterpret_cast<void*>(uintptr_t(256));
+  int st = decode_impl(0, 1, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, out_dtype, probe,
+                       kNoAllocScratchBytes, stream, true);
+  if (st != NVFP4_OK || T == 0) return st;
+  void* ws = nullptr;
+  st = scratch_for_device(as_stream(stream), &ws);
+  if (st != NVFP4_OK) return st;
+  return decode_impl(0, 1, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, out_dtype, ws,
+                     kNoAllocScratchBytes, stream);
 }
 
 size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act) {

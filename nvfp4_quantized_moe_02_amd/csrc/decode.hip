@@ -48,7 +48,7 @@ struct DecodeSmem {
   int start[65];  // group boundaries in list
   float wp[64];   // router weight of each pair
   int nu, drop, ok, last, spin;
-  unsigned long long target;
+  unsigned long long epoch;
   float part[kDecWaves][kRowsPerBlock][kDecodeMaxT];
 };
 
@@ -76,7 +76,8 @@ struct DecodeArgs {
   void* out;
   int out_dtype;
   int32_t* hdr;                  // [0] dropped pairs, [1] error flags, [2] spin-limit override
-  unsigned long long* barrier;   // grid barrier counter
+  unsigned* barrier;             // grid barrier arrival counter (zero between calls)
+  unsigned long long* epoch;     // grid barrier epoch (grows by one per fused call)
   unsigned long long* flags;     // grid barrier release flags, one 128-byte line per block
   int spin_limit;
   int h_in_lds;                  // phase 2 reads h from LDS (P * I * 4 bytes fit)
@@ -158,6 +159,8 @@ __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x)
       // (negative: no polling, every waiting block gives up at once)
       const int ov = a.hdr[2];
       sm.spin = ov > 0 ? ov : ov < 0 ? 0 : a.spin_limit;
+      // the barrier epoch of this call (read before this block arrives at the barrier)
+      sm.epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
@@ -431,30 +434,32 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
 
 // Grid barrier over gridDim.x co-resident blocks. h was stored write-through (agent
 // scope), so arrival only needs every wave's stores complete (vmcnt 0) before one
-// relaxed atomic per block. The counter only grows: the k-th arrival of a call sees
-// old = base + k with base a multiple of the grid size, so the call's target is
-// base + gridDim.x. The block that completes the count writes the target into every
-// block's flag (one 128-byte line each, so the waiting blocks poll different lines
-// instead of all polling the counter); a block waits until its flag reaches the target.
-// Readers then load h with agent-coherent loads. Returns false (and sets bit 0 of
-// hdr[1]) if the wait exceeds the spin limit, so every wave exits.
+// relaxed atomic per block on the arrival counter. Every block read the call's epoch
+// before arriving; the block whose arrival completes the count (it has seen every other
+// arrival) writes epoch + 1 into every block's flag (one 128-byte line each, so the
+// waiting blocks poll different lines instead of one), resets the counter to zero and
+// stores epoch + 1 as the next call's epoch. A block waits until its flag reaches
+// epoch + 1. So every call starts with a zero counter whatever the previous call's grid
+// size was, and stale flags (at most the previous epoch) never release a wait. Readers
+// then load h with agent-coherent loads. Returns false (and sets bit 0 of hdr[1]) if the
+// wait exceeds the spin limit, so every wave exits.
 __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned long long G = gridDim.x;
-    const unsigned long long old =
-        __hip_atomic_fetch_add(a.barrier, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long target = (old / G + 1) * G;
-    sm.target = target;
-    sm.last = old + 1 == target;
+    const unsigned old = __hip_atomic_fetch_add(a.barrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = old + 1 == gridDim.x;
     sm.ok = 1;
   }
   __syncthreads();
-  const unsigned long long target = sm.target;
+  const unsigned long long target = sm.epoch + 1;
   if (sm.last) {
     for (unsigned b = threadIdx.x; b < gridDim.x; b += kDecThreads)
       __hip_atomic_store(a.flags + (size_t)b * 16, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(a.barrier, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.epoch, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return true;
   }
   if (threadIdx.x == 0) {
@@ -495,7 +500,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   if (MODE != 0) down_load<CHD, Q8>(a, sm, 0, row, l8, d);  // in flight during phase 1 and the wait
   if (MODE != 1) phase1<CHG>(a, sm, p1);
   if (MODE == 0) return;
-  if (MODE == 2 && !grid_barrier(a, sm)) return;
+  if (MODE == 2 && !grid_barrier(a, sm)) {
+    // the wait gave up: this block's output rows are written as NaN, never left stale
+    if (tid < kRowsPerBlock * a.T) {
+      const int r = blockIdx.x * kRowsPerBlock + (tid & 7), t = tid >> 3;
+      if (r < a.H) {
+        if (a.out_dtype == 0) reinterpret_cast<float*>(a.out)[(size_t)t * a.H + r] = __builtin_nanf("");
+        else reinterpret_cast<uint16_t*>(a.out)[(size_t)t * a.H + r] = 0x7FC0;
+      }
+    }
+    return;
+  }
   if (a.h_in_lds) {
     // agent-coherent 128-bit loads (cache policy sc1) of h into LDS. Above 4 pieces per
     // thread, kCopyBatch loads are in flight per thread before their LDS stores (one or
@@ -615,7 +630,8 @@ hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const We
   a.gate = gate; a.up = up; a.down = down;
   a.ids = ids; a.w = w; a.h = h; a.out = out; a.out_dtype = out_dtype;
   a.hdr = hdr;
-  a.barrier = reinterpret_cast<unsigned long long*>(hdr + 4);
+  a.barrier = reinterpret_cast<unsigned*>(hdr + 4);
+  a.epoch = reinterpret_cast<unsigned long long*>(hdr + 6);
   a.flags = flags;
   a.spin_limit = 1 << 22;
   a.h_in_lds = 0;

@@ -54,11 +54,13 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, 
 // decode.hip
 constexpr int kDecodeMaxT = 8;
 constexpr int kDecodeMaxPairs = 64;
-constexpr int kDecodeMaxTH = 40960;  // T * H: the bf16 activations of a block live in LDS
+constexpr int kDecodeMaxTH = 40960;
+constexpr int kDecodeMaxH = 8192;  // T * H: the bf16 activations of a block live in LDS
 // stage 0: gate/up + SwiGLU; 1: down + combine; 2: both in one persistent launch (falls
 // back to 0 then 1 when the grid cannot be co-resident). hdr: [0] dropped pairs,
-// [1] error flags, [2] grid-barrier spin limit when positive, [4..5] the grid-barrier counter; flags: decode_flag_bytes(H) of
-// per-block release flags (counter and flags zero before first use).
+// [1] error flags, [2] grid-barrier spin-limit override, [4] the grid-barrier arrival
+// counter, [6..7] its epoch; flags: per-block release flags (counter, error word,
+// override and flags zero before first use; any epoch).
 constexpr int kDecodeRowsPerBlock = 8;
 inline size_t decode_flag_bytes(int H) { return (size_t)((H + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock) * 128; }
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,
