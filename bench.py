@@ -365,10 +365,13 @@ def main():
             dec[f"t{d['T']}"] = d
             log(f"decode T={d['T']}: {d['us']:.2f} us/layer, {d['gbs']:.0f} GB/s (U={d['unique_experts']}), "
                 f"gate/up {d['us_gateup']:.2f} us, down {d['us_down']:.2f} us")
-    w4 = None
+    w4 = w4i = None
     if args.only in ("all", "w4a8"):
         w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2)
         log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
+        w4i = bench_prefill(layers, 4, "w4a8", max(3, args.steps // 8), 1)
+        log(f"w4a8 int8 MFMA 32768: {w4i['ms']:.3f} ms/step, {w4i['tokens_per_s']:.0f} tok/s, "
+            f"stages {w4i['stages_ms']}")
     rt = None
     if args.only in ("all", "router"):
         rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
@@ -457,6 +460,16 @@ def main():
                                                           / 1e12 / PEAK_FP16_TFLOPS, 4),
                           "frac_of_int8_peak_step": round((w4["gu_flops"] + w4["dn_flops"]) / (w4["ms"] * 1e-3)
                                                           / 1e12 / PEAK_INT8_TOPS, 4)}
+    if w4i is not None:
+        result["w4a8_int8_mfma"] = {
+            "workload": "32768 tokens, the same int8 activations on int8 matrix cores (weights as exact int8 "
+                        "2*e2m1, fp32 rescale by e4m3/2 per 16-input group: VALU-bound)",
+            "tokens/s": round(w4i["tokens_per_s"], 1), "ms_per_step": round(w4i["ms"], 4),
+            "stage_ms": [round(v, 4) for v in w4i["stages_ms"]],
+            "frac_of_int8_peak_step": round((w4i["gu_flops"] + w4i["dn_flops"]) / (w4i["ms"] * 1e-3) / 1e12
+                                            / PEAK_INT8_TOPS, 4),
+            "frac_of_fp16_peak_step": round((w4i["gu_flops"] + w4i["dn_flops"]) / (w4i["ms"] * 1e-3) / 1e12
+                                            / PEAK_FP16_TFLOPS, 4)}
     if rt is not None:
         result["router"] = {"workload": "logits of 512 experts (bf16 router matrix, hidden 2048) on bf16 activations, "
                                         "top-8, softmax over the selected logits; us per call in a hipGraph of 48 "

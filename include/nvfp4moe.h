@@ -79,7 +79,10 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
  *                       (x is staged in fp16 with a power-of-two exponent per row, h is
  *                       kept in fp16 with one per block; see nvfp4_moe_prefill).
  *   NVFP4_ACT_W4A8      x and h quantized per row to int8 (scale absmax/127); the GEMMs
- *                       run on int8 matrix cores with an FP32 rescale per 16-input group.
+ *                       run on int8 matrix cores (weights as exact int8 2*e2m1) with an
+ *                       FP32 rescale by e4m3/2 per 16-input group (per 32 for a Q8_0
+ *                       down projection): bound by that VALU rescale, slower than
+ *                       NVFP4_ACT_W4A8_F16, which gives the same result to FP32 rounding.
  *   NVFP4_ACT_W4A8_F16  the same int8 activations and the same result, computed on fp16
  *                       matrix cores (int8 values are exact in fp16; x and h are stored
  *                       as 1-byte codes and widened while staged). */
@@ -210,8 +213,8 @@ int nvfp4_moe_decode_noalloc(const void* x, int32_t x_dtype, int32_t T, int32_t 
  * operand of the path that is not exact.
  * Errors: EINVAL (null pointers, shapes that disagree, unknown act or format,
  * out_dtype F16); EUNSUPPORTED for H not a multiple of 256, I not a multiple of 128 or
- * above 8192, E > 8192, x_dtype other than BF16, a Q8_0 gate or up projection, act W4A8
- * (the int8 matrix-core variant is not in this build); EWORKSPACE. */
+ * above 8192, E > 8192, x_dtype other than BF16, a Q8_0 gate or up projection;
+ * EWORKSPACE. */
 size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                         int32_t act);
 int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,

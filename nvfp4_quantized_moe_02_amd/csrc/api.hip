@@ -345,7 +345,6 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
-  if (act == NVFP4_ACT_W4A8) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
   if ((H % 256) != 0 || (I % 128) != 0 || I > 8192 || E > kMaxExperts) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * topk > (int64_t)1 << 30) return NVFP4_EUNSUPPORTED;
@@ -377,14 +376,22 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
         if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, static_cast<int8_t*>(xa), xscale, s);
       }
     } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
-      e = launch_gemm_gateup(mode, xa, xscale, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
-                             to_args(gate), to_args(up), at<void>(ws, l.h), hexp, s);
+      if (act == NVFP4_ACT_W4A8)
+        e = launch_gemm_gateup_i8(static_cast<const int8_t*>(xa), xscale, sorted, offsets, tiles, hdr + 1,
+                                  l.r.max_tiles, topk, H, I, to_args(gate), to_args(up), at<float>(ws, l.h), s);
+      else
+        e = launch_gemm_gateup(mode, xa, xscale, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H,
+                               I, to_args(gate), to_args(up), at<void>(ws, l.h), hexp, s);
       if (e == hipSuccess && mode == 1)
         e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<int8_t>(ws, l.qh), sh, s);
     } else if (stage == 2) {  // down, scaled by gamma_d and the router weight, per pair
       const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh);
-      e = launch_gemm_down(mode, hA, sh, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
-                           to_args(down), topk_weights, y, s);
+      if (act == NVFP4_ACT_W4A8)
+        e = launch_gemm_down_i8(static_cast<const int8_t*>(hA), sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles,
+                                topk, H, I, to_args(down), topk_weights, y, s);
+      else
+        e = launch_gemm_down(mode, hA, sh, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+                             to_args(down), topk_weights, y, s);
     } else {  // top-k combine in slot order, one rounding to the output dtype
       e = launch_combine(y, at<int32_t>(ws, l.r.inv), T, topk, H, out, out_dtype, s);
     }

@@ -22,6 +22,16 @@ struct TileDesc {
   int m0;
 };
 
+// A prefill GEMM block's work item: expert e, its rows [m0, m0 + rows) in sorted order
+// (sorted positions base + m0 ...), N block nb.
+struct TileCtx {
+  int e, m0, rows, base, nb;
+};
+
+// SiLU for the prefill path's h: exp and reciprocal from the hardware approximations
+// (about 1 ulp each).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 // elementwise.hip
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* global, int64_t rows,
                           int K, int out_dtype, void* out, hipStream_t st);
@@ -87,6 +97,16 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
                               hipStream_t st);
 // gate/up blocks along I (the number of h exponents per sorted pair in act 0)
 int gateup_blocks(int I);
+// prefill_i8.hip: the W4A8 GEMMs on int8 matrix cores (int8 activations with fp32 row
+// scales; NVFP4 weights as exact int8 2*e2m1 with an fp32 rescale per 16-input group)
+hipError_t launch_gemm_gateup_i8(const int8_t* a, const float* a_scale, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count,
+                                 int max_tiles, int topk, int H, int I, const WeightArgs& gate, const WeightArgs& up,
+                                 float* h, hipStream_t st);
+hipError_t launch_gemm_down_i8(const int8_t* h, const float* h_scale, const int32_t* sorted_pairs,
+                               const int32_t* offsets, const TileDesc* tiles, const int32_t* tile_count, int max_tiles,
+                               int topk, int H, int I, const WeightArgs& down, const float* w, float* y,
+                               hipStream_t st);
 // y[pos][n] = gamma_down * w[pair] * (h[pos] . Wdown[n]) for every sorted position pos
 hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* hexp,
                             const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,

@@ -92,13 +92,6 @@ __device__ __forceinline__ uint32_t f16_pow2_neg(int d) {
   return d <= 14 ? (uint32_t)(15 - d) << 10 : d <= 24 ? 1u << (24 - d) : 0u;
 }
 
-// SiLU for the fp16/fp32 h of the prefill path: exp and reciprocal from the hardware
-// approximations (about 1 ulp each).
-__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-
-struct TileCtx {
-  int e, m0, rows, base, nb;
-};
 
 // Scale bytes are loaded KQ K-blocks at a time (4 * KQ bytes of one column's scale row
 // per lane, 16-byte aligned for KQ = 4 when K is a multiple of 256, 8-byte for KQ = 2);

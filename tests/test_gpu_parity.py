@@ -276,7 +276,7 @@ def test_prefill_small_full(out_dtype):
 
 
 @pytest.mark.parametrize("H,I", [(512, 256), (768, 256), (512, 384), (256, 128)])
-@pytest.mark.parametrize("act", ["bf16", "w4a8_f16"])
+@pytest.mark.parametrize("act", ["bf16", "w4a8_f16", "w4a8"])
 def test_prefill_kernel_shapes(H, I, act):
     """Every GEMM variant the launchers pick: 8 or 4 waves for gate/up (I % 256) and for
     down (H % 512), scale groups of 4 or 2 K-blocks for down (I % 256)."""
@@ -326,9 +326,11 @@ def test_prefill_tiny_batches():
             assert max_row_rel_l2(y.cpu().numpy(), ref) < 5e-4
 
 
-def test_w4a8_f16_small():
-    _, _, stats = _prefill_small("w4a8_f16", seed=23, out_dtype=torch.float32)
-    print(f"w4a8 (fp16 MMA) small: {stats}")
+@pytest.mark.parametrize("act", ["w4a8_f16", "w4a8"])
+def test_w4a8_small(act):
+    """Both W4A8 variants (fp16 and int8 matrix cores), strict checks, 600 tokens."""
+    _, _, stats = _prefill_small(act, seed=23, out_dtype=torch.float32)
+    print(f"{act} small: {stats}")
 
 
 @pytest.fixture(scope="module")
@@ -357,19 +359,20 @@ def test_prefill_c3_full_size_cover(full_layer_c3):
     assert torch.isfinite(y.float()).all()
 
 
-def test_w4a8_f16_c4_full_size_cover(full_layer_c3):
-    """32768 tokens, W4A8 (same layer shape, the W4A8 workload's routing and activations):
-    the strict checks on >= 1024 token rows covering every routed expert and its last tile."""
+@pytest.mark.parametrize("act", ["w4a8_f16", "w4a8"])
+def test_w4a8_c4_full_size_cover(full_layer_c3, act):
+    """32768 tokens, W4A8 on fp16 and on int8 matrix cores (same layer shape, the W4A8
+    workload's routing and activations): the strict checks on >= 1024 token rows covering
+    every routed expert and its last tile."""
     lay, dl = full_layer_c3
     wl = W.draw_workload(4)
-    ws = torch.zeros(nv.prefill_workspace_size(wl.T, lay.H, lay.I, lay.E, 8, "w4a8_f16"), dtype=torch.uint8,
-                     device=DEV)
+    ws = torch.zeros(nv.prefill_workspace_size(wl.T, lay.H, lay.I, lay.E, 8, act), dtype=torch.uint8, device=DEV)
     y = nv.moe_prefill(bf16_dev(wl.x), dl, torch.from_numpy(wl.ids).to(DEV), torch.from_numpy(wl.w).to(DEV),
-                       act="w4a8_f16", ws=ws)
+                       act=act, ws=ws)
     rows = cover_rows(wl.ids, lay.E, n=1024, seed=2)
     got = bf16_out_to_f64(y[torch.from_numpy(rows).to(DEV)])
-    stats = w4a8_strict(wl.x, lay, wl.ids, wl.w, rows, ws, got)
-    print(f"w4a8 32768 tokens, {len(rows)} rows: {stats}")
+    stats = w4a8_strict(wl.x, lay, wl.ids, wl.w, rows, ws, got, act=act)
+    print(f"{act} 32768 tokens, {len(rows)} rows: {stats}")
     assert torch.isfinite(y.float()).all()
 
 

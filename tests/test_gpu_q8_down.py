@@ -66,8 +66,9 @@ def test_prefill_q8_down_shapes(H, I):
 def test_prefill_q8_down_tensor_scale_and_w4a8():
     got, ref, _ = _small(33, 8, 512, 256, 400, 8, gamma=True)
     assert max_row_rel_l2(got, ref) < 1e-3
-    _, _, stats = _small(35, 8, 512, 256, 400, 8, act="w4a8_f16")
-    print(f"w4a8 (fp16 MMA) with Q8_0 down: {stats}")
+    for act in ("w4a8_f16", "w4a8"):
+        _, _, stats = _small(35, 8, 512, 256, 400, 8, act=act)
+        print(f"{act} with Q8_0 down: {stats}")
 
 
 def test_prefill_q8_down_equals_nvfp4_down_bitwise():
