@@ -11,14 +11,19 @@
 //
 // A (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into registers and
 // stored to a 2-stage LDS ring at the top of the iteration that uses it.
-// Each LDS row holds 64 inputs (8 slots of 16 bytes); slot c of row r holds chunk
-// c ^ (r & 7), so the 32 rows of an MFMA fragment read hit 8 distinct slots (no bank
-// conflicts). Rows are gathered by token for gate/up and contiguous for down.
+// Each LDS row holds 64 inputs (8 slots of 16 bytes); chunk c of row r sits in slot
+// c ^ ((r >> 1) & 7). gfx950's LDS serves a 128-bit read 16 lanes (256 bytes, all 64
+// banks) per cycle, and the 16 rows of such a lane group then cover every bank once: the
+// row's parity picks the 128-byte half, the slot the 16 bytes within it (with the slot
+// keyed on r & 7, rows r and r + 8 collided: measured 38% of LDS-active cycles in bank
+// conflicts, none with this key). Rows are gathered by token for gate/up and contiguous
+// for down.
 //
 // B (NVFP4 weights): the block stages its weight rows' codes GK K-blocks at a
 // time with coalesced loads (consecutive threads read one row's GK*32 contiguous bytes)
-// one group ahead in registers, stores each group to an XOR-swizzled LDS tile, and every
-// lane reads its fragment's 16 code bytes per K-block from there. Each lane loads its
+// one group ahead in registers, stores each group to one of two XOR-swizzled LDS tiles
+// (alternating, so a group is stored beside A before the K-block's one barrier), and
+// every lane reads its fragment's 16 code bytes per K-block from there. Each lane loads its
 // column's scale bytes for four K-blocks at once. The unpack to fp16 is exact: E2M1 codes
 // and the E4M3 scale both convert exactly to fp16, and their product (at most 5
 // significant bits) is exact in one packed fp16 multiply; each weight is decoded once per
@@ -114,7 +119,9 @@ struct BTile {
   static constexpr int NCB = WPB * 64;
   static constexpr int ROWB = GK * 32;                  // code bytes of one row per group
   static constexpr int CPR = GK * 2;                    // 16-byte chunks per row per group
-  static constexpr int SHIFT = GK == 2 ? 1 : 0;         // swizzle: chunk ^ ((row >> SHIFT) & (CPR-1))
+  // swizzle: chunk ^ ((row >> SHIFT) & (CPR-1)); a 16-lane fragment read (16 rows) then
+  // covers all 64 banks once (row & (256/ROWB - 1) picks the bank block, the key the slot)
+  static constexpr int SHIFT = GK == 2 ? 2 : 3;
   static constexpr int BYTES = NCB * ROWB;
   static constexpr int CH = BYTES / (WPB * 64 * 16);    // 16-byte chunks staged per thread
   static constexpr int RPT = WPB * 64 / CPR;            // rows covered by one staging round
@@ -156,7 +163,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
 #pragma unroll
   for (int i = 0; i < NA; ++i)
     asrc[i] = reinterpret_cast<const char*>(A) + ((size_t)s_src[arow + RPR * i] * K + achunk * 8) * ES;
-  const int aslot = ((achunk ^ (arow & 7)) << 4);
+  const int aslot = ((achunk ^ ((arow >> 1) & 7)) << 4);
 
   // B codes: the block's NCB weight rows, GK K-blocks (GK*32 bytes of each row) per
   // group. Thread t stages chunks j*(WPB*64) + t of the group tile, i.e. chunk t % CPR of
@@ -261,16 +268,18 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     char* st = lds + R * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = a_fp16(aq[R][i], kb, i);
-    // A(kb) visible to all waves. Stage R was last read in iteration kb-2, and every wave
-    // finished those reads before passing the barrier of iteration kb-1.
-    __syncthreads();
+    // At a group start the staged B group goes to tile (group & 1): that tile was last
+    // read in the group before the previous one, which every wave finished before passing
+    // the previous group's first barrier.
     if constexpr (Q % GKB == 0) {
+      char* bt = btiles + ((kb / GKB) & 1) * BT::BYTES;
 #pragma unroll
-      for (int j = 0; j < BT::CH; ++j)
-        *reinterpret_cast<uint4*>(btiles + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
-      __syncthreads();
+      for (int j = 0; j < BT::CH; ++j) *reinterpret_cast<uint4*>(bt + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
     }
-    const char* btile = btiles;
+    // A(kb) (and the B group) visible to all waves. Stage R was last read in iteration
+    // kb-2, and every wave finished those reads before passing the barrier of iteration kb-1.
+    __syncthreads();
+    const char* btile = btiles + ((kb / GKB) & 1) * BT::BYTES;
     // The next B group (at a group start) and A(kb+2) are loaded spread over the MFMAs of
     // this K-block: a burst of loads from every wave right after the barrier queues in the
     // address unit and holds back each wave's first MFMAs.
@@ -323,7 +332,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     auto read_a = [&](int idx) -> f16x8_t {
       const int s = idx / NRB, rb = idx % NRB;
       const int row = rb * 32 + l32, chunk = half * 4 + s;
-      return *reinterpret_cast<const f16x8_t*>(st + row * 128 + ((chunk ^ (row & 7)) << 4));
+      return *reinterpret_cast<const f16x8_t*>(st + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4));
     };
 #pragma unroll
     for (int i = 0; i < LA; ++i) ring[i] = read_a(i);
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w, void* __restrict__ out, int ldo,
     int32_t* __restrict__ hexp_out) {
   // A stages and the B tile; the down epilogue reuses them (32 rows x WPB*64 fp32)
-  constexpr int kMain = NSTAGE * STAGE_BYTES + BTile<WPB, Q8 ? 2 : GK>::BYTES;
+  constexpr int kMain = NSTAGE * STAGE_BYTES + 2 * BTile<WPB, Q8 ? 2 : GK>::BYTES;
   constexpr int kEpi = GATEUP ? 0 : 32 * WPB * 64 * 4;
   constexpr int kLds = kMain > kEpi ? kMain : kEpi;
   constexpr bool kHd = !GATEUP && AM == A_F16;    // down rescales A per gate/up block
