@@ -46,6 +46,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router", "host"], default="all")
+    ap.add_argument("--decode-tokens", type=int, choices=[0, 1, 4], default=0,
+                    help="decode leg: only the 1-token or only the 4-token workload (0: both)")
+    ap.add_argument("--w4a8-variant", choices=["both", "f16", "int8"], default="both",
+                    help="W4A8 leg: fp16 matrix cores, int8 matrix cores, or both")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the prefill steps and the decode calls as plain launch loops instead of "
+                         "hipGraph replays (for counter runs)")
+    ap.add_argument("--no-stage-times", action="store_true",
+                    help="skip the per-stage event pass, so a kernel trace of the run holds the timed steps "
+                         "(and the warm-up before them) only")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print a markdown table of a rocprofv3 kernel trace: per kernel, the last --take "
+                         "dispatches (the timed steps) and nothing else runs")
+    ap.add_argument("--take", type=int, default=0, help="dispatches per kernel kept by --summarize-trace")
+    ap.add_argument("--match", default="nvfp4::",
+                    help="--summarize-trace keeps kernels whose name contains this (default: the library's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run device-to-device copies of 1 GiB (the plain copy kernel whose HBM "
                          "counter readings scale the GEMM's FETCH_SIZE / WRITE_SIZE)")
@@ -79,9 +95,33 @@ def stage_times(calls, steps, nstages):
 
 
 def timed_steps(calls, steps, warmup):
+    """ms per step: `warmup` eager calls, then the `steps` calls (rotating over the layer
+    copies) captured once in a hipGraph; one untimed replay, then one timed replay."""
     import torch
     for i in range(warmup):
         calls[i % len(calls)].run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            calls[i % len(calls)].run()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g
+    return ms
+
+
+def eager_steps(calls, steps):
+    """ms per step of the same calls as a plain launch loop (no graph)."""
+    import torch
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -93,7 +133,7 @@ def timed_steps(calls, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def bench_prefill(layers, index, act, steps, warmup):
+def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=False):
     import numpy as np
     import torch
     import nvfp4_quantized_moe_02_amd as nv
@@ -107,21 +147,31 @@ def bench_prefill(layers, index, act, steps, warmup):
     out = torch.empty((wl.T, L0.H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(nv.prefill_workspace_size(wl.T, L0.H, L0.I, L0.E, 8, act), dtype=torch.uint8, device=dev)
     calls = [nv.PreparedCall("prefill", x, L, ids, w, out, ws, act=act) for L in layers]
-    ms = timed_steps(calls, steps, warmup)
-    st = stage_times(calls, steps, 4)
+    if eager:
+        for i in range(warmup):
+            calls[i % len(calls)].run()
+        ms = eager_steps(calls, steps)
+    else:
+        ms = timed_steps(calls, steps, warmup)
+    if stage_pass:
+        st = stage_times(calls, steps, 4)
+        ms_eager = eager_steps(calls, steps)
+    else:
+        st, ms_eager = [float("nan")] * 4, float("nan")
     P = wl.T * 8
     H, I = L0.H, L0.I
     gu_flops = 2.0 * P * (2 * I) * H
     dn_flops = 2.0 * P * H * I
     counts = np.bincount(wl.ids.reshape(-1), minlength=L0.E)
     tiles = int(np.sum((counts + 127) // 128))
-    return dict(T=wl.T, ms=ms, stages_ms=st, gu_flops=gu_flops, dn_flops=dn_flops,
+    return dict(T=wl.T, ms=ms, ms_eager=ms_eager, stages_ms=st, gu_flops=gu_flops, dn_flops=dn_flops,
                 padded_frac=P / (tiles * 128.0), tokens_per_s=wl.T / (ms / 1e3))
 
 
-def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4):
-    """hipGraph of one call per layer (48 layers), replayed `rounds` times. down_bytes:
-    bytes of one expert's down projection (NVFP4 or Q8_0)."""
+def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4, eager=False):
+    """hipGraph of one call per layer (48 layers), replayed `rounds` times (eager: the same
+    calls as a plain launch loop, for counter runs). down_bytes: bytes of one expert's down
+    projection (NVFP4 or Q8_0)."""
     import numpy as np
     import torch
     import nvfp4_quantized_moe_02_amd as nv
@@ -140,6 +190,17 @@ def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4):
         for c in calls[:4]:
             fn(c)
         torch.cuda.synchronize()
+        if eager:
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(rounds):
+                for c in calls:
+                    fn(c)
+            t1.record()
+            torch.cuda.synchronize()
+            res[name] = t0.elapsed_time(t1) * 1e3 / (rounds * len(calls))
+            continue
         s = torch.cuda.Stream()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
@@ -270,7 +331,7 @@ def bench_host(reps=24):
 
 # Kernel sources whose hash a traffic profile records: counters taken on other sources
 # no longer describe the kernel and are not reported.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gateup_t8192_zipf_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_decode_hbm_traffic.md")
 TRAFFIC_SOURCES = ["nvfp4_quantized_moe_02_amd/csrc/prefill.hip", "nvfp4_quantized_moe_02_amd/csrc/common.h",
                    "nvfp4_quantized_moe_02_amd/csrc/kernels.h"]
 
@@ -311,22 +372,88 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 4, "source_hash": source_hash()}), flush=True)
 
 
+def summarize_trace(path, take, match):
+    """Markdown table of a rocprofv3 kernel trace (`*_kernel_trace.csv`): for each kernel
+    name containing `match`, the last `take` dispatches in start order (all of them when
+    take is 0), with their average, minimum and maximum duration in microseconds."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if match not in r["Kernel_Name"]:
+                continue
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            rows.setdefault(r["Kernel_Name"], []).append((t0, t1))
+    out = []
+    for name, d in rows.items():
+        d.sort()
+        kept = d[-take:] if take else d
+        us = [(b - a) / 1e3 for a, b in kept]
+        out.append((sum(us), name, len(d), len(kept), sum(us) / len(us), min(us), max(us)))
+    out.sort(reverse=True)
+    tot = sum(o[0] for o in out)
+    if not out:
+        return
+    print("| kernel | dispatches in trace | kept | avg us | min us | max us | % of kept time |")
+    print("|---|---|---|---|---|---|---|")
+    for t, name, n, k, avg, lo, hi in out:
+        print(f"| `{name}` | {n} | {k} | {avg:.2f} | {lo:.2f} | {hi:.2f} | {100 * t / tot:.1f} |")
+
+
+def cpu_description():
+    """The host CPU's model (lscpu's "Model name"), the CPUs it reports (nproc) and the
+    CPUs this process may run on."""
+    import subprocess
+    model = None
+    try:
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout.splitlines():
+            if line.strip().startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, timeout=10).stdout.strip())
+    except (OSError, subprocess.SubprocessError, ValueError):
+        nproc = None
+    return {"lscpu_model": model or cpu_model(), "nproc": nproc, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(n_tokens):
+    """The float64 oracle on bounded samples: the 8192-token bf16 prefill workload on all
+    BLAS threads (the reported value) and on one thread, and the 32768-token W4A8 workload
+    on all threads."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle as O
     import workloads as W
     lay = W.draw_layer(W.config_seed(3))
     wl = W.draw_workload(3)
     x = O.bf16_to_f64(wl.x)
-    rows = np.arange(n_tokens)
-    t = time.perf_counter()
-    O.moe_grouped(x, lay, wl.ids, wl.w, rows=rows)
-    dt = time.perf_counter() - t
+
+    def run(fn, n):
+        t = time.perf_counter()
+        fn(np.arange(n))
+        return time.perf_counter() - t
+
+    dt = run(lambda rows: O.moe_grouped(x, lay, wl.ids, wl.w, rows=rows), n_tokens)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    n1 = max(16, n_tokens // 8)
+    with threadpool_limits(limits=1):
+        dt1 = run(lambda rows: O.moe_grouped(x, lay, wl.ids, wl.w, rows=rows), n1)
+    w4 = W.draw_workload(4)
+    n4 = max(16, n_tokens // 2)
+    dt4 = run(lambda rows: O.moe_w4a8(w4.x, lay, w4.ids, w4.w, rows=rows), n4)
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the 8192-token prefill workload (all {len(np.unique(wl.ids[:n_tokens]))} "
-                      f"experts they route to), float64 numpy oracle, {dt:.1f} s"}
+            "sample": f"first {n_tokens} tokens of the 8192-token prefill workload (all "
+                      f"{len(np.unique(wl.ids[:n_tokens]))} experts they route to), float64 numpy oracle, "
+                      f"{dt:.1f} s on {threads} BLAS threads",
+            "one_core": {"value": round(n1 / dt1, 3), "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {n1} tokens of the same workload, one BLAS thread, {dt1:.1f} s"},
+            "w4a8_t32768": {"value": round(n4 / dt4, 3), "unit": "tokens/s", "cores": threads,
+                            "sample": f"first {n4} tokens of the 32768-token W4A8 workload (int8 x and h per "
+                                      f"row, float64 oracle), {dt4:.1f} s"},
+            "host": cpu_description()}
 
 
 def main():
@@ -336,6 +463,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.take, args.match)
         return
     import torch
     import nvfp4_quantized_moe_02_amd as nv
@@ -356,22 +486,27 @@ def main():
     result = {}
     pre = None
     if args.only in ("all", "prefill"):
-        pre = bench_prefill(layers, 3, "bf16", args.steps, args.warmup)
-        log(f"prefill 8192: {pre['ms']:.3f} ms/step, {pre['tokens_per_s']:.0f} tok/s, stages {pre['stages_ms']}")
+        pre = bench_prefill(layers, 3, "bf16", args.steps, args.warmup, not args.no_stage_times, args.eager)
+        log(f"prefill 8192: {pre['ms']:.3f} ms/step (graph; eager loop {pre['ms_eager']:.3f}), "
+            f"{pre['tokens_per_s']:.0f} tok/s, stages {pre['stages_ms']}")
     dec = {}
     if args.only in ("all", "decode"):
         for idx in (1, 2):
-            d = bench_decode(layers, idx, args.decode_rounds)
+            if args.decode_tokens and W.draw_workload(idx).T != args.decode_tokens:
+                continue
+            d = bench_decode(layers, idx, args.decode_rounds, eager=args.eager)
             dec[f"t{d['T']}"] = d
             log(f"decode T={d['T']}: {d['us']:.2f} us/layer, {d['gbs']:.0f} GB/s (U={d['unique_experts']}), "
                 f"gate/up {d['us_gateup']:.2f} us, down {d['us_down']:.2f} us")
     w4 = w4i = None
     if args.only in ("all", "w4a8"):
-        w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2)
-        log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
-        w4i = bench_prefill(layers, 4, "w4a8", max(3, args.steps // 8), 1)
-        log(f"w4a8 int8 MFMA 32768: {w4i['ms']:.3f} ms/step, {w4i['tokens_per_s']:.0f} tok/s, "
-            f"stages {w4i['stages_ms']}")
+        if args.w4a8_variant in ("both", "f16"):
+            w4 = bench_prefill(layers, 4, "w4a8_f16", max(4, args.steps // 4), 2, not args.no_stage_times)
+            log(f"w4a8 32768: {w4['ms']:.3f} ms/step, {w4['tokens_per_s']:.0f} tok/s, stages {w4['stages_ms']}")
+        if args.w4a8_variant in ("both", "int8"):
+            w4i = bench_prefill(layers, 4, "w4a8", max(3, args.steps // 8), 1, not args.no_stage_times)
+            log(f"w4a8 int8 MFMA 32768: {w4i['ms']:.3f} ms/step, {w4i['tokens_per_s']:.0f} tok/s, "
+                f"stages {w4i['stages_ms']}")
     rt = None
     if args.only in ("all", "router"):
         rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
@@ -403,7 +538,7 @@ def main():
         cpu = cpu_baseline(args.cpu_sample_tokens)
         log(f"cpu oracle: {cpu}")
 
-    if pre is not None:
+    if pre is not None and not args.no_stage_times:
         gu_ms = pre["stages_ms"][1]
         dn_ms = pre["stages_ms"][2]
         achieved = pre["gu_flops"] / (gu_ms * 1e-3) / 1e12
@@ -416,6 +551,10 @@ def main():
             "steps": args.steps,
             "warmup": args.warmup,
             "ms_per_step": round(pre["ms"], 4),
+            "ms_per_step_eager_loop": round(pre["ms_eager"], 4),
+            "timing": ("plain launch loop" if args.eager else
+                       "steps captured in one hipGraph and replayed once (after one untimed replay); "
+                       "ms_per_step_eager_loop: the same calls as a plain launch loop"),
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,

@@ -395,8 +395,9 @@ def test_prefill_stages_equal_full_call():
     c = nv.PreparedCall("prefill", x, dl, ids, w, out_st, ws)
     for s in range(4):
         c.stage(s)
-    a, b = out_full.cpu().numpy(), out_st.cpu().numpy()
-    assert max_row_rel_l2(b, a) < 1e-6  # fp32 atomic-add order only
+    # every output row is computed by one fixed sequence of operations (the combine sums a
+    # token's slots in slot order), so the staged launches give the same bits
+    assert torch.equal(out_full, out_st)
 
 
 def test_decode_stages_equal_full_call():
@@ -430,18 +431,20 @@ def test_decode_barrier_timeout_is_reported():
     assert torch.equal(again, good)
 
 
-@pytest.mark.parametrize("kind", ["decode", "prefill"])
-def test_graph_replays_match_eager(kind):
+@pytest.mark.parametrize("kind,act", [("decode", "bf16"), ("prefill", "bf16"), ("prefill", "w4a8_f16"),
+                                      ("prefill", "w4a8")])
+def test_graph_replays_match_eager(kind, act):
     """Capture one call in a hipGraph; replay it several times with eager work and
-    synchronizations in between, and check every replay against the eager result."""
+    synchronizations in between, and check every replay against the eager result bit for
+    bit (the benchmark times prefill calls of every activation mode this way)."""
     T = 4 if kind == "decode" else 300
     lay, dl, x, ids, w = _small_problem(T=T)
     out = torch.empty((T, dl.H), dtype=torch.float32, device=DEV)
     if kind == "decode":
         ws = torch.zeros(nv.decode_workspace_size(T, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
     else:
-        ws = torch.empty(nv.prefill_workspace_size(T, dl.H, dl.I, dl.E, 8), dtype=torch.uint8, device=DEV)
-    call = nv.PreparedCall(kind, x, dl, ids, w, out, ws)
+        ws = torch.empty(nv.prefill_workspace_size(T, dl.H, dl.I, dl.E, 8, act), dtype=torch.uint8, device=DEV)
+    call = nv.PreparedCall(kind, x, dl, ids, w, out, ws, act=act)
     call.run()
     torch.cuda.synchronize()
     eager = out.clone()
@@ -460,9 +463,6 @@ def test_graph_replays_match_eager(kind):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        if kind == "decode":
-            assert torch.equal(out, eager), f"replay {rep}"
-        else:
-            assert max_row_rel_l2(out.cpu().numpy(), eager.cpu().numpy()) < 1e-6, f"replay {rep}"
+        assert torch.equal(out, eager), f"replay {rep}"
         call.run()  # eager work between replays
         torch.cuda.synchronize()
