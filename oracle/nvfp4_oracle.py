@@ -50,6 +50,8 @@ Readings where the pages are silent (each listed in the design notes):
   * SwiGLU is SiLU(gate) * up with SiLU(z) = z / (1 + exp(-z)), no clamp;
   * router weights are used as given; duplicate ids are summed; ids outside
     [0, E) are dropped;
+  * the shared expert is an NVFP4 SwiGLU expert of the routed experts' shape,
+    applied to every token with weight 1 and added before the final rounding;
   * W4A8: per row s = fp32(absmax / 127) by an fp32 division, q = clamp(
     rint_even(fp32(x / s)), -127, 127), s = q = 0 for an all-zero row; the
     down projection's input h is quantized per (token, slot) row the same
@@ -273,6 +275,21 @@ def moe_grouped(x: np.ndarray, layer, ids: np.ndarray, w: np.ndarray,
     return out
 
 
+def moe_with_shared(x: np.ndarray, layer, shared, ids: np.ndarray, w: np.ndarray,
+                    rows: Optional[Sequence[int]] = None, ffn=None) -> np.ndarray:
+    """[S-NVFP4] (the shared expert) The routed sum plus the layer's shared expert:
+    out[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]) + FFN_shared(x[t]). Reading (the pages
+    give the shared expert no shape, format or weight): an NVFP4 SwiGLU expert of the
+    routed experts' shape, applied to every token with weight 1 before the one final
+    rounding. `shared` is a one-expert layer; ffn as in moe_grouped."""
+    T = ids.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    ffn = expert_ffn if ffn is None else ffn
+    out = moe_grouped(x, layer, ids, w, rows=rows, ffn=ffn)
+    out += ffn(x[rows], *_expert(shared, 0))
+    return out
+
+
 # ----------------------------------------------------------------- router
 def router_topk(x: np.ndarray, w_router_bf16_bits: np.ndarray, k: int):
     """[S-RT] x float64 [T][H] (exact values of the fp32 or bf16 inputs), Wr bf16 bits
@@ -348,6 +365,14 @@ def moe_w4a8(x_bf16_bits: np.ndarray, layer, ids, w, rows=None) -> np.ndarray:
     """W4A8 MoE: both expert GEMMs take per-row int8 activations."""
     xh = w4a8_activations(x_bf16_bits)
     return moe_grouped(xh, layer, ids, w, rows=rows, ffn=w4a8_expert_ffn)
+
+
+def moe_w4a8_with_shared(x_bf16_bits: np.ndarray, layer, shared, ids, w, rows=None) -> np.ndarray:
+    """W4A8 MoE with the shared expert (moe_with_shared's reading): the shared expert's
+    GEMMs take the same per-row int8 activations as the routed experts' (x per token, h
+    per (token, shared) row)."""
+    xh = w4a8_activations(x_bf16_bits)
+    return moe_with_shared(xh, layer, shared, ids, w, rows=rows, ffn=w4a8_expert_ffn)
 
 
 def w4a8_pair_hidden(x_bf16_bits: np.ndarray, layer, ids, rows=None):

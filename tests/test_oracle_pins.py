@@ -701,3 +701,97 @@ def test_router_bf16_weights_decode_and_negative_controls(monkeypatch):
     monkeypatch.setattr(O, "router_topk", reversed_ties)
     with pytest.raises(AssertionError):
         test_router_hand_example()
+
+
+# ------------------------------------------------------------------ shared expert
+def _append_expert(lay, sh):
+    """The routed layer with the shared expert's bytes appended as expert E."""
+    def cat(a, b):
+        return type(a)(np.concatenate([a.codes, b.codes]), np.concatenate([a.scales, b.scales]),
+                       np.concatenate([a.gamma, b.gamma]))
+    return W.Layer(cat(lay.gate, sh.gate), cat(lay.up, sh.up), cat(lay.down, sh.down), lay.E + 1, lay.H, lay.I)
+
+
+def _shared_case(seed=41, E=6, H=32, I=64, T=7, k=3, down_fmt="nvfp4"):
+    lay = W.draw_layer(seed, E=E, H=H, I=I, down_fmt=down_fmt)
+    sh = W.draw_shared_expert(seed, H=H, I=I, down_fmt=down_fmt)
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[1, 0] = -1   # dropped routed slot: the shared expert still applies
+    w = rng.random((T, k)).astype(np.float32)
+    return lay, sh, ids, w
+
+
+@pytest.mark.parametrize("down_fmt", ["nvfp4", "q8_0"])
+def test_shared_expert_is_an_always_routed_expert_of_weight_one(down_fmt):
+    """The reading, checked through the independent per-pair path: the shared expert gives
+    the same result as the same bytes appended as expert E, routed by every token as one
+    more slot with weight 1 (moe_pairwise dequantizes per pair; moe_with_shared groups)."""
+    lay, sh, ids, w = _shared_case(down_fmt=down_fmt)
+    T, k = ids.shape
+    x = np.random.default_rng(3).standard_normal((T, lay.H))
+    lay2 = _append_expert(lay, sh)
+    ids2 = np.hstack([ids, np.full((T, 1), lay.E, np.int32)])
+    w2 = np.hstack([w, np.ones((T, 1), np.float32)])
+    ref = O.moe_pairwise(x, lay2, ids2, w2)
+    got = O.moe_with_shared(x, lay, sh, ids, w)
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+    # the rows option selects rows of the same result
+    rows = np.array([5, 1, 2])
+    assert np.abs(O.moe_with_shared(x, lay, sh, ids, w, rows=rows) - ref[rows]).max() <= 1e-12 * np.abs(ref).max()
+    # the W4A8 variant quantizes the shared expert's x and h rows like a routed pair's
+    xb = W.draw_activations(3, T, lay.H)
+    a = O.moe_w4a8(xb, lay2, ids2, w2)
+    b = O.moe_w4a8_with_shared(xb, lay, sh, ids, w)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_shared_expert_identity_closed_form():
+    """H = I = 32, the shared expert's gate, up and down are identity matrices (E2M1 code 2
+    = 1.0 on the diagonal, E4M3 scale byte 0x38 = 1.0, global scales 1), the routed weights
+    zero: out = SiLU(x) * x elementwise, i.e. x^2 / (1 + exp(-x))."""
+    n = 32
+    nib = np.zeros((n, n), np.uint8)
+    nib[np.arange(n), np.arange(n)] = 2
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)[None]
+    eye = W.Proj(codes, np.full((1, n, n // 16), 0x38, np.uint8), np.ones(1, np.float32))
+    sh = W.Layer(eye, eye, eye, 1, n, n)
+    lay = W.draw_layer(43, E=3, H=n, I=n)
+    x = np.linspace(-6.0, 6.0, 2 * n).reshape(2, n)
+    ids = np.array([[0, 2], [1, 1]], np.int32)
+    w = np.zeros((2, 2), np.float32)
+    out = O.moe_with_shared(x, lay, sh, ids, w)
+    expect = x * x / (1.0 + np.exp(-x))
+    assert np.allclose(out, expect, rtol=1e-14, atol=1e-300)
+
+
+def test_shared_expert_negative_controls(monkeypatch):
+    """Plausible mistakes in the shared term fail the pins above: weighting it by a router
+    weight, adding it per routed slot, and dropping it for rows whose slots are dropped."""
+    real = O.nvfp4_oracle.moe_with_shared
+
+    def weighted_by_slot0(x, layer, shared, ids, w, rows=None, ffn=None):
+        rows_ = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
+        base = O.moe_grouped(x, layer, ids, w, rows=rows_, ffn=ffn)
+        return base + w[rows_, :1].astype(np.float64) * O.expert_ffn(x[rows_], *O.nvfp4_oracle._expert(shared, 0))
+
+    def once_per_slot(x, layer, shared, ids, w, rows=None, ffn=None):
+        rows_ = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
+        base = O.moe_grouped(x, layer, ids, w, rows=rows_, ffn=ffn)
+        n = (ids[rows_] >= 0).sum(1, keepdims=True)
+        return base + n * O.expert_ffn(x[rows_], *O.nvfp4_oracle._expert(shared, 0))
+
+    def routed_only(x, layer, shared, ids, w, rows=None, ffn=None):
+        return O.moe_grouped(x, layer, ids, w, rows=rows, ffn=ffn)
+
+    for bad in (weighted_by_slot0, once_per_slot, routed_only):
+        monkeypatch.setattr(O, "moe_with_shared", bad)
+        with pytest.raises(AssertionError):
+            test_shared_expert_is_an_always_routed_expert_of_weight_one("nvfp4")
+        monkeypatch.undo()
+    # routed_only also fails the closed form (zero routed weights leave only the shared term)
+    monkeypatch.setattr(O, "moe_with_shared", routed_only)
+    with pytest.raises(AssertionError):
+        test_shared_expert_identity_closed_form()
+    monkeypatch.undo()
+    assert O.moe_with_shared is real

@@ -69,6 +69,7 @@ GROUP = 16
 PROJ_TAG = {"gate": 1, "up": 2, "down": 3, "down_q8": 4, "router": 5}
 Q8_BLOCK = 32
 _TAG_X, _TAG_IDS, _TAG_W, _TAG_GAMMA, _TAG_OUTLIER, _TAG_PERM = 11, 12, 13, 14, 15, 16
+_TAG_SHARED = 17
 
 
 def config_seed(index: int) -> int:
@@ -197,6 +198,12 @@ def draw_layer(seed: int, E: int = EXPERTS, H: int = HIDDEN, I: int = INTER,
         lay.experts = ids
         lay.index = {int(e): i for i, e in enumerate(ids)}
     return lay
+
+
+def draw_shared_expert(seed: int, H: int = HIDDEN, I: int = INTER, down_fmt: str = "nvfp4") -> Layer:
+    """The layer's shared expert: a one-expert layer of the routed experts' shape, drawn from
+    streams of its own (the routed layer of the same seed is unrelated to it)."""
+    return draw_layer(int(_rng(seed, _TAG_SHARED).integers(1 << 31)), E=1, H=H, I=I, down_fmt=down_fmt)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
