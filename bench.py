@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--decode-rounds", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router", "host"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router", "host", "shared"],
+                    default="all")
     ap.add_argument("--decode-tokens", type=int, choices=[0, 1, 4], default=0,
                     help="decode leg: only the 1-token or only the 4-token workload (0: both)")
     ap.add_argument("--w4a8-variant", choices=["both", "f16", "int8"], default="both",
@@ -133,7 +134,9 @@ def eager_steps(calls, steps):
     return t0.elapsed_time(t1) / steps
 
 
-def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=False):
+def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=False, shared=None):
+    """shared: per-layer shared experts (one-expert layers, same count as layers), or None.
+    The shared-expert call has no staged form: no stage pass with it."""
     import numpy as np
     import torch
     import nvfp4_quantized_moe_02_amd as nv
@@ -145,8 +148,11 @@ def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=Fals
     w = torch.from_numpy(wl.w).to(dev)
     L0 = layers[0]
     out = torch.empty((wl.T, L0.H), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(nv.prefill_workspace_size(wl.T, L0.H, L0.I, L0.E, 8, act), dtype=torch.uint8, device=dev)
-    calls = [nv.PreparedCall("prefill", x, L, ids, w, out, ws, act=act) for L in layers]
+    ws = torch.empty(nv.prefill_workspace_size(wl.T, L0.H, L0.I, L0.E, 8, act, shared=shared is not None),
+                     dtype=torch.uint8, device=dev)
+    calls = [nv.PreparedCall("prefill", x, L, ids, w, out, ws, act=act,
+                             shared=None if shared is None else shared[i]) for i, L in enumerate(layers)]
+    stage_pass = stage_pass and shared is None
     if eager:
         for i in range(warmup):
             calls[i % len(calls)].run()
@@ -160,6 +166,8 @@ def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=Fals
         st, ms_eager = [float("nan")] * 4, float("nan")
     P = wl.T * 8
     H, I = L0.H, L0.I
+    if shared is not None:
+        P += wl.T  # the shared expert's pairs
     gu_flops = 2.0 * P * (2 * I) * H
     dn_flops = 2.0 * P * H * I
     counts = np.bincount(wl.ids.reshape(-1), minlength=L0.E)
@@ -168,7 +176,7 @@ def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=Fals
                 padded_frac=P / (tiles * 128.0), tokens_per_s=wl.T / (ms / 1e3))
 
 
-def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4, eager=False):
+def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4, eager=False, shared=None):
     """hipGraph of one call per layer (48 layers), replayed `rounds` times (eager: the same
     calls as a plain launch loop, for counter runs). down_bytes: bytes of one expert's down
     projection (NVFP4 or Q8_0)."""
@@ -183,10 +191,16 @@ def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4, eager=False
     w = torch.from_numpy(wl.w).to(dev)
     L0 = layers[0]
     out = torch.empty((wl.T, L0.H), dtype=torch.float32, device=dev)
-    ws = torch.zeros(nv.decode_workspace_size(wl.T, L0.H, L0.I, L0.E, 8), dtype=torch.uint8, device=dev)
-    calls = [nv.PreparedCall("decode", x, L, ids, w, out, ws) for L in layers]
+    ws = torch.zeros(nv.decode_workspace_size(wl.T, L0.H, L0.I, L0.E, 8, shared=shared is not None),
+                     dtype=torch.uint8, device=dev)
+    calls = [nv.PreparedCall("decode", x, L, ids, w, out, ws, shared=None if shared is None else shared[i])
+             for i, L in enumerate(layers)]
     res = {}
-    for name, fn in (("call", lambda c: c.run()), ("gateup", lambda c: c.stage(0)), ("down", lambda c: c.stage(1))):
+    legs = (("call", lambda c: c.run()), ("gateup", lambda c: c.stage(0)), ("down", lambda c: c.stage(1)))
+    if shared is not None:
+        legs = legs[:1]
+        res["gateup"] = res["down"] = float("nan")
+    for name, fn in legs:
         for c in calls[:4]:
             fn(c)
         torch.cuda.synchronize()
@@ -217,7 +231,7 @@ def bench_decode(layers, index, rounds, down_bytes=DOWN_BYTES_NVFP4, eager=False
         torch.cuda.synchronize()
         res[name] = t0.elapsed_time(t1) * 1e3 / (rounds * len(calls))  # us per launch
         del g
-    U = len(np.unique(wl.ids))
+    U = len(np.unique(wl.ids)) + (shared is not None)
     byt = U * (GATEUP_BYTES + down_bytes)
     return dict(T=wl.T, unique_experts=U, bytes=byt, us=res["call"], us_gateup=res["gateup"],
                 us_down=res["down"], gbs=byt / (res["call"] * 1e-6) / 1e9,
@@ -511,6 +525,23 @@ def main():
     if args.only in ("all", "router"):
         rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
         log(f"router: {rt}")
+    sh = None
+    if args.only in ("all", "shared"):
+        # the same layers with a shared expert each (a one-expert layer of the same shape)
+        sl = W.draw_shared_expert(W.config_seed(3))
+        sbase = nv.Layer.from_numpy(sl, "cuda")
+        shared = replicate(sbase, args.layers)
+        p = bench_prefill(layers, 3, "bf16", args.steps, args.warmup, shared=shared)
+        sh = {"prefill_t8192": {"tokens/s": round(p["tokens_per_s"], 1), "ms_per_step": round(p["ms"], 4),
+                                "useful_tflops_step": round((p["gu_flops"] + p["dn_flops"]) / (p["ms"] * 1e-3) / 1e12,
+                                                            1)}}
+        for idx in (1, 2):
+            d = bench_decode(layers, idx, args.decode_rounds, eager=args.eager, shared=shared)
+            sh[f"decode_t{d['T']}"] = {"us_per_layer": round(d["us"], 3), "GB/s": round(d["gbs"], 1),
+                                       "frac_hbm_peak": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                       "experts_read": d["unique_experts"], "weight_bytes": d["bytes"]}
+        log(f"shared expert: {sh}")
+        del shared, sbase
     hd = None
     if args.only in ("all", "host"):
         hd = bench_host()
@@ -629,6 +660,12 @@ def main():
         if dec:
             result["q8_down"]["decode_time_vs_nvfp4"] = {
                 k: round(q8[f"decode_{k}"]["us"] / dec[k]["us"], 3) for k in dec if f"decode_{k}" in q8}
+    if sh is not None:
+        result["shared_expert"] = {
+            "workload": "the same layers with a shared expert each (an NVFP4 SwiGLU expert of the routed "
+                        "experts' shape applied to every token with weight 1, in the same launches); prefill "
+                        "8192 tokens, decode 1 and 4 tokens",
+            **sh}
     if hd is not None:
         result["host_decode"] = hd
     if cpu is not None:

@@ -222,6 +222,41 @@ int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
                       const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act,
                       void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* The layer's shared expert ("Strata NVFP4" README, 0.1.39-nvfp4.2 entry: the shared
+ * expert, with its fused SwiGLU quantizer keeping the fp16 scale finite). The pages give the
+ * shared expert no shape, format or weight; the reading taken here: an NVFP4 SwiGLU expert
+ * of the routed experts' shape (its own gate, up and down projections, each one expert:
+ * codes [1][N][K/2], scales [1][N][K/16], global [1]; the down projection in the routed
+ * down projection's format) applied to every token with weight 1 and added to the routed
+ * sum before the one final rounding:
+ *   out[t] = sum_j topk_weights[t][j] * y_{topk_ids[t][j]}(x_t) + y_shared(x_t).
+ * It runs in the same launches as the routed experts, as one more expert (index E) that
+ * every token routes to as slot topk; its h goes through the same fused SwiGLU epilogue,
+ * whose per-block power-of-two scale (act BF16) or per-row fp32 scale (W4A8) is finite for
+ * every finite h. All arguments are those of nvfp4_moe_decode / nvfp4_moe_prefill plus the
+ * three shared projections. ws needs the *_shared_workspace_size() bytes; the dropped count
+ * is in its first 4 bytes as for the plain calls (ids equal to E count as dropped: only the
+ * library's own slot reaches the shared expert). The prefill workspace regions are those of
+ * nvfp4_moe_prefill_workspace_region(T, H, I, E + 1, topk + 1, act). Decode keeps its
+ * grid-barrier state at the front of ws like nvfp4_moe_decode and needs T * (topk + 1) <= 64.
+ * Errors: those of the plain calls, and EINVAL for a shared projection that is null,
+ * misaligned or of another shape, EUNSUPPORTED for a shared gate or up that is not NVFP4 or
+ * a shared down whose format differs from the routed down's. */
+size_t nvfp4_moe_prefill_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                               int32_t act);
+int nvfp4_moe_prefill_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                             const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                             const nvfp4_weight* shared_gate, const nvfp4_weight* shared_up,
+                             const nvfp4_weight* shared_down, const int32_t* topk_ids, const float* topk_weights,
+                             int32_t topk, int32_t act, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                             void* stream);
+size_t nvfp4_moe_decode_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk);
+int nvfp4_moe_decode_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                            const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                            const nvfp4_weight* shared_gate, const nvfp4_weight* shared_up,
+                            const nvfp4_weight* shared_down, const int32_t* topk_ids, const float* topk_weights,
+                            int32_t topk, void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* Where a prefill call keeps its intermediate results in its workspace, for callers
  * that inspect them (tests, debugging) after running the stages: *offset receives the
  * region's byte offset from the start of ws and *bytes its size (0 when the region does

@@ -97,6 +97,17 @@ _SIGS = {
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]),
+    "nvfp4_moe_prefill_shared_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 6),
+    "nvfp4_moe_prefill_shared": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                                 + [ctypes.POINTER(_Weight)] * 3 + [ctypes.c_int32] + [ctypes.POINTER(_Weight)] * 3
+                                 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_void_p]),
+    "nvfp4_moe_decode_shared_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 5),
+    "nvfp4_moe_decode_shared": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                                + [ctypes.POINTER(_Weight)] * 3 + [ctypes.c_int32] + [ctypes.POINTER(_Weight)] * 3
+                                + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -286,12 +297,17 @@ def router_topk(x: torch.Tensor, w_router: torch.Tensor, topk: int, ws: Optional
     return ids, wts
 
 
-def decode_workspace_size(T: int, H: int, I: int, E: int, topk: int) -> int:
-    return int(load_library().nvfp4_moe_decode_workspace_size(T, H, I, E, topk))
+def decode_workspace_size(T: int, H: int, I: int, E: int, topk: int, shared: bool = False) -> int:
+    lib = load_library()
+    fn = lib.nvfp4_moe_decode_shared_workspace_size if shared else lib.nvfp4_moe_decode_workspace_size
+    return int(fn(T, H, I, E, topk))
 
 
-def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str = "bf16") -> int:
-    return int(load_library().nvfp4_moe_prefill_workspace_size(T, H, I, E, topk, ACT[act]))
+def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str = "bf16",
+                           shared: bool = False) -> int:
+    lib = load_library()
+    fn = lib.nvfp4_moe_prefill_shared_workspace_size if shared else lib.nvfp4_moe_prefill_workspace_size
+    return int(fn(T, H, I, E, topk, ACT[act]))
 
 
 WS_REGION = {"expert_offsets": 0, "sorted_pairs": 1, "pair_position": 2, "x_staged": 3, "x_rowscale": 4,
@@ -330,20 +346,29 @@ def _ws(ws: Optional[torch.Tensor], need: int, dev) -> torch.Tensor:
 
 def moe_decode(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor,
                out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
-               ws: Optional[torch.Tensor] = None, check: bool = True) -> torch.Tensor:
+               ws: Optional[torch.Tensor] = None, check: bool = True,
+               shared: Optional[Layer] = None) -> torch.Tensor:
     """check: read the workspace's error word after the call (a device synchronization)
     and raise if the grid barrier timed out; launch loops pass False and call
-    check_decode_workspace() when they use a result."""
+    check_decode_workspace() when they use a result. shared: the layer's shared expert (a
+    one-expert Layer), applied to every token with weight 1 (nvfp4_moe_decode_shared)."""
     lib = load_library()
     T, H = int(x.shape[0]), int(x.shape[1])
     k = int(ids.shape[1])
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=x.device)
-    ws = _ws(ws, decode_workspace_size(T, H, layer.I, layer.E, k), x.device)
+    ws = _ws(ws, decode_workspace_size(T, H, layer.I, layer.E, k, shared=shared is not None), x.device)
     g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
-    _check("nvfp4_moe_decode", lib.nvfp4_moe_decode(
-        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
-        _ptr(w), k, _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    if shared is None:
+        _check("nvfp4_moe_decode", lib.nvfp4_moe_decode(
+            _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+            _ptr(w), k, _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    else:
+        sg, su, sd = shared.gate.cstruct(), shared.up.cstruct(), shared.down.cstruct()
+        _check("nvfp4_moe_decode_shared", lib.nvfp4_moe_decode_shared(
+            _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E,
+            ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), _ptr(ids), _ptr(w), k, _ptr(out),
+            DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
     if check and T > 0:
         check_decode_workspace(ws)
     return out
@@ -405,17 +430,26 @@ def moe_decode_host(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.T
 
 def moe_prefill(x: torch.Tensor, layer: Layer, ids: torch.Tensor, w: torch.Tensor, act: str = "bf16",
                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
-                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+                ws: Optional[torch.Tensor] = None, shared: Optional[Layer] = None) -> torch.Tensor:
+    """shared: the layer's shared expert (a one-expert Layer), applied to every token with
+    weight 1 in the same launches (nvfp4_moe_prefill_shared)."""
     lib = load_library()
     T, H = int(x.shape[0]), int(x.shape[1])
     k = int(ids.shape[1])
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=x.device)
-    ws = _ws(ws, prefill_workspace_size(T, H, layer.I, layer.E, k, act), x.device)
+    ws = _ws(ws, prefill_workspace_size(T, H, layer.I, layer.E, k, act, shared=shared is not None), x.device)
     g, u, d = layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct()
-    _check("nvfp4_moe_prefill", lib.nvfp4_moe_prefill(
-        _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
-        _ptr(w), k, ACT[act], _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    if shared is None:
+        _check("nvfp4_moe_prefill", lib.nvfp4_moe_prefill(
+            _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E, _ptr(ids),
+            _ptr(w), k, ACT[act], _ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
+    else:
+        sg, su, sd = shared.gate.cstruct(), shared.up.cstruct(), shared.down.cstruct()
+        _check("nvfp4_moe_prefill_shared", lib.nvfp4_moe_prefill_shared(
+            _ptr(x), DTYPE[x.dtype], T, H, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), layer.E,
+            ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), _ptr(ids), _ptr(w), k, ACT[act], _ptr(out),
+            DTYPE[out.dtype], _ptr(ws), ws.numel(), _stream(x.device)))
     return out
 
 
@@ -423,17 +457,29 @@ class PreparedCall:
     """A decode or prefill call with its arguments marshalled once, for launch loops
     (benchmarks, graph capture): run() enqueues the whole call, stage(i) one stage."""
 
-    def __init__(self, kind: str, x, layer: Layer, ids, w, out, ws, act: str = "bf16"):
+    def __init__(self, kind: str, x, layer: Layer, ids, w, out, ws, act: str = "bf16",
+                 shared: Optional[Layer] = None):
         self.lib = load_library()
         self.kind = kind
-        self.keep = (x, layer, ids, w, out, ws)
+        self.keep = (x, layer, ids, w, out, ws, shared)
         self._w = (layer.gate.cstruct(), layer.up.cstruct(), layer.down.cstruct())
         g, u, d = (ctypes.byref(v) for v in self._w)
         T, H = int(x.shape[0]), int(x.shape[1])
         k = int(ids.shape[1])
-        common = [_ptr(x), DTYPE[x.dtype], T, H, g, u, d, layer.E, _ptr(ids), _ptr(w), k]
         tail = [_ptr(out), DTYPE[out.dtype], _ptr(ws), ws.numel()]
         self.device = x.device
+        if shared is not None:
+            # the shared-expert entry points have no staged form
+            self._s = (shared.gate.cstruct(), shared.up.cstruct(), shared.down.cstruct())
+            sg, su, sd = (ctypes.byref(v) for v in self._s)
+            common = [_ptr(x), DTYPE[x.dtype], T, H, g, u, d, layer.E, sg, su, sd, _ptr(ids), _ptr(w), k]
+            self.staged, self.nstages = None, 0
+            if kind == "decode":
+                self.args, self.full = common + tail, self.lib.nvfp4_moe_decode_shared
+            else:
+                self.args, self.full = common + [ACT[act]] + tail, self.lib.nvfp4_moe_prefill_shared
+            return
+        common = [_ptr(x), DTYPE[x.dtype], T, H, g, u, d, layer.E, _ptr(ids), _ptr(w), k]
         if kind == "decode":
             self.args = common + tail
             self.full, self.staged, self.nstages = self.lib.nvfp4_moe_decode, self.lib.nvfp4_moe_decode_stage, 2
@@ -446,6 +492,8 @@ class PreparedCall:
         _check(self.kind, self.full(*self.args, _stream(self.device)))
 
     def stage(self, i: int) -> None:
+        if self.staged is None:
+            raise NVFP4Error(self.kind + "_stage", -1, "the shared-expert calls have no staged form")
         _check(self.kind + "_stage", self.staged(i, *self.args, _stream(self.device)))
 
     def check(self) -> None:

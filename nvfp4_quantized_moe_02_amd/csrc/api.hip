@@ -27,6 +27,35 @@ WeightArgs to_args(const nvfp4_weight* w) {
   return WeightArgs{w->codes, w->scales, w->global, w->N, w->K, w->format == NVFP4_FMT_Q8_0 ? 1 : 0};
 }
 
+// The layer's shared expert, when a call has one: its three projections (one expert each,
+// the routed experts' shapes and formats) become expert index E of the routed tensors.
+WeightArgs to_args_shared(const nvfp4_weight* w, const nvfp4_weight* x, int xe) {
+  WeightArgs a = to_args(w);
+  if (x != nullptr) {
+    a.xcodes = x->codes;
+    a.xscales = x->scales;
+    a.xglobal = x->global;
+    a.xe = xe;
+  }
+  return a;
+}
+
+int check_shared(const nvfp4_weight* const* sh, const nvfp4_weight* gate, const nvfp4_weight* up,
+                 const nvfp4_weight* down) {
+  if (sh == nullptr) return NVFP4_OK;
+  if (!weight_ok(sh[0]) || !weight_ok(sh[1]) || !weight_ok(sh[2])) return NVFP4_EINVAL;
+  if (sh[0]->N != gate->N || sh[0]->K != gate->K || sh[1]->N != up->N || sh[1]->K != up->K ||
+      sh[2]->N != down->N || sh[2]->K != down->K)
+    return NVFP4_EINVAL;
+  if (sh[0]->format != NVFP4_FMT_NVFP4 || sh[1]->format != NVFP4_FMT_NVFP4 || sh[2]->format != down->format)
+    return NVFP4_EUNSUPPORTED;
+  return NVFP4_OK;
+}
+
+// Bytes after the main workspace that hold the routing with the shared slot appended
+// (ids [T][topk+1], then weights [T][topk+1]).
+size_t shared_routing_bytes(int T, int topk) { return 2 * align_up((size_t)T * (topk + 1) * 4); }
+
 // Workspace carving: offsets are computed identically by the size query and the call.
 struct Carver {
   size_t off = 0;
@@ -228,26 +257,45 @@ static int check_moe_common(const void* x, int32_t T, int32_t H, const nvfp4_wei
 }
 
 // dry: validate only (nothing is enqueued).
+// dry: validate only (nothing is enqueued). shared: the layer's shared expert (gate, up,
+// down) or null; with one, every token gets slot topk = the shared expert (index E, weight
+// 1), and the routing with that slot is written after the main workspace first.
 static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int32_t T, int32_t H,
                        const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
                        const int32_t* topk_ids, const float* topk_weights, int32_t topk, void* out,
-                       int32_t out_dtype, void* ws, size_t ws_bytes, void* stream, bool dry = false) {
+                       int32_t out_dtype, void* ws, size_t ws_bytes, void* stream, bool dry = false,
+                       const nvfp4_weight* const* shared = nullptr) {
   int st = check_moe_common(x, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, ws);
   if (st != NVFP4_OK) return st;
+  if ((st = check_shared(shared, gate, up, down)) != NVFP4_OK) return st;
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
-  if (T > kDecodeMaxT || T * topk > kDecodeMaxPairs || H > kDecodeMaxH || I > 8192) return NVFP4_EUNSUPPORTED;
+  const int keff = shared ? topk + 1 : topk;
+  if (T > kDecodeMaxT || T * keff > kDecodeMaxPairs || H > kDecodeMaxH || I > 8192) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * H > kDecodeMaxTH) return NVFP4_EUNSUPPORTED;  // activations are staged in LDS
-  const DecodeLayout l = decode_layout(T, H, I, topk);
-  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
+  const DecodeLayout l = decode_layout(T, H, I, keff);
+  const size_t extra = shared ? shared_routing_bytes(T, topk) : 0;
+  if (ws_bytes < l.end + extra) return NVFP4_EWORKSPACE;
   if (T == 0 || dry) return NVFP4_OK;
   (void)hipGetLastError();
+  hipStream_t s = as_stream(stream);
+  const int32_t* ids = topk_ids;
+  const float* wts = topk_weights;
+  if (shared) {
+    int32_t* ids2 = at<int32_t>(ws, l.end);
+    float* w2 = at<float>(ws, l.end + extra / 2);
+    if (launch_append_shared(topk_ids, topk_weights, T, topk, E, ids2, w2, s) != hipSuccess) return NVFP4_EHIP;
+    ids = ids2;
+    wts = w2;
+  }
+  const nvfp4_weight* const* sh = shared;
   // the full call runs as one persistent launch (mode 2); a single stage as mode 0 or 1
   const int mode = (first == 0 && last == 1) ? 2 : first;
-  hipError_t e = launch_decode(mode, x, T, H, I, to_args(gate), to_args(up), to_args(down), E, topk_ids,
-                               topk_weights, topk, out, out_dtype, at<float>(ws, l.h), at<int32_t>(ws, l.hdr),
-                               at<unsigned long long>(ws, l.flags), as_stream(stream));
+  hipError_t e = launch_decode(mode, x, T, H, I, to_args_shared(gate, sh ? sh[0] : nullptr, E),
+                               to_args_shared(up, sh ? sh[1] : nullptr, E), to_args_shared(down, sh ? sh[2] : nullptr, E),
+                               shared ? E + 1 : E, ids, wts, keff, out, out_dtype, at<float>(ws, l.h),
+                               at<int32_t>(ws, l.hdr), at<unsigned long long>(ws, l.flags), s);
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
@@ -266,6 +314,22 @@ int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_
   if (stage < 0 || stage > 1) return NVFP4_EINVAL;
   return decode_impl(stage, stage, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out,
                      out_dtype, ws, ws_bytes, stream);
+}
+
+size_t nvfp4_moe_decode_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk) {
+  (void)E;
+  if (T < 0 || I < 1 || topk < 1) return 0;
+  return decode_layout(T, H, I, topk + 1).end + shared_routing_bytes(T, topk);
+}
+
+int nvfp4_moe_decode_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                            const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                            const nvfp4_weight* shared_gate, const nvfp4_weight* shared_up,
+                            const nvfp4_weight* shared_down, const int32_t* topk_ids, const float* topk_weights,
+                            int32_t topk, void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const nvfp4_weight* sh[3] = {shared_gate, shared_up, shared_down};
+  return decode_impl(0, 1, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, out_dtype, ws,
+                     ws_bytes, stream, false, sh);
 }
 
 }  // extern "C"
@@ -336,23 +400,35 @@ size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
   return prefill_layout(T, H, I, E, topk, act).end;
 }
 
+// shared: the layer's shared expert (gate, up, down) or null; with one, the call routes
+// E + 1 experts with topk + 1 slots per token, slot topk being the shared expert (index E,
+// weight 1), from a routing written after the main workspace at the start of stage 0.
 static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int32_t T, int32_t H,
-                        const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
-                        const int32_t* topk_ids, const float* topk_weights, int32_t topk, int32_t act, void* out,
-                        int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_moe_common(x, T, H, gate, up, down, E, topk_ids, topk_weights, topk, out, ws);
+                        const nvfp4_weight* gate, const nvfp4_weight* up, const nvfp4_weight* down, int32_t E0,
+                        const int32_t* topk_ids0, const float* topk_weights0, int32_t topk0, int32_t act, void* out,
+                        int32_t out_dtype, void* ws, size_t ws_bytes, void* stream,
+                        const nvfp4_weight* const* shared = nullptr) {
+  int st = check_moe_common(x, T, H, gate, up, down, E0, topk_ids0, topk_weights0, topk0, out, ws);
   if (st != NVFP4_OK) return st;
+  if ((st = check_shared(shared, gate, up, down)) != NVFP4_OK) return st;
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
   if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
+  const int E = shared ? E0 + 1 : E0, topk = shared ? topk0 + 1 : topk0;
   if ((H % 256) != 0 || (I % 128) != 0 || I > 8192 || E > kMaxExperts) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * topk > (int64_t)1 << 30) return NVFP4_EUNSUPPORTED;
   const PrefillLayout l = prefill_layout(T, H, I, E, topk, act);
-  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
+  const size_t extra = shared ? shared_routing_bytes(T, topk0) : 0;
+  if (ws_bytes < l.end + extra) return NVFP4_EWORKSPACE;
   if (T == 0) return NVFP4_OK;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
+  const int32_t* topk_ids = shared ? at<int32_t>(ws, l.end) : topk_ids0;
+  const float* topk_weights = shared ? at<float>(ws, l.end + extra / 2) : topk_weights0;
+  const WeightArgs ga = to_args_shared(gate, shared ? shared[0] : nullptr, E0);
+  const WeightArgs ua = to_args_shared(up, shared ? shared[1] : nullptr, E0);
+  const WeightArgs da = to_args_shared(down, shared ? shared[2] : nullptr, E0);
   const int64_t P = (int64_t)T * topk;
   float* y = at<float>(ws, l.y);
   int32_t* offsets = at<int32_t>(ws, l.r.offsets);
@@ -369,29 +445,32 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
     hipError_t e = hipSuccess;
     if (stage == 0) {  // route, stage the activations
       RouteWs rw{at<int32_t>(ws, l.r.counts), at<int32_t>(ws, l.r.dropped), hdr, tiles, at<int32_t>(ws, l.r.inv)};
-      if (mode == 0) {
+      if (shared)
+        e = launch_append_shared(topk_ids0, topk_weights0, T, topk0, E0, const_cast<int32_t*>(topk_ids),
+                                 const_cast<float*>(topk_weights), s);
+      if (e == hipSuccess && mode == 0) {
         e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s, x, xa, xexp, T, H);
-      } else {
+      } else if (e == hipSuccess) {
         e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
         if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, static_cast<int8_t*>(xa), xscale, s);
       }
     } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
       if (act == NVFP4_ACT_W4A8)
         e = launch_gemm_gateup_i8(static_cast<const int8_t*>(xa), xscale, sorted, offsets, tiles, hdr + 1,
-                                  l.r.max_tiles, topk, H, I, to_args(gate), to_args(up), at<float>(ws, l.h), s);
+                                  l.r.max_tiles, topk, H, I, ga, ua, at<float>(ws, l.h), s);
       else
         e = launch_gemm_gateup(mode, xa, xscale, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H,
-                               I, to_args(gate), to_args(up), at<void>(ws, l.h), hexp, s);
+                               I, ga, ua, at<void>(ws, l.h), hexp, s);
       if (e == hipSuccess && mode == 1)
         e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<int8_t>(ws, l.qh), sh, s);
     } else if (stage == 2) {  // down, scaled by gamma_d and the router weight, per pair
       const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh);
       if (act == NVFP4_ACT_W4A8)
         e = launch_gemm_down_i8(static_cast<const int8_t*>(hA), sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles,
-                                topk, H, I, to_args(down), topk_weights, y, s);
+                                topk, H, I, da, topk_weights, y, s);
       else
         e = launch_gemm_down(mode, hA, sh, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
-                             to_args(down), topk_weights, y, s);
+                             da, topk_weights, y, s);
     } else {  // top-k combine in slot order, one rounding to the output dtype
       e = launch_combine(y, at<int32_t>(ws, l.r.inv), T, topk, H, out, out_dtype, s);
     }
@@ -428,6 +507,24 @@ int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
                       size_t ws_bytes, void* stream) {
   return prefill_impl(0, 3, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, act, out, out_dtype,
                       ws, ws_bytes, stream);
+}
+
+size_t nvfp4_moe_prefill_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
+                                               int32_t act) {
+  if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return 0;
+  return prefill_layout(T, H, I, E + 1, topk + 1, act).end + shared_routing_bytes(T, topk);
+}
+
+int nvfp4_moe_prefill_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,
+                             const nvfp4_weight* up, const nvfp4_weight* down, int32_t E,
+                             const nvfp4_weight* shared_gate, const nvfp4_weight* shared_up,
+                             const nvfp4_weight* shared_down, const int32_t* topk_ids, const float* topk_weights,
+                             int32_t topk, int32_t act, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                             void* stream) {
+  const nvfp4_weight* sh[3] = {shared_gate, shared_up, shared_down};
+  return prefill_impl(0, 3, x, x_dtype, T, H, gate, up, down, E, topk_ids, topk_weights, topk, act, out, out_dtype,
+                      ws, ws_bytes, stream, sh);
 }
 
 int nvfp4_moe_prefill_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,

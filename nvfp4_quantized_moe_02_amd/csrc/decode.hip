@@ -232,16 +232,19 @@ struct GateUpRows {
   float gg, gu;  // the expert's global scales, loaded with its rows
 };
 
-template <int CH>
-__device__ __forceinline__ void gateup_load(const DecodeArgs& a, int e, int row, int l16, GateUpRows<CH>& r) {
+// X: the call has a separately stored (shared) expert, index a.gate.xe
+template <int CH, bool X>
+__device__ __forceinline__ void gateup_load(const DecodeArgs& a, int e_in, int row, int l16, GateUpRows<CH>& r) {
   const int nch = a.H >> 5;
-  const size_t grow = (size_t)e * a.I + row;
-  const uint8_t* gc = a.gate.codes + grow * (a.H / 2);
-  const uint8_t* uc = a.up.codes + grow * (a.H / 2);
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(a.gate.scales + grow * (a.H / 16));
-  const uint16_t* us = reinterpret_cast<const uint16_t*>(a.up.scales + grow * (a.H / 16));
-  r.gg = a.gate.global[e];
-  r.gu = a.up.global[e];
+  // the unit's expert is the same for the whole wave: with a shared expert, keep it (and
+  // the selected weight bases) scalar
+  const int e = X ? __builtin_amdgcn_readfirstlane(e_in) : e_in;
+  const uint8_t* gc = a.gate.code_row<X>(e, row, a.H / 2);
+  const uint8_t* uc = a.up.code_row<X>(e, row, a.H / 2);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(a.gate.scale_row<X>(e, row));
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(a.up.scale_row<X>(e, row));
+  r.gg = a.gate.gamma_nvfp4<X>(e);
+  r.gu = a.up.gamma_nvfp4<X>(e);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int ch = l16 + 16 * c;
@@ -297,7 +300,7 @@ struct Phase1 {
   int j;
 };
 
-template <int CH>
+template <int CH, bool X>
 __device__ __forceinline__ void phase1_issue(const DecodeArgs& a, const DecodeSmem& sm, int j, Phase1<CH>& st) {
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, rq = lane >> 4;
@@ -307,15 +310,15 @@ __device__ __forceinline__ void phase1_issue(const DecodeArgs& a, const DecodeSm
   st.j = j;
   if (j < units) {
     const int u0 = j / quads;
-    gateup_load<CH>(a, sm.uniq[u0], (j - u0 * quads) * 4 + rq, l16, st.r0);
+    gateup_load<CH, X>(a, sm.uniq[u0], (j - u0 * quads) * 4 + rq, l16, st.r0);
   }
   if (j + nw < units) {
     const int u1 = (j + nw) / quads;
-    gateup_load<CH>(a, sm.uniq[u1], (j + nw - u1 * quads) * 4 + rq, l16, st.r1);
+    gateup_load<CH, X>(a, sm.uniq[u1], (j + nw - u1 * quads) * 4 + rq, l16, st.r1);
   }
 }
 
-template <int CH>
+template <int CH, bool X>
 __device__ void phase1(const DecodeArgs& a, const DecodeSmem& sm, Phase1<CH>& st) {
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, rq = lane >> 4;
@@ -323,7 +326,7 @@ __device__ void phase1(const DecodeArgs& a, const DecodeSmem& sm, Phase1<CH>& st
   const int units = sm.nu * quads;
   const int nw = gridDim.x * kDecWaves;
   for (int j = st.j; j < units; j += 2 * nw) {
-    if (j != st.j) phase1_issue<CH>(a, sm, j, st);
+    if (j != st.j) phase1_issue<CH, X>(a, sm, j, st);
     const int u0 = j / quads;
     gateup_compute<CH>(a, sm, u0, (j - u0 * quads) * 4 + rq, l16, st.r0);
     if (j + nw < units) {
@@ -352,7 +355,7 @@ __device__ __forceinline__ int down_expert(int wave, int ub) { return wave + kDe
 // Loads the weight chunks of this wave's experts ub0 .. ub0+kUB-1 for output row `row`;
 // experts beyond the unique list get an empty pair range and rows beyond H zero codes,
 // scales and global scale (they add exactly 0).
-template <int CH, bool Q8>
+template <int CH, bool Q8, bool X>
 __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem& sm, int ub0, int row, int l16,
                                           DownRows<CH, Q8>& d) {
   const int wave = threadIdx.x >> 6;
@@ -366,11 +369,13 @@ __device__ __forceinline__ void down_load(const DecodeArgs& a, const DecodeSmem&
     d.p0[b] = have ? sm.list[d.ps[b]] : 0;
     d.w0[b] = have ? sm.wp[d.p0[b]] : 0.f;
     const bool ok = have && row < a.H;
-    d.gd[b] = ok ? (a.down.global ? a.down.global[sm.uniq[u]] : 1.0f) : 0.f;
-    const size_t grow = ok ? (size_t)sm.uniq[u] * a.H + row : 0;
+    d.gd[b] = ok ? a.down.gamma<X>(X ? __builtin_amdgcn_readfirstlane(sm.uniq[u]) : sm.uniq[u]) : 0.f;
     // per row: NVFP4 I/2 code bytes and I/16 scale bytes; Q8_0 I code bytes and I/32 fp16
-    const uint8_t* rc = a.down.codes + grow * (Q8 ? a.I : a.I / 2);
-    const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scales + grow * (a.I / 16));
+    const int ue = ok ? sm.uniq[u] : 0;
+    const size_t rr = ok ? (size_t)row : 0;
+    const int uex = X ? __builtin_amdgcn_readfirstlane(have ? sm.uniq[u] : 0) : ue;  // one expert per wave and b
+    const uint8_t* rc = a.down.code_row<X>(uex, rr, Q8 ? a.I : a.I / 2);
+    const uint16_t* rs = reinterpret_cast<const uint16_t*>(a.down.scale_row<X>(uex, rr));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ch = l16 + kDownLanes * c;
@@ -478,8 +483,8 @@ __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
 }
 
 // MODE 0: phase 1 only; MODE 1: phase 2 only; MODE 2: both with the grid barrier.
-// Q8: the down projection is Q8_0.
-template <int MODE, int CHG, int CHD, bool Q8>
+// Q8: the down projection is Q8_0. X: one expert (the shared one) is stored apart.
+template <int MODE, int CHG, int CHD, bool Q8, bool X>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ DecodeSmem sm;
   decode_prepare(sm, a, MODE != 1);
@@ -495,10 +500,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   // spreads the units beyond the first round over all blocks (measured: 1 token 13.8 us
   // block-major vs 14.6 wave-major; 4 tokens 29.8 vs 28.9).
   const int j0 = a.T == 1 ? (int)blockIdx.x * kDecWaves + wave : wave * (int)gridDim.x + (int)blockIdx.x;
-  if (MODE != 1) phase1_issue<CHG>(a, sm, j0, p1);
+  if (MODE != 1) phase1_issue<CHG, X>(a, sm, j0, p1);
   DownRows<CHD, Q8> d;
-  if (MODE != 0) down_load<CHD, Q8>(a, sm, 0, row, l8, d);  // in flight during phase 1 and the wait
-  if (MODE != 1) phase1<CHG>(a, sm, p1);
+  if (MODE != 0) down_load<CHD, Q8, X>(a, sm, 0, row, l8, d);  // in flight during phase 1 and the wait
+  if (MODE != 1) phase1<CHG, X>(a, sm, p1);
   if (MODE == 0) return;
   if (MODE == 2 && !grid_barrier(a, sm)) {
     // the wait gave up: this block's output rows are written as NaN, never left stale
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   for (int t = 0; t < kDecodeMaxT; ++t) acc[t] = 0.f;
   const int per_wave = (sm.nu - wave + kDecWaves - 1) / kDecWaves;  // experts of this wave
   for (int ub0 = 0; ub0 < per_wave; ub0 += kUBof<Q8>) {
-    if (ub0 > 0) down_load<CHD, Q8>(a, sm, ub0, row, l8, d);
+    if (ub0 > 0) down_load<CHD, Q8, X>(a, sm, ub0, row, l8, d);
     if (a.h_in_lds) down_accum<CHD, Q8, true>(a, sm, d, l8, acc);
     else down_accum<CHD, Q8, false>(a, sm, d, l8, acc);
   }
@@ -580,45 +585,48 @@ static size_t decode_lds_bytes(const DecodeArgs& a) {
   return x_lds_bytes(a.T, a.H) + (a.h_in_lds ? h_lds_bytes(a.P, a.I) : 0);
 }
 
-template <int MODE, int CHG, int CHD, bool Q8>
+template <int MODE, int CHG, int CHD, bool Q8, bool X>
 static hipError_t launch_mode(const DecodeArgs& a, hipStream_t st) {
   const size_t lds = decode_lds_bytes(a);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<MODE, CHG, CHD, Q8>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<MODE, CHG, CHD, Q8, X>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid((a.H + kRowsPerBlock - 1) / kRowsPerBlock);
-  decode_kernel<MODE, CHG, CHD, Q8><<<grid, kDecThreads, lds, st>>>(a);
+  decode_kernel<MODE, CHG, CHD, Q8, X><<<grid, kDecThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
 // The fused form needs every block of its grid resident at once.
-template <int CHG, int CHD, bool Q8>
+template <int CHG, int CHD, bool Q8, bool X>
 static bool fused_fits(const DecodeArgs& a) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<2, CHG, CHD, Q8>),
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<2, CHG, CHD, Q8, X>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds_bytes(a)) != hipSuccess)
     return false;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<2, CHG, CHD, Q8>, kDecThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<2, CHG, CHD, Q8, X>, kDecThreads,
                                                    decode_lds_bytes(a)) != hipSuccess)
     return false;
   return (long long)((a.H + kRowsPerBlock - 1) / kRowsPerBlock) <= (long long)cus * per_cu;
 }
 
-template <int CHG, int CHD, bool Q8>
+template <int CHG, int CHD, bool Q8, bool X>
 static hipError_t launch_decode_q(int stage, const DecodeArgs& a, hipStream_t st) {
-  if (stage == 0) return launch_mode<0, CHG, CHD, Q8>(a, st);
-  if (stage == 1) return launch_mode<1, CHG, CHD, Q8>(a, st);
+  if (stage == 0) return launch_mode<0, CHG, CHD, Q8, X>(a, st);
+  if (stage == 1) return launch_mode<1, CHG, CHD, Q8, X>(a, st);
   // fused only when h fits in LDS: phase 2 then reads h once, with agent-coherent loads
-  if (a.h_in_lds && fused_fits<CHG, CHD, Q8>(a)) return launch_mode<2, CHG, CHD, Q8>(a, st);
-  const hipError_t e = launch_mode<0, CHG, CHD, Q8>(a, st);
-  return e != hipSuccess ? e : launch_mode<1, CHG, CHD, Q8>(a, st);
+  if (a.h_in_lds && fused_fits<CHG, CHD, Q8, X>(a)) return launch_mode<2, CHG, CHD, Q8, X>(a, st);
+  const hipError_t e = launch_mode<0, CHG, CHD, Q8, X>(a, st);
+  return e != hipSuccess ? e : launch_mode<1, CHG, CHD, Q8, X>(a, st);
 }
 
 template <int CHG, int CHD>
 static hipError_t launch_decode_t(int stage, const DecodeArgs& a, hipStream_t st) {
-  return a.down.fmt == 1 ? launch_decode_q<CHG, CHD, true>(stage, a, st) : launch_decode_q<CHG, CHD, false>(stage, a, st);
+  const bool x = a.gate.xe >= 0;
+  if (a.down.fmt == 1)
+    return x ? launch_decode_q<CHG, CHD, true, true>(stage, a, st) : launch_decode_q<CHG, CHD, true, false>(stage, a, st);
+  return x ? launch_decode_q<CHG, CHD, false, true>(stage, a, st) : launch_decode_q<CHG, CHD, false, false>(stage, a, st);
 }
 
 hipError_t launch_decode(int stage, const void* x, int T, int H, int I, const WeightArgs& gate, const WeightArgs& up,

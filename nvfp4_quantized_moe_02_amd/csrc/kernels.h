@@ -9,12 +9,47 @@ namespace nvfp4 {
 // One projection of all experts. fmt 0: NVFP4 (codes [E][N][K/2], E4M3 scales [E][N][K/16],
 // global [E]); fmt 1: Q8_0 (int8 codes [E][N][K], fp16 scales [E][N][K/32], global [E] or
 // null for 1).
+// Optionally one more expert, index `xe`, lives in tensors of its own (xcodes, xscales,
+// xglobal: one expert's worth, the layer's shared expert); -1 means none.
 struct WeightArgs {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* global;
   int N, K;
   int fmt;
+  const uint8_t* xcodes = nullptr;
+  const uint8_t* xscales = nullptr;
+  const float* xglobal = nullptr;
+  int xe = -1;
+  // First code / scale byte of row n (0 <= n < N) of expert e; rowbytes = code bytes per
+  // row, K / 2 for NVFP4 and K for Q8_0 (the caller knows the format at compile time).
+  // X = false: the call has no separately stored expert (plain indexing, no select).
+  template <bool X = true>
+  __device__ const uint8_t* code_row(int e, size_t n, size_t rowbytes) const {
+    if constexpr (X) return (e == xe ? xcodes : codes + (size_t)e * N * rowbytes) + n * rowbytes;
+    return codes + ((size_t)e * N + n) * rowbytes;
+  }
+  template <bool X = true>
+  __device__ const uint8_t* scale_row(int e, size_t n) const {
+    if constexpr (X) return (e == xe ? xscales : scales + (size_t)e * N * (K / 16)) + n * (K / 16);
+    return scales + ((size_t)e * N + n) * (K / 16);
+  }
+  // the expert's output scale; an NVFP4 projection always has one (one pointer select,
+  // then one load: no branch between the loads a caller issues together)
+  template <bool X = true>
+  __device__ float gamma_nvfp4(int e) const {
+    if constexpr (X) return *(e == xe ? xglobal : global + e);
+    return global[e];
+  }
+  // the same for a projection that may have none (Q8_0: NULL means 1)
+  template <bool X = true>
+  __device__ float gamma(int e) const {
+    if constexpr (X) {
+      const float* g = e == xe ? xglobal : (global != nullptr ? global + e : nullptr);
+      return g != nullptr ? *g : 1.0f;
+    }
+    return global != nullptr ? global[e] : 1.0f;
+  }
 };
 
 struct TileDesc {
@@ -60,6 +95,11 @@ int route_blocks(int64_t P);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, int32_t* sorted_pairs,
                         const RouteWs& ws, int tile_m, hipStream_t st, const void* cvt_src = nullptr,
                         void* cvt_dst = nullptr, int32_t* cvt_exp = nullptr, int cvt_rows = 0, int cvt_cols = 0);
+
+// ids2 [T][k+1] / w2: the k routed slots (ids outside [0, E) as -1) and the shared expert
+// (index E, weight 1) as slot k of every token.
+hipError_t launch_append_shared(const int32_t* ids, const float* w, int64_t T, int k, int E, int32_t* ids2,
+                                float* w2, hipStream_t st);
 
 // decode.hip
 constexpr int kDecodeMaxT = 8;

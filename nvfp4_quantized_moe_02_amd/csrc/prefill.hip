@@ -385,7 +385,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     // index 8*(v/4) + 4*half + v%4 of the wave's 32, for token row rb*32 + l32: four
     // consecutive v are four adjacent h values of one row, stored as one 8-byte (fp16) or
     // 16-byte (fp32) piece straight to memory.
-    const float gg = w0.global[tc.e], gu = w1.global[tc.e];
+    const float gg = w0.gamma_nvfp4(tc.e), gu = w1.gamma_nvfp4(tc.e);
     const int col0 = tc.nb * (WPB * 32) + wave * 32 + 4 * half;
     float hv[NRB][16];
 #pragma unroll
@@ -458,7 +458,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     // non-temporal (y is read once, by the combine). The kernel's LDS holds
     // 32 * NCOL * 4 bytes.
     constexpr int NCOL = WPB * 64;
-    const float gd = w0.global ? w0.global[tc.e] : 1.0f;  // a Q8_0 down may have no tensor scale
+    const float gd = w0.gamma(tc.e);  // a Q8_0 down may have no tensor scale (1)
     float* y = reinterpret_cast<float*>(out);
     float* yl = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -566,17 +566,17 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
   const uint8_t* b1row;
   const uint8_t* bs[2];
   if (GATEUP) {
-    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (WPB * 32);
-    b0row = w0.codes + row0 * (K / 2);
-    b1row = w1.codes + row0 * (K / 2);
-    bs[0] = w0.scales + (row0 + wave * 32 + l32) * (K / 16);
-    bs[1] = w1.scales + (row0 + wave * 32 + l32) * (K / 16);
+    const size_t row0 = (size_t)tc.nb * (WPB * 32);
+    b0row = w0.code_row(tc.e, row0, K / 2);
+    b1row = w1.code_row(tc.e, row0, K / 2);
+    bs[0] = w0.scale_row(tc.e, row0 + wave * 32 + l32);
+    bs[1] = w1.scale_row(tc.e, row0 + wave * 32 + l32);
   } else {
-    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (WPB * 64);
-    b0row = w0.codes + row0 * (Q8 ? K : K / 2);
+    const size_t row0 = (size_t)tc.nb * (WPB * 64);
+    b0row = w0.code_row(tc.e, row0, Q8 ? K : K / 2);
     b1row = b0row;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) bs[cb] = w0.scales + (row0 + wave * 64 + cb * 32 + l32) * (K / 16);
+    for (int cb = 0; cb < 2; ++cb) bs[cb] = w0.scale_row(tc.e, row0 + wave * 64 + cb * 32 + l32);
   }
   __syncthreads();
 

@@ -172,7 +172,7 @@ __device__ __forceinline__ void gemm_i8_tile(const TileCtx& tc, const int8_t* __
   // Accumulator element i of lane (half, l32): row rb*32 + 8*(i/4) + 4*half + i%4 of the
   // tile, weight row l32 of the column block.
   if constexpr (GATEUP) {
-    const float gg = w0.global[tc.e], gu = w1.global[tc.e];
+    const float gg = w0.gamma_nvfp4(tc.e), gu = w1.gamma_nvfp4(tc.e);
     const int col = tc.nb * (Q_NCOL / 2) + wave * 32 + l32;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -184,7 +184,7 @@ __device__ __forceinline__ void gemm_i8_tile(const TileCtx& tc, const int8_t* __
         if (r < tc.rows) reinterpret_cast<float*>(out)[(size_t)(tc.base + tc.m0 + r) * ldo + col] = h;
       }
   } else {
-    const float gd = w0.global ? w0.global[tc.e] : 1.0f;
+    const float gd = w0.gamma(tc.e);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -244,19 +244,19 @@ __global__ __launch_bounds__(Q_THREADS, 2) void moe_gemm_i8_kernel(
     }
   }
   const uint8_t *b0row, *b1row, *s0row, *s1row;
-  const int sstride = K / 16;  // scale bytes per weight row (NVFP4: K/16 E4M3; Q8_0: K/32 fp16)
+  // scale bytes per weight row: NVFP4 K/16 E4M3, Q8_0 K/32 fp16
   if (GATEUP) {
-    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * (Q_NCOL / 2);
-    b0row = w0.codes + row0 * (K / 2);
-    b1row = w1.codes + row0 * (K / 2);
-    s0row = w0.scales + (row0 + wave * 32 + l32) * sstride;
-    s1row = w1.scales + (row0 + wave * 32 + l32) * sstride;
+    const size_t row0 = (size_t)tc.nb * (Q_NCOL / 2);
+    b0row = w0.code_row(tc.e, row0, K / 2);
+    b1row = w1.code_row(tc.e, row0, K / 2);
+    s0row = w0.scale_row(tc.e, row0 + wave * 32 + l32);
+    s1row = w1.scale_row(tc.e, row0 + wave * 32 + l32);
   } else {
-    const size_t row0 = (size_t)tc.e * w0.N + tc.nb * Q_NCOL;
-    b0row = w0.codes + row0 * (Q8 ? K : K / 2);
+    const size_t row0 = (size_t)tc.nb * Q_NCOL;
+    b0row = w0.code_row(tc.e, row0, Q8 ? K : K / 2);
     b1row = b0row;
-    s0row = w0.scales + (row0 + wave * 64 + l32) * sstride;
-    s1row = w0.scales + (row0 + wave * 64 + 32 + l32) * sstride;
+    s0row = w0.scale_row(tc.e, row0 + wave * 64 + l32);
+    s1row = w0.scale_row(tc.e, row0 + wave * 64 + 32 + l32);
   }
   __syncthreads();
   const int nrb = (tc.rows + 31) >> 5;

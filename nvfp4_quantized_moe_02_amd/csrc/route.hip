@@ -231,4 +231,32 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int32_t* offsets, 
   return e;
 }
 
+// Routing of a layer with a shared expert, as one more slot of every token: ids2 [T][k+1]
+// holds the token's k routed ids (those outside [0, E) as -1, so they stay dropped when E + 1
+// experts are routed) and then E, the shared expert's index; w2 the router weights and 1.
+__global__ __launch_bounds__(256) void append_shared_kernel(const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ w, int64_t T, int k, int E,
+                                                            int32_t* __restrict__ ids2, float* __restrict__ w2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * (k + 1)) return;
+  const int64_t t = i / (k + 1);
+  const int j = (int)(i - t * (k + 1));
+  if (j < k) {
+    const int e = ids[t * k + j];
+    ids2[i] = (unsigned)e < (unsigned)E ? e : -1;
+    w2[i] = w[t * k + j];
+  } else {
+    ids2[i] = E;
+    w2[i] = 1.0f;
+  }
+}
+
+hipError_t launch_append_shared(const int32_t* ids, const float* w, int64_t T, int k, int E, int32_t* ids2,
+                                float* w2, hipStream_t st) {
+  const int64_t n = T * (k + 1);
+  if (n == 0) return hipSuccess;
+  append_shared_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(ids, w, T, k, E, ids2, w2);
+  return hipGetLastError();
+}
+
 }  // namespace nvfp4
