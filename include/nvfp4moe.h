@@ -237,8 +237,9 @@ int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
  * three shared projections. ws needs the *_shared_workspace_size() bytes; the dropped count
  * is in its first 4 bytes as for the plain calls (ids equal to E count as dropped: only the
  * library's own slot reaches the shared expert). The prefill workspace regions are those of
- * nvfp4_moe_prefill_workspace_region(T, H, I, E + 1, topk + 1, act). Decode keeps its
- * grid-barrier state at the front of ws like nvfp4_moe_decode and needs T * (topk + 1) <= 64.
+ * nvfp4_moe_prefill_workspace_region(T, H, I, E + 1, topk + 1, act), followed by the routing
+ * with the shared slot appended. Decode forms that slot inside its kernel (no extra launch),
+ * keeps its grid-barrier state in ws like nvfp4_moe_decode and needs T * (topk + 1) <= 64.
  * Errors: those of the plain calls, and EINVAL for a shared projection that is null,
  * misaligned or of another shape, EUNSUPPORTED for a shared gate or up that is not NVFP4 or
  * a shared down whose format differs from the routed down's. */

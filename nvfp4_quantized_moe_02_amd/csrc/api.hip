@@ -275,27 +275,18 @@ static int decode_impl(int first, int last, const void* x, int32_t x_dtype, int3
   if (T > kDecodeMaxT || T * keff > kDecodeMaxPairs || H > kDecodeMaxH || I > 8192) return NVFP4_EUNSUPPORTED;
   if ((int64_t)T * H > kDecodeMaxTH) return NVFP4_EUNSUPPORTED;  // activations are staged in LDS
   const DecodeLayout l = decode_layout(T, H, I, keff);
-  const size_t extra = shared ? shared_routing_bytes(T, topk) : 0;
-  if (ws_bytes < l.end + extra) return NVFP4_EWORKSPACE;
+  if (ws_bytes < l.end) return NVFP4_EWORKSPACE;
   if (T == 0 || dry) return NVFP4_OK;
   (void)hipGetLastError();
-  hipStream_t s = as_stream(stream);
-  const int32_t* ids = topk_ids;
-  const float* wts = topk_weights;
-  if (shared) {
-    int32_t* ids2 = at<int32_t>(ws, l.end);
-    float* w2 = at<float>(ws, l.end + extra / 2);
-    if (launch_append_shared(topk_ids, topk_weights, T, topk, E, ids2, w2, s) != hipSuccess) return NVFP4_EHIP;
-    ids = ids2;
-    wts = w2;
-  }
+  // The decode kernel reads the caller's [T][topk] routing and, with a shared expert (index
+  // E, the expert its WeightArgs hold apart), forms slot topk of every token itself.
   const nvfp4_weight* const* sh = shared;
   // the full call runs as one persistent launch (mode 2); a single stage as mode 0 or 1
   const int mode = (first == 0 && last == 1) ? 2 : first;
   hipError_t e = launch_decode(mode, x, T, H, I, to_args_shared(gate, sh ? sh[0] : nullptr, E),
                                to_args_shared(up, sh ? sh[1] : nullptr, E), to_args_shared(down, sh ? sh[2] : nullptr, E),
-                               shared ? E + 1 : E, ids, wts, keff, out, out_dtype, at<float>(ws, l.h),
-                               at<int32_t>(ws, l.hdr), at<unsigned long long>(ws, l.flags), s);
+                               shared ? E + 1 : E, topk_ids, topk_weights, keff, out, out_dtype, at<float>(ws, l.h),
+                               at<int32_t>(ws, l.hdr), at<unsigned long long>(ws, l.flags), as_stream(stream));
   return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 
@@ -319,7 +310,7 @@ int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_
 size_t nvfp4_moe_decode_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk) {
   (void)E;
   if (T < 0 || I < 1 || topk < 1) return 0;
-  return decode_layout(T, H, I, topk + 1).end + shared_routing_bytes(T, topk);
+  return decode_layout(T, H, I, topk + 1).end;
 }
 
 int nvfp4_moe_decode_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H, const nvfp4_weight* gate,

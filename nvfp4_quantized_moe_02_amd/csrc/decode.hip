@@ -105,8 +105,22 @@ __device__ void decode_prepare(DecodeSmem& sm, const DecodeArgs& a, bool copy_x)
   int e = -1;
   float wv = 0.f;
   if (tid < 64 && tid < a.P) {
-    e = a.ids[tid];
-    wv = a.w[tid];
+    if (a.gate.xe >= 0) {
+      // a shared expert (index xe) is slot topk - 1 of every token, weight 1; the caller's
+      // ids and weights are [T][topk - 1], and their ids outside [0, xe) are dropped
+      const int kk = a.topk - 1, t = tid / a.topk, j = tid - t * a.topk;
+      if (j < kk) {
+        e = a.ids[t * kk + j];
+        wv = a.w[t * kk + j];
+        if ((unsigned)e >= (unsigned)a.gate.xe) e = -1;
+      } else {
+        e = a.gate.xe;
+        wv = 1.0f;
+      }
+    } else {
+      e = a.ids[tid];
+      wv = a.w[tid];
+    }
   }
   if (copy_x) {
     const int n16 = a.T * a.H / 8;  // 16-byte pieces, 4 per 32-input chunk
