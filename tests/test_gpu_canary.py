@@ -1,0 +1,168 @@
+"""Canary-guarded outputs and workspaces: every entry point runs on buffers of exactly the
+documented size placed between canary regions, and the test checks that no byte outside the
+outputs and the workspace changed, that the inputs (activations, weights, routing) are left
+as they were, and that a second call gives the same bits."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import DEV, bf16_dev, layer_dev
+
+pytestmark = pytest.mark.gpu
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+import nvfp4_quantized_moe_02_amd.binding as B  # noqa: E402
+
+CANARY = 0xA5
+PAD = 4096
+
+
+class Guarded:
+    """`nbytes` of device memory between two PAD-byte canary regions (the payload starts
+    PAD bytes into a torch allocation, so it keeps 256-byte alignment)."""
+
+    def __init__(self, nbytes, dtype=torch.uint8, shape=None, fill=CANARY):
+        self.nbytes = int(nbytes)
+        self.raw = torch.full((PAD + self.nbytes + PAD,), CANARY, dtype=torch.uint8, device=DEV)
+        self.raw[PAD:PAD + self.nbytes] = fill
+        self.t = self.raw[PAD:PAD + self.nbytes].view(dtype)
+        if shape is not None:
+            self.t = self.t.view(shape)
+
+    def intact(self):
+        head = self.raw[:PAD]
+        tail = self.raw[PAD + self.nbytes:]
+        return bool((head == CANARY).all()) and bool((tail == CANARY).all())
+
+
+def guarded_like(shape, dtype, fill=CANARY):
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    return Guarded(n, dtype, shape, fill)
+
+
+def snapshot(*tensors):
+    return [t.clone() for t in tensors]
+
+
+def unchanged(before, *tensors):
+    return all(torch.equal(a, b) for a, b in zip(before, tensors))
+
+
+def layer_tensors(dl):
+    ts = []
+    for p in (dl.gate, dl.up, dl.down):
+        ts += [p.codes, p.scales] + ([p.gamma] if p.gamma is not None else [])
+    return ts
+
+
+def _problem(seed, T, E=8, H=512, I=256, k=4, down_fmt="nvfp4"):
+    lay = W.draw_layer(seed, E=E, H=H, I=I, down_fmt=down_fmt)
+    xb = W.draw_activations(seed, T, H)
+    ids = W.draw_routing_zipf(seed, T, E, k)
+    if T > 3:
+        ids[3, 0] = -1
+    w = W.draw_router_weights(seed, T, k)
+    return layer_dev(lay), bf16_dev(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+
+
+@pytest.mark.parametrize("act", ["bf16", "w4a8_f16", "w4a8"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shared", [False, True])
+def test_prefill_writes_only_its_output_and_workspace(act, out_dtype, shared):
+    T, H, I, E, k = 300, 512, 256, 8, 4
+    dl, x, ids, w = _problem(81, T, E, H, I, k)
+    ds = layer_dev(W.draw_shared_expert(81, H=H, I=I)) if shared else None
+    need = nv.prefill_workspace_size(T, H, I, E, k, act, shared=shared)
+    ws = Guarded(need)
+    out = guarded_like((T, H), out_dtype)
+    inputs = [x, ids, w] + layer_tensors(dl) + (layer_tensors(ds) if shared else [])
+    before = snapshot(*inputs)
+    nv.moe_prefill(x, dl, ids, w, act=act, out=out.t, ws=ws.t, shared=ds)
+    torch.cuda.synchronize()
+    first = out.t.clone()
+    assert ws.intact() and out.intact()
+    assert unchanged(before, *inputs)
+    nv.moe_prefill(x, dl, ids, w, act=act, out=out.t, ws=ws.t, shared=ds)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out.t)
+    assert ws.intact() and out.intact()
+
+
+@pytest.mark.parametrize("T", [1, 4, 7])
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("down_fmt", ["nvfp4", "q8_0"])
+def test_decode_writes_only_its_output_and_workspace(T, shared, down_fmt):
+    H, I, E, k = 1024, 512, 16, 8
+    dl, x, ids, w = _problem(83 + T, T, E, H, I, k, down_fmt=down_fmt)
+    ds = layer_dev(W.draw_shared_expert(83, H=H, I=I, down_fmt=down_fmt)) if shared else None
+    ws = Guarded(nv.decode_workspace_size(T, H, I, E, k, shared=shared), fill=0)
+    out = guarded_like((T, H), torch.float32)
+    inputs = [x, ids, w] + layer_tensors(dl) + (layer_tensors(ds) if shared else [])
+    before = snapshot(*inputs)
+    nv.moe_decode(x, dl, ids, w, out=out.t, ws=ws.t, shared=ds)
+    first = out.t.clone()
+    assert ws.intact() and out.intact()
+    assert unchanged(before, *inputs)
+    nv.moe_decode(x, dl, ids, w, out=out.t, ws=ws.t, shared=ds)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out.t)
+    assert ws.intact() and out.intact()
+
+
+def test_router_route_quant_dequant_linear_write_only_their_outputs():
+    lib = B.load_library()
+    s = B._stream(torch.device(DEV))
+    # router
+    T, H, E, k = 37, 512, 64, 8
+    x = bf16_dev(W.draw_activations(85, T, H))
+    wr = torch.from_numpy(W.draw_router(85, E=E, H=H).view(np.int16)).to(DEV)
+    ids, wts = guarded_like((T, k), torch.int32), guarded_like((T, k), torch.float32)
+    ws = Guarded(nv.router_workspace_size(T, E), fill=0)
+    before = snapshot(x, wr)
+    assert lib.nvfp4_router_topk(x.data_ptr(), 1, T, H, wr.data_ptr(), E, k, ids.t.data_ptr(), wts.t.data_ptr(),
+                                 ws.t.data_ptr(), ws.nbytes, s) == 0
+    torch.cuda.synchronize()
+    assert ids.intact() and wts.intact() and ws.intact() and unchanged(before, x, wr)
+    # routing sort
+    P = T * k
+    off, srt = guarded_like((E + 1,), torch.int32), guarded_like((P,), torch.int32)
+    rws = Guarded(nv.route_workspace_size(T, k, E))
+    rid = ids.t.clone()
+    assert lib.nvfp4_moe_route(rid.data_ptr(), T, k, E, off.t.data_ptr(), srt.t.data_ptr(), rws.t.data_ptr(),
+                               rws.nbytes, s) == 0
+    torch.cuda.synchronize()
+    assert off.intact() and srt.intact() and rws.intact() and torch.equal(rid, ids.t)
+    # int8 row quantizer (bf16 and fp32 inputs)
+    for xin, dt in ((x, 1), (x.float(), 0)):
+        q, sc = guarded_like((T, H), torch.int8), guarded_like((T,), torch.float32)
+        b = snapshot(xin)
+        assert lib.nvfp4_quant_rows_i8(xin.data_ptr(), dt, T, H, q.t.data_ptr(), sc.t.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        assert q.intact() and sc.intact() and unchanged(b, xin)
+    # dequant and the single-expert linear
+    lay = W.draw_layer(87, E=2, H=256, I=128)
+    p = nv.Proj.from_numpy(lay.gate, DEV)
+    rows = 2 * 128
+    for dtype in (torch.float32, torch.bfloat16, torch.float16):
+        out = guarded_like((rows, 256), dtype)
+        b = snapshot(p.codes, p.scales, p.gamma)
+        nv.dequant(p.codes.view(rows, 128), p.scales.view(rows, 16), p.gamma[:1], out_dtype=dtype, out=out.t)
+        torch.cuda.synchronize()
+        assert out.intact() and unchanged(b, p.codes, p.scales, p.gamma)
+    xl = torch.from_numpy(np.random.default_rng(1).standard_normal((5, 256)).astype(np.float32)).to(DEV)
+    out = guarded_like((5, 128), torch.float32)
+    nv.linear(xl, p, expert=1, out=out.t)
+    torch.cuda.synchronize()
+    assert out.intact()
+
+
+def test_noalloc_decode_writes_only_its_output():
+    T, H, I, E, k = 4, 1024, 512, 16, 8
+    dl, x, ids, w = _problem(89, T, E, H, I, k)
+    out = guarded_like((T, H), torch.float32)
+    before = snapshot(x, ids, w, *layer_tensors(dl))
+    nv.moe_decode_noalloc(x, dl, ids, w, out.t)
+    torch.cuda.synchronize()
+    assert out.intact() and unchanged(before, x, ids, w, *layer_tensors(dl))
