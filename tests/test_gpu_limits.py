@@ -1,0 +1,99 @@
+"""The largest supported shapes, and the first shapes past each limit, through the C-ABI:
+prefill with 8192 experts (most of them unrouted, with NaN scales, so any read of one
+poisons the output) and with I = 8192 (64 h-exponent segments per pair, the down GEMM's
+limit); decode at H = 8192 and at I = 8192. Past each limit the call returns
+NVFP4_EUNSUPPORTED before enqueueing anything."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import DEV, bf16_dev, layer_dev, max_row_rel_l2, sparse_layer
+
+pytestmark = pytest.mark.gpu
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+
+
+@pytest.mark.parametrize("act", ["bf16", "w4a8_f16"])
+def test_prefill_8192_experts(act):
+    E, H, I, T, k = 8192, 256, 128, 1024, 8
+    rng = np.random.default_rng(91)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[:, 0] = E - 1   # the last expert id: every token (a tile list end)
+    ids[:64, 1] = 0     # the first
+    dl, sub = sparse_layer(91, np.unique(ids), E=E, H=H, I=I)
+    xb = W.draw_activations(91, T, H)
+    w = W.draw_router_weights(91, T, k)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act=act,
+                       out_dtype=torch.float32)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()  # no unrouted (NaN-scaled) expert was read
+    if act == "bf16":
+        ref = O.moe_grouped(O.bf16_to_f64(xb), sub, ids, w)
+        err = max_row_rel_l2(got, ref)
+        print(f"prefill with 8192 experts: max row rel L2 {err:.3e}")
+        assert err < 5e-4
+
+
+def test_prefill_intermediate_8192():
+    """I = 8192: 64 fp16-h exponent segments per pair, every one used by the down GEMM."""
+    E, H, I, T, k = 4, 256, 8192, 200, 2
+    lay = W.draw_layer(93, E=E, H=H, I=I)
+    xb = W.draw_activations(93, T, H, outlier_frac=0.01)
+    ids = W.draw_routing_zipf(93, T, E, k)
+    w = W.draw_router_weights(93, T, k)
+    y = nv.moe_prefill(bf16_dev(xb), layer_dev(lay), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV),
+                       out_dtype=torch.float32)
+    ref = O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w)
+    err = max_row_rel_l2(y.cpu().numpy(), ref)
+    print(f"prefill I=8192: max row rel L2 {err:.3e}")
+    assert err < 5e-4
+
+
+@pytest.mark.parametrize("T,H,I", [(5, 8192, 256), (2, 1024, 8192)])
+def test_decode_largest_shapes(T, H, I):
+    """H = 8192 (the LDS-staged activations' limit, T * H <= 40960) and I = 8192."""
+    E, k = 12, 8
+    lay = W.draw_layer(95, E=E, H=H, I=I)
+    xb = W.draw_activations(95, T, H)
+    ids = W.draw_routing_uniform(95, T, E, k)
+    w = W.draw_router_weights(95, T, k)
+    y = nv.moe_decode(bf16_dev(xb), layer_dev(lay), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    ref = O.moe_pairwise(O.bf16_to_f64(xb), lay, ids, w)
+    err = max_row_rel_l2(y.cpu().numpy(), ref)
+    print(f"decode T={T} H={H} I={I}: max row rel L2 {err:.3e}")
+    assert err < 1e-5
+
+
+def test_past_the_limits_is_unsupported():
+    small = W.draw_layer(97, E=2, H=256, I=128)
+    dl = layer_dev(small)
+    x = bf16_dev(W.draw_activations(97, 9, 256))
+    ids = torch.zeros((9, 2), dtype=torch.int32, device=DEV)
+    w = torch.ones((9, 2), dtype=torch.float32, device=DEV)
+    out = torch.empty((9, 256), dtype=torch.float32, device=DEV)
+    # decode: 9 tokens (at most 8)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.moe_decode(x, dl, ids, w, out=out)
+    assert ei.value.status == -2
+    # decode: H above 8192 (the activations are staged in LDS)
+    big = W.draw_layer(97, E=2, H=8448, I=128)
+    xb = bf16_dev(W.draw_activations(97, 5, 8448))
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.moe_decode(xb, layer_dev(big), ids[:5].contiguous(), w[:5].contiguous())
+    assert ei.value.status == -2
+    # prefill: I above 8192
+    wide = W.draw_layer(97, E=1, H=256, I=8320)
+    with pytest.raises(nv.NVFP4Error) as ei:
+        nv.moe_prefill(x, layer_dev(wide), ids[:, :1].contiguous(), w[:, :1].contiguous())
+    assert ei.value.status == -2
+    # prefill: more than 8192 experts (the routing's LDS histograms hold 8192)
+    import nvfp4_quantized_moe_02_amd.binding as B
+    g, u, d = dl.gate.cstruct(), dl.up.cstruct(), dl.down.cstruct()
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    import ctypes
+    r = B.load_library().nvfp4_moe_prefill(x.data_ptr(), 1, 9, 256, ctypes.byref(g), ctypes.byref(u),
+                                           ctypes.byref(d), 8193, ids.data_ptr(), w.data_ptr(), 2, 0,
+                                           out.data_ptr(), 0, ws.data_ptr(), ws.numel(), None)
+    assert r == -2
