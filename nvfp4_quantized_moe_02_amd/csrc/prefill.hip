@@ -33,7 +33,7 @@
 //
 // Inside a K-block each lane reads its A fragments two ahead of their MFMAs (the LDS
 // latency hides under the MFMAs in between), unpacks the B fragments of the next step
-// right after issuing the current step's last MFMA, and issues the global loads of later
+// between the current step's MFMAs, and issues the global loads of later
 // K-blocks spread over the MFMAs: all waves issuing them in one burst after the barrier
 // made each wave queue in the address unit before its first MFMA.
 //
@@ -326,7 +326,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     };
     // A fragments are read LA fragments ahead of their MFMAs (a ring of LA+1), so the LDS
     // latency of each read hides under the MFMAs issued in between; the B fragments of
-    // step s+1 are unpacked right after the last MFMA of step s is issued.
+    // step s+1 are unpacked between the MFMAs of step s into a second pair of registers.
     constexpr int NF = 4 * NRB, LA = 2;
     f16x8_t ring[LA + 1];
     auto read_a = [&](int idx) -> f16x8_t {
@@ -338,6 +338,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     for (int i = 0; i < LA; ++i) ring[i] = read_a(i);
     f16x8_t b0 = bstep(cur0, cur0b, s0, 0);
     f16x8_t b1 = bstep(cur1, cur1b, s1, 0);
+    f16x8_t n0 = b0, n1 = b1;
 #pragma unroll
     for (int idx = 0; idx < NF; ++idx) {
       if (idx + LA < NF) ring[(idx + LA) % (LA + 1)] = read_a(idx + LA);
@@ -345,16 +346,21 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
       __builtin_amdgcn_sched_barrier(0);
       const int s = idx / NRB, rb = idx % NRB;
       // gate/up: weights as the first operand (output-major accumulators, see the epilogue)
-      if constexpr (GATEUP) {
+      if constexpr (GATEUP)
         acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, ring[idx % (LA + 1)], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, ring[idx % (LA + 1)], acc[rb][1], 0, 0, 0);
-      } else {
+      else
         acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[idx % (LA + 1)], b0, acc[rb][0], 0, 0, 0);
+      // the next step's fragments are unpacked between this step's MFMAs (column block 0
+      // after row block 0, column block 1 after row block NRB / 2) into n0 / n1
+      if (s < 3 && rb == 0) n0 = bstep(cur0, cur0b, s0, s + 1);
+      if constexpr (GATEUP)
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, ring[idx % (LA + 1)], acc[rb][1], 0, 0, 0);
+      else
         acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[idx % (LA + 1)], b1, acc[rb][1], 0, 0, 0);
-      }
+      if (s < 3 && rb == NRB / 2) n1 = bstep(cur1, cur1b, s1, s + 1);
       if (rb == NRB - 1 && s < 3) {
-        b0 = bstep(cur0, cur0b, s0, s + 1);
-        b1 = bstep(cur1, cur1b, s1, s + 1);
+        b0 = n0;
+        b1 = n1;
       }
     }
   };
