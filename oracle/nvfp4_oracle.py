@@ -52,6 +52,8 @@ Readings where the pages are silent (each listed in the design notes):
     [0, E) are dropped;
   * the shared expert is an NVFP4 SwiGLU expert of the routed experts' shape,
     applied to every token with weight 1 and added before the final rounding;
+  * W4A4: activations quantized per row to NVFP4 with an FP32 row scale (the rule is
+    stated beside quant_rows_nvfp4);
   * W4A8: per row s = fp32(absmax / 127) by an fp32 division, q = clamp(
     rint_even(fp32(x / s)), -127, 127), s = q = 0 for an all-zero row; the
     down projection's input h is quantized per (token, slot) row the same
@@ -407,6 +409,135 @@ def w4a8_down_from_codes(qh: np.ndarray, sh: np.ndarray, pairs: np.ndarray, laye
     T, k = ids.shape
     pairs = np.asarray(pairs, dtype=np.int64)
     hh = np.asarray(qh, dtype=np.int8).astype(np.float64) * np.asarray(sh, dtype=np.float32).astype(np.float64)[:, None]
+    row_of = {t: t for t in range(T)} if rows is None else {int(t): i for i, t in enumerate(rows)}
+    out = np.zeros((len(row_of), layer.H), dtype=np.float64)
+    ex = ids.reshape(-1)[pairs]
+    for e in np.unique(ex):
+        if e < 0 or e >= layer.E:
+            continue
+        sel = np.nonzero(ex == e)[0]
+        _, _, _, _, Wd, gd = _expert(layer, int(e))
+        Y = (hh[sel] @ Wd.T) * gd
+        for i, r in enumerate(sel):
+            p = int(pairs[r])
+            out[row_of[p // k]] += float(w[p // k, p % k]) * Y[i]
+    return out
+
+
+# ----------------------------------------------------------------- W4A4
+# [S-NVFP4] W4A8 bullet: llama.cpp builds the NVFP4 prompt path as FP4 x FP4, i.e. the
+# activations are quantized to NVFP4 too. The pages give no activation quantization rule;
+# the reading taken (r9): per row an FP32 scale g = fp32(absmax / 2688) (2688 = 6 * 448, so
+# the largest block scale is 448), per 16 inputs an E4M3 scale s = E4M3_RNE(fp32(blockmax /
+# fp32(6 g))) (saturating at 448), and per input the E2M1 code nearest to fp32(v / fp32(s g))
+# with ties to the even code (saturating at 6), its sign bit set for v < 0. A zero row has
+# g = 0 and all codes and scales 0; a zero or underflowed block scale gives zero codes. A row
+# holding a NaN gets g = NaN, else one holding an infinity g = +inf, with zero codes and
+# scales, so the dequantized row (code * s * g) is NaN and propagates.
+
+E4M3_POS = E4M3_TABLE[:127]          # the finite non-negative E4M3 values, codes 0..126, ascending
+E2M1_POS = E2M1_TABLE[:8]            # 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7)
+
+
+def _rne_table(t: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the table value nearest to each t >= 0 (table ascending, index parity =
+    mantissa parity), ties to the even index; values above the last entry take the last."""
+    t = np.asarray(t, dtype=np.float64)
+    hi = np.clip(np.searchsorted(table, t, side="left"), 0, len(table) - 1)
+    lo = np.clip(hi - 1, 0, len(table) - 1)
+    dlo, dhi = t - table[lo], table[hi] - t
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return np.where(t >= table[-1], len(table) - 1, pick)
+
+
+def quant_rows_nvfp4(v32: np.ndarray):
+    """Rows of fp32 values [R][K] (K % 16 == 0) -> (codes uint8 [R][K/2], two per byte, low
+    nibble first; scales uint8 [R][K/16] E4M3; g float32 [R]) by the r9 rule above."""
+    v = np.asarray(v32, dtype=np.float32)
+    R, K = v.shape
+    nib = np.zeros((R, K), dtype=np.uint8)
+    sc = np.zeros((R, K // GROUP), dtype=np.uint8)
+    g = np.zeros(R, dtype=np.float32)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        for r in range(R):
+            row = v[r]
+            if np.isnan(row).any():
+                g[r] = np.float32(np.nan)
+                continue
+            amax = np.float32(np.max(np.abs(row))) if K else np.float32(0)
+            if np.isinf(amax):
+                g[r] = np.float32(np.inf)
+                continue
+            if amax == 0:
+                continue
+            gr = np.float32(amax / np.float32(2688.0))
+            g[r] = gr
+            d6 = np.float32(np.float32(6.0) * gr)
+            for b in range(K // GROUP):
+                blk = row[b * GROUP:(b + 1) * GROUP]
+                t = np.float32(np.float32(np.max(np.abs(blk))) / d6) if d6 > 0 else np.float32(0)
+                si = int(_rne_table(np.float64(t), E4M3_POS))
+                sc[r, b] = si
+                sv = np.float32(E4M3_POS[si])
+                den = np.float32(sv * gr)
+                if den == 0:
+                    continue
+                q = (blk / den).astype(np.float32)
+                mag = _rne_table(np.abs(q).astype(np.float64), E2M1_POS).astype(np.uint8)
+                nib[r, b * GROUP:(b + 1) * GROUP] = mag | np.where(blk < 0, 8, 0).astype(np.uint8)
+    return pack_codes(nib), sc, g
+
+
+def dequant_rows_nvfp4(codes: np.ndarray, scales: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """code * scale * g in float64 (exact: 2 + 4 + 24 significant bits); a NaN or infinite
+    row scale with zero codes gives NaN (0 * inf)."""
+    with np.errstate(invalid="ignore"):
+        return dequant(codes, scales) * np.asarray(g, dtype=np.float32).astype(np.float64)[:, None]
+
+
+def w4a4_activations(x_bf16_bits: np.ndarray) -> np.ndarray:
+    """x (bf16) -> per-row NVFP4 quantization -> dequantized x in float64."""
+    return dequant_rows_nvfp4(*quant_rows_nvfp4(bf16_to_f64(x_bf16_bits).astype(np.float32)))
+
+
+def w4a4_expert_ffn(xq: np.ndarray, Wg, gg, Wu, gu, Wd, gd) -> np.ndarray:
+    """Expert FFN on already-dequantized NVFP4 activations: h (fp32) is quantized per row
+    to NVFP4 by the same rule, and the down projection consumes the dequantized h."""
+    h = w4a8_hidden(xq, Wg, gg, Wu, gu)
+    return (dequant_rows_nvfp4(*quant_rows_nvfp4(h)) @ Wd.T) * gd
+
+
+def moe_w4a4(x_bf16_bits: np.ndarray, layer, ids, w, rows=None) -> np.ndarray:
+    """W4A4 MoE: both expert GEMMs take per-row NVFP4 activations (reading r9)."""
+    return moe_grouped(w4a4_activations(x_bf16_bits), layer, ids, w, rows=rows, ffn=w4a4_expert_ffn)
+
+
+def w4a4_pair_hidden(x_bf16_bits: np.ndarray, layer, ids, rows=None):
+    """For the routed pairs of the given token rows, expert by expert in route() order:
+    (expert id, sorted pair indices into ids[rows], fp32 hidden rows h)."""
+    xh = w4a4_activations(x_bf16_bits)
+    T, k = ids.shape
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    offsets, sp = route(ids[rows], layer.E)
+    out = []
+    for e in range(layer.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        pairs = sp[a:b]
+        Wg, gg, Wu, gu, _, _ = _expert(layer, e)
+        out.append((e, pairs, w4a8_hidden(xh[rows[pairs // k]], Wg, gg, Wu, gu)))
+    return out
+
+
+def w4a4_down_from_codes(qc: np.ndarray, qs: np.ndarray, qg: np.ndarray, pairs: np.ndarray, layer,
+                         ids: np.ndarray, w: np.ndarray, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The W4A4 down projection and combine on given NVFP4 hidden rows (codes, scales, row
+    scales; row i belongs to pair pairs[i] = t*k + j): out[t] += w[t][j] * gamma_d * h_hat .
+    Wd_e^T. Returns float64 [T][H], or only the given token rows."""
+    T, k = ids.shape
+    pairs = np.asarray(pairs, dtype=np.int64)
+    hh = dequant_rows_nvfp4(qc, qs, qg)
     row_of = {t: t for t in range(T)} if rows is None else {int(t): i for i, t in enumerate(rows)}
     out = np.zeros((len(row_of), layer.H), dtype=np.float64)
     ex = ids.reshape(-1)[pairs]

@@ -795,3 +795,147 @@ def test_shared_expert_negative_controls(monkeypatch):
         test_shared_expert_identity_closed_form()
     monkeypatch.undo()
     assert O.moe_with_shared is real
+
+
+# ------------------------------------------------------------------ W4A4 (NVFP4 activations)
+def _nvfp4_fixture_row():
+    x = np.zeros((1, 32), np.float32)
+    x[0, :8] = [6, 3, 1.5, 0.75, -0.25, 0.2, 5, -5]
+    x[0, 15] = 0.3
+    x[0, 16:19] = [0.3, -0.15, 0.075]
+    return x
+
+
+def test_quant_nvfp4_fixture():
+    """The hand-worked row of tests/golden/quant_nvfp4_cases.txt."""
+    line = [ln for ln in read_golden("quant_nvfp4_cases.txt") if ln.startswith("scales")][0]
+    sc_hex, co_hex = line[len("scales"):].split("| codes")
+    codes, scales, g = O.quant_rows_nvfp4(_nvfp4_fixture_row())
+    assert [int(b, 16) for b in sc_hex.split()] == list(scales[0])
+    assert [int(b, 16) for b in co_hex.split()] == list(codes[0])
+    assert g[0] == np.float32(6.0) / np.float32(2688.0)
+
+
+def _nearest_even(t, values):
+    """Brute force over exact rationals: index of the value nearest to t, ties to the even
+    index, values above the last to the last."""
+    tf = Fraction(float(t))
+    if tf >= Fraction(float(values[-1])):
+        return len(values) - 1
+    best = None
+    for i, v in enumerate(values):
+        d = abs(Fraction(float(v)) - tf)
+        if best is None or d < best[0] or (d == best[0] and i % 2 == 0):
+            best = (d, i)
+    return best[1]
+
+
+def test_quant_nvfp4_bruteforce():
+    """Random rows (with zeros, ties, tiny and saturating values): every scale byte is the
+    E4M3 value nearest to fp32(blockmax / fp32(6 g)) with ties to even, and every code the
+    E2M1 magnitude nearest to fp32(v / fp32(s g)) with ties to even (saturating at 6), found
+    by exact rational brute force; the sign bit follows v < 0."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((6, 64)) * np.exp2(rng.integers(-30, 30, size=(6, 1)))).astype(np.float32)
+    x[1, 16:32] = 0                       # a zero group
+    x[2, :] *= np.float32(1e-38)          # tiny values: scales underflow E4M3
+    x[3, 5] = x[3].max() * 1.001 if x[3].max() > 0 else 1.0
+    x[4, 0:16] = np.float32(0.25) * np.sign(x[4, 0:16] + 1e-30)  # ties on the E2M1 grid
+    x[4, 16] = 6.0
+    codes, scales, g = O.quant_rows_nvfp4(x)
+    nib = O.unpack_codes(codes)
+    e4 = [float(v) for v in O.E4M3_TABLE[:127]]
+    e2 = [float(v) for v in O.E2M1_TABLE[:8]]
+    for r in range(x.shape[0]):
+        amax = np.float32(np.abs(x[r]).max())
+        gr = np.float32(amax / np.float32(2688.0))
+        assert g[r] == gr
+        d6 = np.float32(np.float32(6.0) * gr)
+        for b in range(4):
+            blk = x[r, 16 * b:16 * b + 16]
+            t = np.float32(np.float32(np.abs(blk).max()) / d6) if d6 > 0 else np.float32(0)
+            assert scales[r, b] == _nearest_even(t, e4)
+            sv = np.float32(O.E4M3_TABLE[scales[r, b]])
+            den = np.float32(sv * gr)
+            for k in range(16):
+                c = int(nib[r, 16 * b + k])
+                if den == 0:
+                    assert c == 0
+                    continue
+                q = np.float32(blk[k] / den)
+                assert (c & 7) == _nearest_even(abs(q), e2), (r, b, k, q)
+                assert (c >> 3) == (1 if blk[k] < 0 else 0)
+
+
+def test_quant_nvfp4_zero_and_nonfinite_rows():
+    x = np.zeros((3, 32), np.float32)
+    x[1, 3] = np.nan
+    x[2, 7] = -np.inf
+    codes, scales, g = O.quant_rows_nvfp4(x)
+    assert not codes.any() and not scales.any()
+    assert g[0] == 0 and np.isnan(g[1]) and g[2] == np.inf
+    deq = O.dequant_rows_nvfp4(codes, scales, g)
+    assert not deq[0].any() and np.isnan(deq[1]).all() and np.isnan(deq[2]).all()
+
+
+def test_w4a4_ffn_composition_and_down_from_codes():
+    """moe_w4a4 is the MoE over the dequantized NVFP4 activations with the hidden rows
+    requantized the same way (composition of pinned pieces), and w4a4_down_from_codes on
+    the oracle's own hidden codes reproduces it."""
+    lay = W.draw_layer(15, E=5, H=64, I=48)
+    xb = W.draw_activations(15, 9, 64)
+    ids = W.draw_routing_zipf(15, 9, 5, 3)
+    w = W.draw_router_weights(15, 9, 3)
+    got = O.moe_w4a4(xb, lay, ids, w)
+    xq = O.dequant_rows_nvfp4(*O.quant_rows_nvfp4(O.bf16_to_f64(xb).astype(np.float32)))
+    ref = np.zeros_like(got)
+    for t in range(9):
+        for j in range(3):
+            e = int(ids[t, j])
+            g = O.linear(xq[t:t + 1], lay.gate.codes[e], lay.gate.scales[e], lay.gate.gamma[e])
+            u = O.linear(xq[t:t + 1], lay.up.codes[e], lay.up.scales[e], lay.up.gamma[e])
+            h = (O.silu(g) * u).astype(np.float32)
+            hq = O.dequant_rows_nvfp4(*O.quant_rows_nvfp4(h))
+            ref[t] += float(w[t, j]) * O.linear(hq, lay.down.codes[e], lay.down.scales[e], lay.down.gamma[e])[0]
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+    pairs, hs = [], []
+    for e, pe, h in O.w4a4_pair_hidden(xb, lay, ids):
+        pairs.append(pe)
+        hs.append(h)
+    qc, qs, qg = O.quant_rows_nvfp4(np.concatenate(hs))
+    again = O.w4a4_down_from_codes(qc, qs, qg, np.concatenate(pairs), lay, ids, w)
+    assert np.abs(again - got).max() <= 1e-12 * np.abs(got).max()
+
+
+def test_quant_nvfp4_negative_controls(monkeypatch):
+    """Ties away from zero, a missing row scale, or a truncating E4M3 conversion fail a pin."""
+    real = O.nvfp4_oracle._rne_table
+
+    def ties_up(t, table):
+        t = np.asarray(t, dtype=np.float64)
+        hi = np.clip(np.searchsorted(table, t, side="left"), 0, len(table) - 1)
+        lo = np.clip(hi - 1, 0, len(table) - 1)
+        pick = np.where(t - table[lo] < table[hi] - t, lo, hi)
+        return np.where(t >= table[-1], len(table) - 1, pick)
+
+    def truncating(t, table):
+        t = np.asarray(t, dtype=np.float64)
+        idx = np.clip(np.searchsorted(table, t, side="right") - 1, 0, len(table) - 1)
+        return np.where(t >= table[-1], len(table) - 1, idx)
+
+    for bad in (ties_up, truncating):
+        monkeypatch.setattr(O.nvfp4_oracle, "_rne_table", bad)
+        with pytest.raises(AssertionError):
+            test_quant_nvfp4_fixture()
+        monkeypatch.undo()
+    assert O.nvfp4_oracle._rne_table is real
+
+    def no_row_scale(v32):
+        codes, scales, g = real_q(v32)
+        return real_q(np.asarray(v32, np.float32) / np.where(g > 0, g, 1)[:, None] / np.float32(2688.0))
+
+    real_q = O.nvfp4_oracle.quant_rows_nvfp4
+    monkeypatch.setattr(O, "quant_rows_nvfp4", no_row_scale)
+    with pytest.raises(AssertionError):
+        test_quant_nvfp4_fixture()
+    monkeypatch.undo()
