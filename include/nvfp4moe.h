@@ -19,6 +19,10 @@
  *   - W4A8 prompt path: activations quantized per row to int8 with an FP32 scale
  *     absmax / 127 before each expert GEMM ("Strata NVFP4" README, "How it differs from
  *     upstream Strata": an int8 (W4A8) prompt path that keeps 8-bit activations).
+ *   - W4A4 prompt path: activations quantized per row to NVFP4 before each expert GEMM
+ *     ("Strata NVFP4" README, "How it differs from upstream Strata": llama.cpp's NVFP4
+ *     prompt GEMM multiplies FP4 activations by FP4 weights, the path W4A8 is measured
+ *     against; its quantization rule is not on the pages, see nvfp4_quant_rows_nvfp4).
  *   - Mixed packs: the down projection of a layer may be Q8_0 instead of NVFP4 ("Strata
  *     NVFP4" README, the re-quantized experts pack: Q8_0 down projections in 27 of the 48
  *     layers). The pages name the format only; its element rule here is GGML's: blocks
@@ -85,8 +89,15 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1, NVFP4_F16 = 2 } nvfp4_dtype;
  *                       NVFP4_ACT_W4A8_F16, which gives the same result to FP32 rounding.
  *   NVFP4_ACT_W4A8_F16  the same int8 activations and the same result, computed on fp16
  *                       matrix cores (int8 values are exact in fp16; x and h are stored
- *                       as 1-byte codes and widened while staged). */
-typedef enum { NVFP4_ACT_BF16 = 0, NVFP4_ACT_W4A8 = 1, NVFP4_ACT_W4A8_F16 = 2 } nvfp4_act;
+ *                       as 1-byte codes and widened while staged).
+ *   NVFP4_ACT_W4A4      x and h quantized per row to NVFP4 by the rule of
+ *                       nvfp4_quant_rows_nvfp4 (E2M1 codes, an E4M3 scale per 16 inputs, an
+ *                       fp32 scale per row); both GEMMs run on fp16 matrix cores, where
+ *                       code * block scale is exact for activations and weights alike, and
+ *                       the row scale multiplies at the FP32 accumulator. ("Strata NVFP4"
+ *                       README: the prompt path that multiplies FP4 activations by FP4
+ *                       weights.) */
+typedef enum { NVFP4_ACT_BF16 = 0, NVFP4_ACT_W4A8 = 1, NVFP4_ACT_W4A8_F16 = 2, NVFP4_ACT_W4A4 = 3 } nvfp4_act;
 
 /* Weight format of a projection: NVFP4 (every projection) or Q8_0 (down only). */
 typedef enum { NVFP4_FMT_NVFP4 = 0, NVFP4_FMT_Q8_0 = 1 } nvfp4_format;
@@ -143,6 +154,26 @@ int nvfp4_moe_route(const int32_t* topk_ids, int32_t T, int32_t topk, int32_t E,
  * Errors: EINVAL for null pointers, rows < 0, cols < 1. */
 int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, int8_t* q,
                         float* scale, void* stream);
+
+/* Per-row NVFP4 quantization (the W4A4 activation rule; "Strata NVFP4" README: FP4
+ * activations on the prompt path; the NVFP4 element formats above. The pages fix the
+ * formats, not this rule: the reading here is the plainest one that fills every code range):
+ *   g[r] = fp32(absmax_r / 2688) by an fp32 division (2688 = 6 * 448, the largest
+ *     E2M1 * E4M3 product), so the row's largest 16-group scale lands on 448;
+ *   scale byte of group b = the E4M3 value nearest to fp32(blockmax / fp32(6 * g[r])),
+ *     ties to the even code, saturating at 448 (0x7E);
+ *   code of x[r][c] = the E2M1 magnitude nearest to |fp32(x / fp32(s * g[r]))|, ties to the
+ *     even code, saturating at 6, with the sign bit set for x < 0;
+ * so x ~ code * scale * g. A zero row, or a block whose scale rounds to zero, gives zero
+ * codes (and g = 0 for a zero row); a row holding a NaN gets g = NaN, else one holding an
+ * infinity g = +inf, with zero codes and scales (so code * scale * g is NaN there).
+ * x [rows][cols] in x_dtype (F32 or BF16), 16-byte aligned; codes uint8 [rows][cols/2] (two
+ * per byte, the even input in the low nibble), 8-byte aligned; scales uint8
+ * [rows][cols/16]; g fp32 [rows]. Device pointers, the caller's memory.
+ * Errors: EINVAL for null or misaligned pointers, rows < 0, cols not a positive multiple
+ * of 16, an x_dtype other than F32 and BF16. */
+int nvfp4_quant_rows_nvfp4(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* codes,
+                           uint8_t* scales, float* g, void* stream);
 
 /* Decode (small token batches): the full routed-expert projection above for
  * 1 <= T <= 8 tokens, with FP32 arithmetic throughout and h kept in fp32 ("#1858
@@ -265,14 +296,18 @@ int nvfp4_moe_decode_shared(const void* x, int32_t x_dtype, int32_t T, int32_t H
  *   EXPERT_OFFSETS  int32 [E+1]            stage 0 (the routing of nvfp4_moe_route)
  *   SORTED_PAIRS    int32 [T*topk]         stage 0
  *   PAIR_POSITION   int32 [T*topk]         stage 0: sorted position of pair p, -1 if dropped
- *   X_STAGED        BF16: fp16 [T][H] (x * 2^xexp[t]); W4A8*: int8 codes [T][H]  stage 0
- *   X_ROWSCALE      BF16: int32 xexp [T];  W4A8*: fp32 row scales [T]           stage 0
- *   H               BF16: fp16 [P][I] in sorted order, h * 2^hexp[pos][I-block]; W4A8*:
- *                   fp32 [P][I]                                                   stage 1
- *   H_EXP           BF16: int32 [P][I/256] (I/128 when I % 256 != 0); W4A8*: none stage 1
+ *   X_STAGED        BF16: fp16 [T][H] (x * 2^xexp[t]); W4A8*: int8 codes [T][H];
+ *                   W4A4: NVFP4 codes [T][H/2]                                     stage 0
+ *   X_ROWSCALE      BF16: int32 xexp [T];  W4A8*, W4A4: fp32 row scales [T]       stage 0
+ *   X_BLOCKSCALE    W4A4: E4M3 [T][H/16]; others: none                            stage 0
+ *   H               BF16: fp16 [P][I] in sorted order, h * 2^hexp[pos][I-block]; W4A8*,
+ *                   W4A4: fp32 [P][I]                                             stage 1
+ *   H_EXP           BF16: int32 [P][I/256] (I/128 when I % 256 != 0); others: none stage 1
  *   H_Q             W4A8*: int8 codes of h [P][I] (the per-row rule of
- *                   nvfp4_quant_rows_i8 applied to the fp32 H); BF16: none         stage 1
- *   H_SCALE         W4A8*: fp32 [P]; BF16: none                                    stage 1
+ *                   nvfp4_quant_rows_i8 applied to the fp32 H); W4A4: NVFP4 codes
+ *                   [P][I/2] (nvfp4_quant_rows_nvfp4 on H); BF16: none             stage 1
+ *   H_SCALE         W4A8*, W4A4: fp32 [P]; BF16: none                              stage 1
+ *   H_BLOCKSCALE    W4A4: E4M3 [P][I/16]; others: none                            stage 1
  *   Y               fp32 [P][H], each pair's down row times gamma_down and its weight stage 2
  * Errors: EINVAL for null outputs, bad sizes, unknown act or region. */
 typedef enum {
@@ -285,7 +320,9 @@ typedef enum {
   NVFP4_WS_H_EXP = 6,
   NVFP4_WS_H_Q = 7,
   NVFP4_WS_H_SCALE = 8,
-  NVFP4_WS_Y = 9
+  NVFP4_WS_Y = 9,
+  NVFP4_WS_X_BLOCKSCALE = 10,
+  NVFP4_WS_H_BLOCKSCALE = 11
 } nvfp4_ws_region;
 int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act,
                                        int32_t region, size_t* offset, size_t* bytes);
@@ -294,8 +331,9 @@ int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t 
  * Arguments, validation and workspace are those of the full call; running the stages
  * in order on one stream with the same arguments and workspace is the full call.
  * Decode stages: 0 gate/up + SwiGLU (h into the workspace), 1 down + combine.
- * Prefill stages: 0 zero the accumulator, route, stage the activations (fp16, or int8
- * codes and row scales for W4A8); 1 gate/up + SwiGLU (W4A8: then requantize h);
+ * Prefill stages: 0 zero the accumulator, route, stage the activations (fp16, int8 codes
+ * and row scales for W4A8, NVFP4 codes and scales for W4A4); 1 gate/up + SwiGLU (W4A8,
+ * W4A4: then requantize h);
  * 2 down, scaled per pair; 3 top-k combine in slot order and the final rounding.
  * Errors: those of the full call, and EINVAL for a stage outside that range. */
 int nvfp4_moe_decode_stage(int32_t stage, const void* x, int32_t x_dtype, int32_t T, int32_t H,

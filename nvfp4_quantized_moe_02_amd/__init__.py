@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     moe_decode_noalloc,
     moe_prefill,
     quant_rows_i8,
+    quant_rows_nvfp4,
     route,
     router_topk,
     router_workspace_size,

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libnvfp4moe.so"
 
 DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
-ACT = {"bf16": 0, "w4a8": 1, "w4a8_f16": 2}
+ACT = {"bf16": 0, "w4a8": 1, "w4a8_f16": 2, "w4a4": 3}
 ISA = {"auto": 0, "portable": 1, "avx2": 2, "avx512": 3}
 
 _lib = None
@@ -59,6 +59,9 @@ _SIGS = {
                                        ctypes.c_void_p]),
     "nvfp4_quant_rows_i8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "nvfp4_quant_rows_nvfp4": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
     "nvfp4_router_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 2),
     "nvfp4_router_topk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -278,6 +281,19 @@ def quant_rows_i8(x: torch.Tensor):
     return q, s
 
 
+def quant_rows_nvfp4(x: torch.Tensor):
+    """x [rows][cols] float32 or bfloat16 -> (codes uint8 [rows][cols/2], scales uint8
+    [rows][cols/16] E4M3, g float32 [rows]) by the library's per-row NVFP4 rule."""
+    lib = load_library()
+    rows, cols = int(x.shape[0]), int(x.shape[1])
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    g = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check("nvfp4_quant_rows_nvfp4", lib.nvfp4_quant_rows_nvfp4(_ptr(x), DTYPE[x.dtype], rows, cols, _ptr(codes),
+                                                                _ptr(scales), _ptr(g), _stream(x.device)))
+    return codes, scales, g
+
+
 def router_workspace_size(T: int, E: int) -> int:
     return int(load_library().nvfp4_router_workspace_size(T, E))
 
@@ -311,7 +327,7 @@ def prefill_workspace_size(T: int, H: int, I: int, E: int, topk: int, act: str =
 
 
 WS_REGION = {"expert_offsets": 0, "sorted_pairs": 1, "pair_position": 2, "x_staged": 3, "x_rowscale": 4,
-             "h": 5, "h_exp": 6, "h_q": 7, "h_scale": 8, "y": 9}
+             "h": 5, "h_exp": 6, "h_q": 7, "h_scale": 8, "y": 9, "x_blockscale": 10, "h_blockscale": 11}
 
 
 def prefill_workspace_region(T: int, H: int, I: int, E: int, topk: int, act: str, region: str):

@@ -86,14 +86,16 @@ RouteLayout route_layout(int64_t P, int E, bool with_tiles, Carver& c) {
   return l;
 }
 
-// Prefill workspace regions (act BF16 | W4A8): staged x (fp16 | int8) and its per-row
-// exponents (int32) | scales (fp32); h in sorted-pair order (fp16 scaled per gate/up block
-// | fp32) with the block exponents (int32 [P][blocks] | absent); the requantized h (absent |
-// int8 [P][I] and fp32 [P] scales); y, each pair's scaled down row (fp32 [P][H]).
+// Prefill workspace regions (act BF16 | W4A8 | W4A4): staged x (fp16 | int8 | NVFP4 codes
+// [T][H/2]) and its per-row exponents (int32) | scales (fp32) | scales (fp32), the W4A4
+// block scales (E4M3 [T][H/16]); h in sorted-pair order (fp16 scaled per gate/up block |
+// fp32 | fp32) with the block exponents (int32 [P][blocks] | absent | absent); the
+// requantized h (absent | int8 [P][I] | codes [P][I/2]) with its row scales (fp32 [P]) and
+// the W4A4 block scales (E4M3 [P][I/16]); y, each pair's scaled down row (fp32 [P][H]).
 struct PrefillLayout {
   RouteLayout r;
-  size_t xa, xs, h, hexp, qh, sh, y, end;
-  size_t xa_b, xs_b, h_b, hexp_b, qh_b, sh_b, y_b;
+  size_t xa, xs, xbs, h, hexp, qh, sh, qhbs, y, end;
+  size_t xa_b, xs_b, xbs_b, h_b, hexp_b, qh_b, sh_b, qhbs_b, y_b;
 };
 
 PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
@@ -101,20 +103,25 @@ PrefillLayout prefill_layout(int T, int H, int I, int E, int topk, int act) {
   PrefillLayout l;
   const int64_t P = (int64_t)T * topk;
   l.r = route_layout(P, E, true, c);
-  const bool w4a8 = act != NVFP4_ACT_BF16;
-  l.xa_b = (size_t)T * H * (w4a8 ? 1 : 2);
+  const bool rowq = act != NVFP4_ACT_BF16;  // activations quantized per row
+  const bool f4 = act == NVFP4_ACT_W4A4;
+  l.xa_b = f4 ? (size_t)T * H / 2 : (size_t)T * H * (rowq ? 1 : 2);
   l.xs_b = (size_t)T * 4;
-  l.h_b = (size_t)P * I * (w4a8 ? 4 : 2);
-  l.hexp_b = w4a8 ? 0 : (size_t)P * gateup_blocks(I) * 4;
-  l.qh_b = w4a8 ? (size_t)P * I : 0;
-  l.sh_b = w4a8 ? (size_t)P * 4 : 0;
+  l.xbs_b = f4 ? (size_t)T * H / 16 : 0;
+  l.h_b = (size_t)P * I * (rowq ? 4 : 2);
+  l.hexp_b = rowq ? 0 : (size_t)P * gateup_blocks(I) * 4;
+  l.qh_b = rowq ? (size_t)P * I / (f4 ? 2 : 1) : 0;
+  l.sh_b = rowq ? (size_t)P * 4 : 0;
+  l.qhbs_b = f4 ? (size_t)P * I / 16 : 0;
   l.y_b = (size_t)P * H * 4;
   l.xa = c.take(l.xa_b);
   l.xs = c.take(l.xs_b);
+  l.xbs = c.take(l.xbs_b);
   l.h = c.take(l.h_b);
   l.hexp = c.take(l.hexp_b);
   l.qh = c.take(l.qh_b);
   l.sh = c.take(l.sh_b);
+  l.qhbs = c.take(l.qhbs_b);
   l.y = c.take(l.y_b);
   l.end = c.off;
   return l;
@@ -207,6 +214,16 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
   if (rows > 0x7fffffff) return NVFP4_EUNSUPPORTED;
   (void)hipGetLastError();
   return hip_status(launch_quant_rows(x, x_dtype, rows, cols, q, scale, as_stream(stream)));
+}
+
+int nvfp4_quant_rows_nvfp4(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* codes,
+                           uint8_t* scales, float* g, void* stream) {
+  if (!x || !codes || !scales || !g || rows < 0 || cols < 16 || cols % 16 != 0) return NVFP4_EINVAL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(g, 4)) return NVFP4_EINVAL;
+  if (rows > 0x7fffffff) return NVFP4_EUNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(launch_quant_rows_nvfp4(x, x_dtype, rows, cols, codes, scales, g, as_stream(stream)));
 }
 
 // Router workspace: a 256-byte header (the completion counter of the single-launch path,
@@ -387,7 +404,7 @@ int nvfp4_moe_decode_noalloc(const void* x, int32_t x_dtype, int32_t T, int32_t 
 
 size_t nvfp4_moe_prefill_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
-  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return 0;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A4) return 0;
   return prefill_layout(T, H, I, E, topk, act).end;
 }
 
@@ -403,7 +420,7 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   if (st != NVFP4_OK) return st;
   if ((st = check_shared(shared, gate, up, down)) != NVFP4_OK) return st;
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_EINVAL;
-  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A4) return NVFP4_EINVAL;
   if (x_dtype != NVFP4_BF16) return NVFP4_EUNSUPPORTED;
   const int I = gate->N;
   const int E = shared ? E0 + 1 : E0, topk = shared ? topk0 + 1 : topk0;
@@ -427,11 +444,14 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
   int32_t* hdr = at<int32_t>(ws, l.r.hdr);
   TileDesc* tiles = at<TileDesc>(ws, l.r.tiles);
   void* xa = at<void>(ws, l.xa);
-  const int mode = act == NVFP4_ACT_BF16 ? 0 : 1;
-  float* xscale = mode == 1 ? at<float>(ws, l.xs) : nullptr;
+  // GEMM activation mode: 0 fp16 (BF16), 1 int8 (W4A8, W4A8_F16), 2 NVFP4 (W4A4)
+  const int mode = act == NVFP4_ACT_BF16 ? 0 : act == NVFP4_ACT_W4A4 ? 2 : 1;
+  float* xscale = mode != 0 ? at<float>(ws, l.xs) : nullptr;
   int32_t* xexp = mode == 0 ? at<int32_t>(ws, l.xs) : nullptr;
   int32_t* hexp = mode == 0 ? at<int32_t>(ws, l.hexp) : nullptr;
-  float* sh = mode == 1 ? at<float>(ws, l.sh) : nullptr;
+  float* sh = mode != 0 ? at<float>(ws, l.sh) : nullptr;
+  uint8_t* xbs = mode == 2 ? at<uint8_t>(ws, l.xbs) : nullptr;
+  uint8_t* qhbs = mode == 2 ? at<uint8_t>(ws, l.qhbs) : nullptr;
   for (int stage = first; stage <= last; ++stage) {
     hipError_t e = hipSuccess;
     if (stage == 0) {  // route, stage the activations
@@ -443,24 +463,29 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
         e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s, x, xa, xexp, T, H);
       } else if (e == hipSuccess) {
         e = launch_route(topk_ids, P, E, offsets, sorted, rw, kTileM, s);
-        if (e == hipSuccess) e = launch_quant_rows(x, NVFP4_BF16, T, H, static_cast<int8_t*>(xa), xscale, s);
+        if (e == hipSuccess && mode == 1)
+          e = launch_quant_rows(x, NVFP4_BF16, T, H, static_cast<int8_t*>(xa), xscale, s);
+        else if (e == hipSuccess)
+          e = launch_quant_rows_nvfp4(x, NVFP4_BF16, T, H, static_cast<uint8_t*>(xa), xbs, xscale, s);
       }
-    } else if (stage == 1) {  // gate/up + SwiGLU (W4A8: then requantize h per row)
+    } else if (stage == 1) {  // gate/up + SwiGLU (W4A8, W4A4: then requantize h per row)
       if (act == NVFP4_ACT_W4A8)
         e = launch_gemm_gateup_i8(static_cast<const int8_t*>(xa), xscale, sorted, offsets, tiles, hdr + 1,
                                   l.r.max_tiles, topk, H, I, ga, ua, at<float>(ws, l.h), s);
       else
-        e = launch_gemm_gateup(mode, xa, xscale, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H,
+        e = launch_gemm_gateup(mode, xa, xscale, xbs, xexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H,
                                I, ga, ua, at<void>(ws, l.h), hexp, s);
       if (e == hipSuccess && mode == 1)
         e = launch_quant_rows(at<void>(ws, l.h), NVFP4_F32, P, I, at<int8_t>(ws, l.qh), sh, s);
+      else if (e == hipSuccess && mode == 2)
+        e = launch_quant_rows_nvfp4(at<void>(ws, l.h), NVFP4_F32, P, I, at<uint8_t>(ws, l.qh), qhbs, sh, s);
     } else if (stage == 2) {  // down, scaled by gamma_d and the router weight, per pair
       const void* hA = mode == 0 ? at<void>(ws, l.h) : at<void>(ws, l.qh);
       if (act == NVFP4_ACT_W4A8)
         e = launch_gemm_down_i8(static_cast<const int8_t*>(hA), sh, sorted, offsets, tiles, hdr + 1, l.r.max_tiles,
                                 topk, H, I, da, topk_weights, y, s);
       else
-        e = launch_gemm_down(mode, hA, sh, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
+        e = launch_gemm_down(mode, hA, sh, qhbs, hexp, sorted, offsets, tiles, hdr + 1, l.r.max_tiles, topk, H, I,
                              da, topk_weights, y, s);
     } else {  // top-k combine in slot order, one rounding to the output dtype
       e = launch_combine(y, at<int32_t>(ws, l.r.inv), T, topk, H, out, out_dtype, s);
@@ -473,7 +498,7 @@ static int prefill_impl(int first, int last, const void* x, int32_t x_dtype, int
 int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk, int32_t act,
                                        int32_t region, size_t* offset, size_t* bytes) {
   if (!offset || !bytes || T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return NVFP4_EINVAL;
-  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return NVFP4_EINVAL;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A4) return NVFP4_EINVAL;
   const PrefillLayout l = prefill_layout(T, H, I, E, topk, act);
   const size_t P = (size_t)T * topk;
   switch (region) {
@@ -487,6 +512,8 @@ int nvfp4_moe_prefill_workspace_region(int32_t T, int32_t H, int32_t I, int32_t 
     case NVFP4_WS_H_Q: *offset = l.qh; *bytes = l.qh_b; break;
     case NVFP4_WS_H_SCALE: *offset = l.sh; *bytes = l.sh_b; break;
     case NVFP4_WS_Y: *offset = l.y; *bytes = l.y_b; break;
+    case NVFP4_WS_X_BLOCKSCALE: *offset = l.xbs; *bytes = l.xbs_b; break;
+    case NVFP4_WS_H_BLOCKSCALE: *offset = l.qhbs; *bytes = l.qhbs_b; break;
     default: return NVFP4_EINVAL;
   }
   return NVFP4_OK;
@@ -503,7 +530,7 @@ int nvfp4_moe_prefill(const void* x, int32_t x_dtype, int32_t T, int32_t H, cons
 size_t nvfp4_moe_prefill_shared_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topk,
                                                int32_t act) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || topk < 1) return 0;
-  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A8_F16) return 0;
+  if (act < NVFP4_ACT_BF16 || act > NVFP4_ACT_W4A4) return 0;
   return prefill_layout(T, H, I, E + 1, topk + 1, act).end + shared_routing_bytes(T, topk);
 }
 

@@ -505,7 +505,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0 && MODE != 1) a.hdr[0] = sm.drop;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15;
   const int l8 = lane & (kDownLanes - 1);
   const int row = blockIdx.x * kRowsPerBlock + lane / kDownLanes;  // phase 2: every wave, all 8 rows
   Phase1<CHG> p1;

@@ -246,6 +246,122 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols,
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ NVFP4 row quantization
+// The W4A4 activation rule ("Strata NVFP4" README: llama.cpp's NVFP4 prompt path is FP4 x
+// FP4; the rule is this library's reading): per row g = absmax / 2688 (fp32 division;
+// 2688 = 6 * 448), per 16 inputs an E4M3 scale s = the value nearest to blockmax / (6 g)
+// (fp32 product and division) with ties to the even code, saturating at 448, and per input
+// the E2M1 code nearest to v / (s g) (fp32 product and division), ties to the even code,
+// saturating at 6, with the sign bit for v < 0. Zero rows give g = 0 and zero codes and
+// scales; a zero or underflowed block scale gives zero codes; a row holding a NaN gets
+// g = NaN, else one holding an infinity g = +inf, with zero codes and scales.
+
+// E4M3 ("FN") code of the value nearest to t (0 <= t, finite), ties to the even code,
+// t >= 448 -> 448. Subnormals are multiples of 2^-9 (codes 0..7, code 8 = 2^-6); a normal t
+// = x * 2^e with x in [1, 2) has code (e + 7) * 8 + rint((x - 1) * 8), a carry into the
+// exponent field being the next binade's first code. Every step is exact in fp32.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);
+  const int e = __builtin_amdgcn_frexp_expf(t) - 1;           // t = x * 2^e, 1 <= x < 2
+  const float x = __builtin_amdgcn_ldexpf(t, -e);
+  return (uint32_t)((e + 7) * 8) + (uint32_t)rintf((x - 1.0f) * 8.0f);
+}
+
+// E2M1 magnitude code (0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to a >= 0, ties to the
+// even code (the midpoints 0.25, 1.25, 2.5 and 5 round down, 0.75, 1.75 and 3.5 up),
+// saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_rne(float a) {
+  return a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+       : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  return (c >> 3) == 0 ? (float)c * 0.001953125f : __builtin_amdgcn_ldexpf(1.0f + (float)(c & 7) * 0.125f, (int)(c >> 3) - 7);
+}
+
+// One wave per row, one 16-input group per lane at a time (cols % 16 == 0, 16-byte
+// aligned rows): codes [rows][cols/2] (low nibble = even input), scales [rows][cols/16],
+// g [rows].
+template <int XT>
+__global__ __launch_bounds__(256) void quant_rows_nvfp4_kernel(const void* __restrict__ x, int64_t rows, int cols,
+                                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                               float* __restrict__ g) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63, ng = cols >> 4;
+  auto load16 = [&](int gi, float* v) {
+    if (XT == 1) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + r * cols) + 2 * gi;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 w = p[h];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * h + 2 * j] = bf16_lo(u[j]);
+          v[8 * h + 2 * j + 1] = bf16_hi(u[j]);
+        }
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + r * cols) + 4 * gi;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float4 a = p[h];
+        v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = a.z; v[4 * h + 3] = a.w;
+      }
+    }
+  };
+  float m = 0.f;
+  bool nan = false;
+  for (int gi = lane; gi < ng; gi += 64) {
+    float v[16];
+    load16(gi, v);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float a = fabsf(v[j]);
+      m = fmaxf(m, a);
+      nan |= a != a;
+    }
+  }
+  m = wave_max(m);
+  const bool has_nan = __ballot(nan) != 0ull;
+  const bool finite = !has_nan && m <= 3.402823466e38f;
+  const float gr = has_nan ? __builtin_nanf("") : m / 2688.0f;
+  const float d6 = 6.0f * gr;
+  for (int gi = lane; gi < ng; gi += 64) {
+    float v[16];
+    load16(gi, v);
+    uint32_t sc = 0, w[2] = {0u, 0u};
+    if (finite && d6 > 0.f) {
+      float bm = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bm = fmaxf(bm, fabsf(v[j]));
+      sc = e4m3_rne(bm / d6);
+      const float den = e4m3_value(sc) * gr;
+      if (den > 0.f) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t c = e2m1_rne(fabsf(v[j] / den)) | (v[j] < 0.f ? 8u : 0u);
+          w[j >> 3] |= c << (4 * (j & 7));
+        }
+      }
+    }
+    reinterpret_cast<uint2*>(codes + r * (cols / 2))[gi] = make_uint2(w[0], w[1]);
+    scales[r * (cols / 16) + gi] = (uint8_t)sc;
+  }
+  if (lane == 0) g[r] = gr;
+}
+
+hipError_t launch_quant_rows_nvfp4(const void* x, int x_dtype, int64_t rows, int cols, uint8_t* codes,
+                                   uint8_t* scales, float* g, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (x_dtype == 1) quant_rows_nvfp4_kernel<1><<<grid, 256, 0, st>>>(x, rows, cols, codes, scales, g);
+  else quant_rows_nvfp4_kernel<0><<<grid, 256, 0, st>>>(x, rows, cols, codes, scales, g);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ top-k combine
 // Top-k combine in a fixed order: one thread per (token, 4 outputs). Deterministic. All
 // slot loads are issued before the first add (an absent slot reads row 0 and adds nothing);

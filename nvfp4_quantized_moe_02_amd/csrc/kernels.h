@@ -74,6 +74,10 @@ hipError_t launch_linear(const void* x, int x_dtype, int T, const uint8_t* codes
                          const float* global, int N, int K, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols, int8_t* q, float* scale,
                              hipStream_t st);
+// NVFP4 activation rows (the W4A4 rule): cols % 16 == 0, 16-byte aligned rows; codes
+// [rows][cols/2], scales [rows][cols/16] E4M3, g [rows] fp32.
+hipError_t launch_quant_rows_nvfp4(const void* x, int x_dtype, int64_t rows, int cols, uint8_t* codes,
+                                   uint8_t* scales, float* g, hipStream_t st);
 // out[t][n] = sum over slots j (in order) of y[inv[t*topk + j]][n]; dropped slots skipped.
 hipError_t launch_combine(const float* y, const int32_t* inv, int T, int topk, int H, void* out, int out_dtype,
                           hipStream_t st);
@@ -130,7 +134,10 @@ constexpr int kTileM = 128;
 // act 0: fp16 activations with power-of-two row exponents (a_exp: x per token; h written
 // as fp16 with one exponent per (sorted pair, gate/up block) into hexp); act 1: int8
 // activations with fp32 row scales (a_scale), fp32 h.
-hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* a_exp,
+// act: 0 fp16 x (a_exp), 1 int8 x (a_scale), 2 NVFP4 x (codes, a_scale = row scales,
+// a_bscale = E4M3 block scales)
+hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const uint8_t* a_bscale,
+                              const int32_t* a_exp,
                               const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
                               const int32_t* tile_count, int max_tiles, int topk, int H, int I,
                               const WeightArgs& gate, const WeightArgs& up, void* h, int32_t* hexp,
@@ -148,7 +155,8 @@ hipError_t launch_gemm_down_i8(const int8_t* h, const float* h_scale, const int3
                                int topk, int H, int I, const WeightArgs& down, const float* w, float* y,
                                hipStream_t st);
 // y[pos][n] = gamma_down * w[pair] * (h[pos] . Wdown[n]) for every sorted position pos
-hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* hexp,
+hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const uint8_t* h_bscale,
+                            const int32_t* hexp,
                             const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
                             const int32_t* tile_count, int max_tiles, int topk, int H, int I,
                             const WeightArgs& down, const float* w, float* y, hipStream_t st);

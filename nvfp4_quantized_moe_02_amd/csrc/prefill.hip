@@ -134,20 +134,24 @@ struct BTile {
 // LDS); the epilogue multiplies by 2^-exponent with ldexp, so no operand overflows or
 // underflows fp16 whatever the activations' range. A_I8: int8 activations (1 byte each,
 // converted to fp16 exactly when staged) with an fp32 scale per row (the W4A8 path).
-constexpr int A_F16 = 0, A_I8 = 1;
+// A_F4: NVFP4 activations (E2M1 codes, two per byte, and an E4M3 scale per 16 inputs)
+// with an fp32 scale per row (the W4A4 path); code * scale is exact in fp16 (as for the
+// weights), so the operands are exact and the row scale multiplies at the accumulator.
+constexpr int A_F16 = 0, A_I8 = 1, A_F4 = 2;
 constexpr int kMaxHSeg = 64;  // gate/up blocks along I that the down GEMM can rescale (I <= 8192)
 
 template <bool GATEUP, int AM, int NRB, int KQ, int WPB, int GK, bool Q8>
-__device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restrict__ A, int K,
+__device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restrict__ A,
+                                          const uint8_t* __restrict__ Abs, int K,
                                           const uint8_t* b0row, const uint8_t* b1row,
                                           const uint8_t* const* bs, const WeightArgs& w0,
                                           const WeightArgs& w1, void* __restrict__ out, int ldo, char* lds,
                                           const int* s_src, const float* s_coef, const int* s_exp,
                                           const uint8_t* s_hd, int seg_shift, float* s_red,
                                           int32_t* __restrict__ hexp_out, int NB) {
-  constexpr bool HOUT32 = GATEUP && AM == A_I8;
-  constexpr int ES = AM == A_I8 ? 1 : 2;  // bytes per activation in memory
-  typedef typename std::conditional<AM == A_I8, uint2, uint4>::type ARaw;
+  constexpr bool HOUT32 = GATEUP && AM != A_F16;
+  // A_F4 raw chunk: x = the 8 codes, y = the K-block's 4 scale bytes
+  typedef typename std::conditional<AM == A_F16, uint4, uint2>::type ARaw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int nkb = K / KBLK;
@@ -159,11 +163,18 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   constexpr int RPR = WPB * 8;
   constexpr int NA = (NRB * 32 + RPR - 1) / RPR;
   const int arow = tid >> 3, achunk = tid & 7;
+  // bytes per K-block of one A row in memory (A_F4: codes; its scales are 4 more)
+  constexpr int KBB = AM == A_F16 ? KBLK * 2 : AM == A_I8 ? KBLK : KBLK / 2;
   const char* asrc[NA];
+  const uint8_t* absrc[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i)
-    asrc[i] = reinterpret_cast<const char*>(A) + ((size_t)s_src[arow + RPR * i] * K + achunk * 8) * ES;
+  for (int i = 0; i < NA; ++i) {
+    const size_t row = (size_t)s_src[arow + RPR * i];
+    asrc[i] = reinterpret_cast<const char*>(A) + row * (K / KBLK) * KBB + achunk * (KBB / 8);
+    absrc[i] = AM == A_F4 ? Abs + row * (K / kGroup) : nullptr;
+  }
   const int aslot = ((achunk ^ ((arow >> 1) & 7)) << 4);
+  const int ashift = 8 * (achunk >> 1);  // A_F4: the chunk's scale byte in the K-block's word
 
   // B codes: the block's NCB weight rows, GK K-blocks (GK*32 bytes of each row) per
   // group. Thread t stages chunks j*(WPB*64) + t of the group tile, i.e. chunk t % CPR of
@@ -210,12 +221,19 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   };
   auto load_a = [&](int kb, int i) -> ARaw {
     const int kc = kb < nkb ? kb : nkb - 1;
-    return *reinterpret_cast<const ARaw*>(asrc[i] + kc * KBLK * ES);
+    if constexpr (AM == A_F4)
+      return make_uint2(*reinterpret_cast<const uint32_t*>(asrc[i] + kc * KBB),
+                        *reinterpret_cast<const uint32_t*>(absrc[i] + kc * 4));
+    else
+      return *reinterpret_cast<const ARaw*>(asrc[i] + kc * KBB);
   };
   // the 8 fp16 values a thread stores for row arow + RPR*i of K-block kb
   auto a_fp16 = [&](const ARaw& v, int kb, int i) -> uint4 {
     if constexpr (AM == A_I8) {
       return __builtin_bit_cast(uint4, i8x8_f16(v.x, v.y));
+    } else if constexpr (AM == A_F4) {
+      const _Float16 sc = e4m3x2_f16<false>((v.y >> ashift) & 0xFFu)[0];
+      return __builtin_bit_cast(uint4, bfrag(v.x, sc));
     } else if constexpr (!GATEUP) {
       const uint32_t m = f16_pow2_neg(s_hd[(arow + RPR * i) * kMaxHSeg + (kb >> seg_shift)]);
       const f16x2_t mm = __builtin_bit_cast(f16x2_t, m | (m << 16));
@@ -399,7 +417,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
       const int r = rb * 32 + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        if constexpr (AM == A_I8) {
+        if constexpr (AM != A_F16) {
           const float xs = s_coef[r];
           hv[rb][v] = silu_fast(acc[rb][0][v] * (xs * gg)) * (acc[rb][1][v] * (xs * gu));
         } else {
@@ -498,14 +516,16 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
 }
 
 // GATEUP: gate/up + SwiGLU (w0 = gate, w1 = up), else down + combine (w0 = down).
-// AM: the activation mode (A_F16 or A_I8, above).
-// a_scale: A_I8 row scales (gate/up: per token; down: per sorted position).
+// AM: the activation mode (A_F16, A_I8 or A_F4, above).
+// a_scale: A_I8 / A_F4 row scales (gate/up: per token; down: per sorted position).
+// a_bscale: A_F4 block scales (E4M3, one per 16 inputs of a row).
 // a_exp: A_F16 exponents (gate/up: per token; down: per sorted position and gate/up block,
 // [P][nbh], whose blocks span 2^seg_shift K-blocks of the down GEMM).
 // hexp_out: gate/up A_F16 only, the exponents of the fp16 h it writes ([P][NB]).
 template <bool GATEUP, int AM, int KQ, int WPB, int GK, bool Q8 = false>
 __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
-    const void* __restrict__ A, const float* __restrict__ a_scale, const int32_t* __restrict__ a_exp, int nbh,
+    const void* __restrict__ A, const float* __restrict__ a_scale, const uint8_t* __restrict__ a_bscale,
+    const int32_t* __restrict__ a_exp, int nbh,
     int seg_shift, const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ offsets,
     const TileDesc* __restrict__ tiles, const int32_t* __restrict__ tile_count, int topk, int K, int NB,
     WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w, void* __restrict__ out, int ldo,
@@ -549,11 +569,11 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     const int p = sorted_pairs[pos];
     if (GATEUP) {
       s_src[tid] = p / topk;
-      s_coef[tid] = AM == A_I8 ? a_scale[p / topk] : 1.0f;
+      s_coef[tid] = AM != A_F16 ? a_scale[p / topk] : 1.0f;
       s_exp[tid] = AM == A_F16 ? a_exp[p / topk] : 0;
     } else {
       s_src[tid] = pos;
-      s_coef[tid] = route_w[p] * (AM == A_I8 ? a_scale[pos] : 1.0f);
+      s_coef[tid] = route_w[p] * (AM != A_F16 ? a_scale[pos] : 1.0f);
       if constexpr (kHd) {
         // the row's smallest exponent (its largest block), and each block's shift down to it
         const int32_t* ex = a_exp + (size_t)pos * nbh;
@@ -588,7 +608,7 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
 
   const int nrb = (tc.rows + 31) >> 5;
 #define NVFP4_TILE(R)                                                                                            \
-  gemm_tile<GATEUP, AM, R, KQ, WPB, GK, Q8>(tc, A, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef, \
+  gemm_tile<GATEUP, AM, R, KQ, WPB, GK, Q8>(tc, A, a_bscale, K, b0row, b1row, bs, w0, w1, out, ldo, lds, s_src, s_coef, \
                                             s_exp, s_hd, seg_shift, s_red, hexp_out, NB)
   if (nrb == 4)
     NVFP4_TILE(4);
@@ -606,7 +626,8 @@ static inline unsigned grid_for(int max_tiles, int NB) {
   return (unsigned)(((g + 7) / 8) * 8);
 }
 
-hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const int32_t* a_exp,
+hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, const uint8_t* a_bscale,
+                              const int32_t* a_exp,
                               const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
                               const int32_t* tile_count, int max_tiles, int topk, int H, int I,
                               const WeightArgs& gate, const WeightArgs& up, void* h, int32_t* hexp,
@@ -616,19 +637,24 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
   // multiple of 256, so scale groups of 4 K-blocks; B groups of 2 K-blocks.
 #define NVFP4_GU(AM, WPB)                                                                                  \
   moe_gemm_f16_kernel<true, AM, 4, WPB, 2><<<grid_for(max_tiles, I / (WPB * 32)), WPB * 64, 0, st>>>(      \
-      a, a_scale, a_exp, 0, 0, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), gate, up, \
-      nullptr, h, I, hexp)
+      a, a_scale, a_bscale, a_exp, 0, 0, sorted_pairs, offsets, tiles, tile_count, topk, H, I / (WPB * 32), \
+      gate, up, nullptr, h, I, hexp)
   const bool w8 = I % 256 == 0;
   if (act == 0) {
     if (w8)
       NVFP4_GU(A_F16, 8);
     else
       NVFP4_GU(A_F16, 4);
-  } else {
+  } else if (act == 1) {
     if (w8)
       NVFP4_GU(A_I8, 8);
     else
       NVFP4_GU(A_I8, 4);
+  } else {
+    if (w8)
+      NVFP4_GU(A_F4, 8);
+    else
+      NVFP4_GU(A_F4, 4);
   }
 #undef NVFP4_GU
   return hipGetLastError();
@@ -636,7 +662,8 @@ hipError_t launch_gemm_gateup(int act, const void* a, const float* a_scale, cons
 
 int gateup_blocks(int I) { return I % 256 == 0 ? I / 256 : I / 128; }
 
-hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const int32_t* hexp,
+hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const uint8_t* h_bscale,
+                            const int32_t* hexp,
                             const int32_t* sorted_pairs, const int32_t* offsets, const TileDesc* tiles,
                             const int32_t* tile_count, int max_tiles, int topk, int H, int I,
                             const WeightArgs& down, const float* w, float* y, hipStream_t st) {
@@ -652,11 +679,13 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
     const dim3 grid = grid_for(max_tiles, H / (WPB * 64));                                                  \
     if (down.fmt == 1)                                                                                      \
       moe_gemm_f16_kernel<false, AM, KQ, WPB, 2, true><<<grid, WPB * 64, 0, st>>>(                          \
-          h, h_scale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), \
+          h, h_scale, h_bscale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I,     \
+          H / (WPB * 64),                                                                                   \
           down, down, w, y, H, nullptr);                                                                    \
     else                                                                                                    \
       moe_gemm_f16_kernel<false, AM, KQ, WPB, 2><<<grid, WPB * 64, 0, st>>>(                                \
-          h, h_scale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I, H / (WPB * 64), \
+          h, h_scale, h_bscale, hexp, nbh, seg_shift, sorted_pairs, offsets, tiles, tile_count, topk, I,     \
+          H / (WPB * 64),                                                                                   \
           down, down, w, y, H, nullptr);                                                                    \
   } while (0)
 #define NVFP4_DOWN_W(AM, KQ) \
@@ -671,11 +700,17 @@ hipError_t launch_gemm_down(int act, const void* h, const float* h_scale, const 
     } else {
       NVFP4_DOWN_W(A_F16, 2)
     }
-  } else {
+  } else if (act == 1) {
     if (q4) {
       NVFP4_DOWN_W(A_I8, 4)
     } else {
       NVFP4_DOWN_W(A_I8, 2)
+    }
+  } else {
+    if (q4) {
+      NVFP4_DOWN_W(A_F4, 4)
+    } else {
+      NVFP4_DOWN_W(A_F4, 2)
     }
   }
 #undef NVFP4_DOWN_W

@@ -452,40 +452,33 @@ def _rne_table(t: np.ndarray, table: np.ndarray) -> np.ndarray:
 
 def quant_rows_nvfp4(v32: np.ndarray):
     """Rows of fp32 values [R][K] (K % 16 == 0) -> (codes uint8 [R][K/2], two per byte, low
-    nibble first; scales uint8 [R][K/16] E4M3; g float32 [R]) by the r9 rule above."""
+    nibble first; scales uint8 [R][K/16] E4M3; g float32 [R]) by the r9 rule above. Every
+    quotient is one fp32 operation on fp32 operands; the two roundings to the nearest table
+    value are done on exact float64 copies of those quotients."""
     v = np.asarray(v32, dtype=np.float32)
     R, K = v.shape
-    nib = np.zeros((R, K), dtype=np.uint8)
-    sc = np.zeros((R, K // GROUP), dtype=np.uint8)
-    g = np.zeros(R, dtype=np.float32)
-    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
-        for r in range(R):
-            row = v[r]
-            if np.isnan(row).any():
-                g[r] = np.float32(np.nan)
-                continue
-            amax = np.float32(np.max(np.abs(row))) if K else np.float32(0)
-            if np.isinf(amax):
-                g[r] = np.float32(np.inf)
-                continue
-            if amax == 0:
-                continue
-            gr = np.float32(amax / np.float32(2688.0))
-            g[r] = gr
-            d6 = np.float32(np.float32(6.0) * gr)
-            for b in range(K // GROUP):
-                blk = row[b * GROUP:(b + 1) * GROUP]
-                t = np.float32(np.float32(np.max(np.abs(blk))) / d6) if d6 > 0 else np.float32(0)
-                si = int(_rne_table(np.float64(t), E4M3_POS))
-                sc[r, b] = si
-                sv = np.float32(E4M3_POS[si])
-                den = np.float32(sv * gr)
-                if den == 0:
-                    continue
-                q = (blk / den).astype(np.float32)
-                mag = _rne_table(np.abs(q).astype(np.float64), E2M1_POS).astype(np.uint8)
-                nib[r, b * GROUP:(b + 1) * GROUP] = mag | np.where(blk < 0, 8, 0).astype(np.uint8)
-    return pack_codes(nib), sc, g
+    G = K // GROUP
+    a = np.abs(v)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore", under="ignore"):
+        nan_row = np.isnan(v).any(axis=1)
+        amax = a.max(axis=1) if K else np.zeros(R, np.float32)
+        inf_row = ~nan_row & np.isinf(amax)
+        g = np.where(nan_row, np.float32(np.nan),
+                     np.where(inf_row, np.float32(np.inf), amax / np.float32(2688.0))).astype(np.float32)
+        live = ~nan_row & ~inf_row & (amax > 0)          # rows that get codes
+        d6 = (np.float32(6.0) * g).astype(np.float32)
+        live &= d6 > 0
+        # block scales: t = blockmax / (6 g) in fp32, then the nearest E4M3 value
+        bmax = a.reshape(R, G, GROUP).max(axis=2)
+        t = (bmax / np.where(live, d6, np.float32(1))[:, None]).astype(np.float32)
+        si = np.where(live[:, None], _rne_table(t.astype(np.float64), E4M3_POS), 0).astype(np.uint8)
+        # codes: v / (s g) in fp32 (s g rounded to fp32 first), then the nearest E2M1 value
+        den = (E4M3_POS[si].astype(np.float32) * g[:, None]).astype(np.float32)
+        coded = live[:, None] & (den > 0)
+        q = (v.reshape(R, G, GROUP) / np.where(coded, den, np.float32(1))[:, :, None]).astype(np.float32)
+        mag = _rne_table(np.abs(q).astype(np.float64), E2M1_POS).astype(np.uint8)
+        nib = np.where(coded[:, :, None], mag | np.where(v.reshape(R, G, GROUP) < 0, 8, 0).astype(np.uint8), 0)
+    return pack_codes(nib.reshape(R, K).astype(np.uint8)), si, g
 
 
 def dequant_rows_nvfp4(codes: np.ndarray, scales: np.ndarray, g: np.ndarray) -> np.ndarray:

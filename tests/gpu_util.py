@@ -159,3 +159,96 @@ def w4a8_strict(xb, lay, ids, w, rows, ws, got, act="w4a8_f16"):
     e2e = max_row_rel_l2(got, O.w4a8_down_from_codes(q_o, s_o, pairs, lay, ids, w, rows=rows))
     return dict(err=err, err_vs_oracle_codes=e2e, h_err=h_err, flips=int(flip.sum()), codes=int(flip.size),
                 near_ties=int((tie_dist < 1e-3).sum()))
+
+
+def _nibbles(packed: np.ndarray) -> np.ndarray:
+    """uint8 [R][K/2] -> codes [R][K] (low nibble first). Byte handling only."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def w4a4_strict(xb, lay, ids, w, rows, ws, got, act="w4a4"):
+    """The W4A4 checks, strict as for W4A8, on the pairs of the given token rows after a
+    prefill call on ws:
+      (a) the staged x codes, block scales and row scales equal the oracle's NVFP4
+          quantization bit for bit;
+      (b) the GPU's fp32 h is within 1e-5 (per pair row, relative L2) of the oracle's;
+      (c) the quantizer applied to the GPU's own fp32 h gives the GPU's codes, block scales
+          and row scales bit for bit;
+      (d) against the oracle's quantization of its own h: row scales within 1e-5; a block
+          scale differs only where the two fp32 quotients blockmax / (6 g) agree to 1e-4
+          (a rounding boundary between them); within blocks of equal scale a code differs
+          only in magnitude by one step, where the two quotients v / (s g) agree to 1e-3
+          (a tie between them), or as the sign of a zero; at most 1e-3 of the codes differ;
+      (e) the oracle's down step and combine on the GPU's codes match the GPU's output rows
+          within the 2e-3 bound.
+    Returns the measured figures, including the end-to-end error against the oracle's own
+    codes (reported, not bounded)."""
+    T, k = ids.shape
+    H, I, E = lay.H, lay.I, lay.E
+    P = T * k
+    reg = lambda name, dt: ws_region(ws, T, H, I, E, k, act, name, dt)  # noqa: E731
+    rows = np.asarray(rows)
+    rt = torch.from_numpy(rows).to(ws.device)
+    # (a)
+    xc = reg("x_staged", torch.uint8).view(T, H // 2)[rt].cpu().numpy()
+    xs = reg("x_blockscale", torch.uint8).view(T, H // 16)[rt].cpu().numpy()
+    xg = reg("x_rowscale", torch.float32)[rt].cpu().numpy()
+    rc, rs, rg = O.quant_rows_nvfp4(O.bf16_to_f64(xb[rows]).astype(np.float32))
+    assert np.array_equal(xc, rc) and np.array_equal(xs, rs) and np.array_equal(xg.view(np.uint32), rg.view(np.uint32))
+    inv = reg("pair_position", torch.int32).cpu().numpy()
+    pairs, h_orc = [], []
+    for e, pe, h in O.w4a4_pair_hidden(xb, lay, ids, rows):
+        pairs.append(rows[pe // k] * k + pe % k)
+        h_orc.append(h)
+    pairs = np.concatenate(pairs)
+    h_orc = np.concatenate(h_orc)
+    assert (inv[pairs] >= 0).all()
+    pos = torch.from_numpy(inv[pairs].astype(np.int64)).to(ws.device)
+    hg = reg("h", torch.float32).view(P, I)[pos].cpu().numpy()
+    qc = reg("h_q", torch.uint8).view(P, I // 2)[pos].cpu().numpy()
+    qs = reg("h_blockscale", torch.uint8).view(P, I // 16)[pos].cpu().numpy()
+    qg = reg("h_scale", torch.float32)[pos].cpu().numpy()
+    # (b)
+    h_err = float(np.max(O.rel_l2_rows(hg, h_orc)))
+    assert h_err < 1e-5, h_err
+    # (c)
+    c_re, s_re, g_re = O.quant_rows_nvfp4(hg)
+    assert np.array_equal(c_re, qc) and np.array_equal(s_re, qs) and np.array_equal(g_re.view(np.uint32),
+                                                                                      qg.view(np.uint32))
+    # (d)
+    oc, os_, og = O.quant_rows_nvfp4(h_orc)
+    assert np.all(np.abs(qg.astype(np.float64) - og) <= 1e-5 * np.abs(og))
+    G = I // 16
+    bm_g = np.abs(hg).reshape(len(pairs), G, 16).max(-1)
+    bm_o = np.abs(h_orc).reshape(len(pairs), G, 16).max(-1)
+    t_g = (bm_g / (np.float32(6) * qg)[:, None]).astype(np.float32).astype(np.float64)
+    t_o = (bm_o / (np.float32(6) * og)[:, None]).astype(np.float32).astype(np.float64)
+    sflip = qs != os_
+    assert np.all(np.abs(t_g - t_o)[sflip] <= 1e-4 * t_o[sflip])
+    ng, no = _nibbles(qc), _nibbles(oc)
+    same_blk = np.repeat(~sflip, 16, axis=1)
+    mg, mo = ng & 7, no & 7
+    cflip = (ng != no) & same_blk & ~((mg == 0) & (mo == 0))
+    assert np.all(np.abs(mg.astype(np.int32) - mo.astype(np.int32))[cflip] == 1)
+    assert np.all((ng >> 3)[cflip] == (no >> 3)[cflip])
+    sv = np.repeat(np.asarray(O.E4M3_POS, dtype=np.float64)[os_], 16, axis=1)
+    den_o = (sv.astype(np.float32) * og[:, None]).astype(np.float32).astype(np.float64)
+    den_g = (np.repeat(np.asarray(O.E4M3_POS, dtype=np.float64)[qs], 16, axis=1).astype(np.float32)
+             * qg[:, None]).astype(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q_o = np.abs(h_orc / den_o)
+        q_g = np.abs(hg.astype(np.float64) / den_g)
+    assert np.all(np.abs(q_g - q_o)[cflip] <= 1e-3)
+    nflip = int(sflip.sum()) * 16 + int(cflip.sum())
+    assert nflip <= 1e-3 * ng.size, nflip
+    # (e)
+    ref = O.w4a4_down_from_codes(qc, qs, qg, pairs, lay, ids, w, rows=rows)
+    err = max_row_rel_l2(got, ref)
+    assert err < TOL, err
+    e2e = max_row_rel_l2(got, O.w4a4_down_from_codes(oc, os_, og, pairs, lay, ids, w, rows=rows))
+    return dict(err=err, err_vs_oracle_codes=e2e, h_err=h_err, scale_flips=int(sflip.sum()),
+                code_flips=int(cflip.sum()), codes=int(ng.size))

@@ -432,7 +432,7 @@ def test_decode_barrier_timeout_is_reported():
 
 
 @pytest.mark.parametrize("kind,act", [("decode", "bf16"), ("prefill", "bf16"), ("prefill", "w4a8_f16"),
-                                      ("prefill", "w4a8")])
+                                      ("prefill", "w4a8"), ("prefill", "w4a4")])
 def test_graph_replays_match_eager(kind, act):
     """Capture one call in a hipGraph; replay it several times with eager work and
     synchronizations in between, and check every replay against the eager result bit for

@@ -1,0 +1,234 @@
+"""W4A4 prefill (activations quantized per row to NVFP4) against the oracle, through the
+C ABI: the quantizer bit for bit, then the full prefill with the strict checks of
+gpu_util.w4a4_strict, on small ragged problems, every GEMM variant, the shared expert and
+the full-size 32768-token workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import DEV, TOL, bf16_dev, bf16_out_to_f64, cover_rows, layer_dev, max_row_rel_l2, w4a4_strict
+
+nv = pytest.importorskip("nvfp4_quantized_moe_02_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_case_rows():
+    """fp32 rows: seeded normals over a wide range of row magnitudes, rows with zero, tiny
+    (subnormal block scales) and saturating blocks, exact ties of both roundings, a zero
+    row, and NaN / +inf / -inf rows."""
+    rng = np.random.default_rng(77)
+    K = 256
+    rows = [(rng.standard_normal(K) * np.exp2(rng.integers(-60, 60))).astype(np.float32) for _ in range(24)]
+    r = rng.standard_normal(K).astype(np.float32)
+    r[16:32] = 0
+    r[32:48] *= np.float32(1e-5)  # block max far below the row max: subnormal E4M3 scales
+    r[48:64] *= np.float32(3e-7)  # a scale that rounds to zero
+    rows.append(r)
+    # ties: row max 2688 gives g = 1 and 6g = 6; a block of max 6 * 1.0625 has the E4M3 tie
+    # t = 1.0625 (between 1 and 1.125, to the even code: 1.0), so s * g = 1 and the listed
+    # quotients are the E2M1 midpoints
+    t = np.zeros(K, np.float32)
+    t[0] = 2688
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0], np.float32)
+    t[16] = 6 * 1.0625
+    t[17:17 + len(mids)] = mids
+    t[32] = 6 * 1.1875  # between 1.125 and 1.25 -> 1.25 (even code); quotients mids again
+    t[33:33 + len(mids)] = mids * np.float32(1.25)
+    rows.append(t)
+    rows.append(np.zeros(K, np.float32))
+    for bad in (np.nan, np.inf, -np.inf):
+        b = rng.standard_normal(K).astype(np.float32)
+        b[37] = bad
+        rows.append(b)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("cols", [16, 48, 256, 1040])
+def test_quant_rows_nvfp4_bit_exact_f32(cols):
+    """fp32 rows of several widths (one group, fewer groups than lanes, more groups than
+    lanes): codes, scale bytes and row scales equal the oracle's bit for bit."""
+    base = _quant_case_rows()
+    x = np.resize(base, (base.shape[0], cols)).astype(np.float32) if cols != base.shape[1] else base
+    if cols == 16:
+        x = base[:, 16:32].copy()
+    c, s, g = nv.quant_rows_nvfp4(torch.from_numpy(np.ascontiguousarray(x)).to(DEV))
+    rc, rs, rg = O.quant_rows_nvfp4(x)
+    assert np.array_equal(c.cpu().numpy(), rc)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+
+
+def test_quant_rows_nvfp4_bit_exact_bf16_and_fixture():
+    """bf16 activations of the prompt workloads (with outliers) and the hand-worked row of
+    the golden file."""
+    xb = W.draw_activations(5, 300, 2048, outlier_frac=0.001)
+    c, s, g = nv.quant_rows_nvfp4(bf16_dev(xb))
+    rc, rs, rg = O.quant_rows_nvfp4(O.bf16_to_f64(xb).astype(np.float32))
+    assert np.array_equal(c.cpu().numpy(), rc) and np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    row = np.zeros((1, 32), np.float32)
+    row[0, :8] = [6, 3, 1.5, 0.75, -0.25, 0.2, 5, -5]
+    row[0, 15] = 0.3
+    row[0, 16:19] = [0.3, -0.15, 0.075]
+    c, s, g = nv.quant_rows_nvfp4(torch.from_numpy(row).to(DEV))
+    assert list(s.cpu().numpy()[0]) == [0x7E, 0x5B]
+    assert list(c.cpu().numpy()[0]) == [0x57, 0x23, 0x08, 0xE6, 0, 0, 0, 0x10, 0xD7, 0x03, 0, 0, 0, 0, 0, 0]
+
+
+def test_quant_rows_nvfp4_validation():
+    lib = nv.load_library()
+    x = torch.zeros((4, 32), dtype=torch.float32, device=DEV)
+    c = torch.zeros((4, 16), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4, 2), dtype=torch.uint8, device=DEV)
+    g = torch.zeros(4, dtype=torch.float32, device=DEV)
+    args = lambda **kw: [kw.get("x", x.data_ptr()), kw.get("dt", 0), kw.get("rows", 4), kw.get("cols", 32),  # noqa
+                         kw.get("c", c.data_ptr()), s.data_ptr(), g.data_ptr(), None]
+    assert lib.nvfp4_quant_rows_nvfp4(*args()) == 0
+    assert lib.nvfp4_quant_rows_nvfp4(*args(cols=24)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(cols=0)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(rows=-1)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(dt=2)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(x=x.data_ptr() + 4)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(c=c.data_ptr() + 1)) == -1
+    assert lib.nvfp4_quant_rows_nvfp4(*args(rows=0)) == 0
+    torch.cuda.synchronize()
+
+
+def _w4a4_small(seed=23, E=8, H=512, I=256, T=600, k=8, out_dtype=torch.float32, routing="zipf"):
+    lay = W.draw_layer(seed, E=E, H=H, I=I)
+    dl = layer_dev(lay)
+    xb = W.draw_activations(seed, T, H, outlier_frac=0.001)
+    if routing == "zipf":
+        ids = W.draw_routing_zipf(seed, T, E, k, s=1.1)
+    else:
+        ids = np.random.default_rng(seed).integers(0, E, size=(T, k)).astype(np.int32)
+    w = W.draw_router_weights(seed, T, k)
+    ws = torch.zeros(nv.prefill_workspace_size(T, H, I, E, k, "w4a4"), dtype=torch.uint8, device=DEV)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act="w4a4",
+                       out_dtype=out_dtype, ws=ws)
+    got = bf16_out_to_f64(y) if out_dtype == torch.bfloat16 else y.cpu().numpy().astype(np.float64)
+    return w4a4_strict(xb, lay, ids, w, np.arange(T), ws, got), got, (xb, lay, ids, w)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_w4a4_small(out_dtype):
+    """600 tokens, 8 experts (Zipf routing, partial last tiles): strict checks, and the
+    end-to-end output against the oracle's own W4A4 MoE (the quantization of its own h),
+    which may differ from the GPU's only through the few codes at rounding ties."""
+    stats, got, (xb, lay, ids, w) = _w4a4_small(out_dtype=out_dtype)
+    ref = O.moe_w4a4(xb, lay, ids, w)
+    e2e = max_row_rel_l2(got, ref)
+    print(f"w4a4 small ({out_dtype}): {stats}, end to end vs oracle {e2e:.3e}")
+    assert e2e < 5e-2
+
+
+@pytest.mark.parametrize("H,I", [(512, 256), (768, 256), (512, 384), (256, 128)])
+def test_w4a4_kernel_shapes(H, I):
+    """Every GEMM variant: 8 or 4 waves for gate/up (I % 256) and for down (H % 512), scale
+    groups of 4 or 2 K-blocks for down (I % 256)."""
+    stats, _, _ = _w4a4_small(seed=25, E=6, H=H, I=I, T=300, k=4)
+    print(f"w4a4 H={H} I={I}: {stats}")
+
+
+def test_w4a4_ragged_dropped_and_tiny():
+    """Uneven experts, dropped and duplicate ids; T = 1 and T = 0."""
+    E, H, I, T, k = 5, 256, 128, 333, 3
+    lay = W.draw_layer(31, E=E, H=H, I=I)
+    dl = layer_dev(lay)
+    xb = W.draw_activations(31, T, H)
+    rng = np.random.default_rng(31)
+    ids = rng.choice(E, size=(T, k), p=[0.7, 0.2, 0.08, 0.0, 0.02]).astype(np.int32)
+    ids[0, 0] = 3
+    ids[1, :] = ids[1, 0]
+    ids[7, 2] = -5
+    ids[9, 1] = E
+    w = rng.random((T, k)).astype(np.float32)
+    ws = torch.zeros(nv.prefill_workspace_size(T, H, I, E, k, "w4a4"), dtype=torch.uint8, device=DEV)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act="w4a4",
+                       out_dtype=torch.float32, ws=ws)
+    live = np.array([t for t in range(T) if np.any((ids[t] >= 0) & (ids[t] < E))])
+    stats = w4a4_strict(xb, lay, ids, w, live, ws, y.cpu().numpy()[live].astype(np.float64))
+    print(f"w4a4 ragged: {stats}")
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    for T1 in (1, 0):
+        ids1 = ids[:T1].copy()
+        ws1 = torch.zeros(max(1, nv.prefill_workspace_size(T1, H, I, E, k, "w4a4")), dtype=torch.uint8, device=DEV)
+        y1 = nv.moe_prefill(bf16_dev(xb[:T1]), dl, torch.from_numpy(ids1).to(DEV), torch.from_numpy(w[:T1]).to(DEV),
+                            act="w4a4", out_dtype=torch.float32, ws=ws1)
+        assert y1.shape == (T1, H)
+        if T1:
+            w4a4_strict(xb[:T1], lay, ids1, w[:T1], np.arange(T1), ws1, y1.cpu().numpy().astype(np.float64))
+
+
+def test_w4a4_zero_and_nonfinite_rows():
+    """A zero token row gives a zero output row; a row holding an infinity or a NaN gives a
+    NaN output row (0 * inf in the row scale), as the oracle's dequantization does; the
+    other rows are unaffected."""
+    E, H, I, T, k = 4, 256, 128, 40, 2
+    lay = W.draw_layer(33, E=E, H=H, I=I)
+    dl = layer_dev(lay)
+    xb = W.draw_activations(33, T, H).copy()
+    xb[3] = 0
+    xb[5, 17] = 0x7F80  # +inf
+    xb[6, 100] = 0x7FC0  # NaN
+    ids = np.random.default_rng(33).integers(0, E, size=(T, k)).astype(np.int32)
+    w = np.full((T, k), 0.5, np.float32)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act="w4a4",
+                       out_dtype=torch.float32).cpu().numpy()
+    ref = O.moe_w4a4(xb, lay, ids, w)
+    assert np.all(y[3] == 0) and np.all(ref[3] == 0)
+    assert np.all(np.isnan(y[5])) and np.all(np.isnan(ref[5]))
+    assert np.all(np.isnan(y[6])) and np.all(np.isnan(ref[6]))
+    ok = [t for t in range(T) if t not in (3, 5, 6)]
+    assert np.isfinite(y[ok]).all()
+    assert max_row_rel_l2(y[ok], ref[ok]) < 5e-2
+
+
+def test_w4a4_shared_expert():
+    """With a shared expert the call equals the plain call with the shared expert appended
+    as expert E and routed by every token as slot topk with weight 1, bit for bit."""
+    E, H, I, T, k = 6, 512, 256, 200, 4
+    lay = W.draw_layer(35, E=E, H=H, I=I)
+    sh = W.draw_shared_expert(35, H=H, I=I)
+    dl, dsh = layer_dev(lay), layer_dev(sh)
+    xb = W.draw_activations(35, T, H)
+    ids = W.draw_routing_zipf(35, T, E, k)
+    w = W.draw_router_weights(35, T, k)
+    x = bf16_dev(xb)
+    y = nv.moe_prefill(x, dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act="w4a4",
+                       out_dtype=torch.float32, shared=dsh)
+    big = nv.Layer(*[type(p)(torch.cat([p.codes, q.codes]), torch.cat([p.scales, q.scales]),
+                             torch.cat([p.gamma, q.gamma]))
+                     for p, q in ((dl.gate, dsh.gate), (dl.up, dsh.up), (dl.down, dsh.down))])
+    ids2 = np.concatenate([ids, np.full((T, 1), E, np.int32)], 1)
+    w2 = np.concatenate([w, np.ones((T, 1), np.float32)], 1)
+    y2 = nv.moe_prefill(x, big, torch.from_numpy(ids2).to(DEV), torch.from_numpy(w2).to(DEV), act="w4a4",
+                        out_dtype=torch.float32)
+    assert torch.equal(y, y2)
+
+
+@pytest.fixture(scope="module")
+def full_layer_c3():
+    lay = W.draw_layer(W.config_seed(3))
+    return lay, layer_dev(lay)
+
+
+def test_w4a4_c4_full_size_cover(full_layer_c3):
+    """32768 tokens (the prompt-chunk workload of the W4A8 leg), full layer shape: the
+    strict checks on >= 1024 token rows covering every routed expert and its last tile;
+    every output row finite."""
+    lay, dl = full_layer_c3
+    wl = W.draw_workload(4)
+    ws = torch.zeros(nv.prefill_workspace_size(wl.T, lay.H, lay.I, lay.E, 8, "w4a4"), dtype=torch.uint8,
+                     device=DEV)
+    y = nv.moe_prefill(bf16_dev(wl.x), dl, torch.from_numpy(wl.ids).to(DEV), torch.from_numpy(wl.w).to(DEV),
+                       act="w4a4", ws=ws)
+    rows = cover_rows(wl.ids, lay.E, n=1024, seed=3)
+    got = bf16_out_to_f64(y[torch.from_numpy(rows).to(DEV)])
+    stats = w4a4_strict(wl.x, lay, wl.ids, wl.w, rows, ws, got)
+    print(f"w4a4 32768 tokens, {len(rows)} rows: {stats}")
+    assert torch.isfinite(y.float()).all()
+    assert stats["err"] < TOL
