@@ -10,7 +10,7 @@ layer (65 GB), so no step finds its weights in the 256 MB Infinity Cache.
 Also reported on the same line: per-kernel times from HIP events on the launch stream
 and the roofline of the dominant kernel (the gate/up grouped GEMM against the dense
 fp16 matrix-core peak), decode HBM bandwidth at 1 and 4 tokens (hipGraph of 48
-layer calls, replayed), the W4A8 prefill at 32768 tokens, the router, the Q8_0-down
+layer calls, replayed), the W4A8 and W4A4 prefills at 32768 tokens, the router, the Q8_0-down
 layer, the host-CPU decode projection, and the CPU oracle timed on a bounded sample of
 the prefill workload.
 """
@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--decode-rounds", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "q8down", "router", "host", "shared"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "w4a8", "w4a4", "q8down", "router", "host",
+                                       "shared"],
                     default="all")
     ap.add_argument("--decode-tokens", type=int, choices=[0, 1, 4], default=0,
                     help="decode leg: only the 1-token or only the 4-token workload (0: both)")
@@ -435,8 +436,8 @@ def cpu_description():
 
 def cpu_baseline(n_tokens):
     """The float64 oracle on bounded samples: the 8192-token bf16 prefill workload on all
-    BLAS threads (the reported value) and on one thread, and the 32768-token W4A8 workload
-    on all threads."""
+    BLAS threads (the reported value) and on one thread, and the 32768-token W4A8 and W4A4
+    workloads on all threads."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     import oracle as O
@@ -458,6 +459,8 @@ def cpu_baseline(n_tokens):
     w4 = W.draw_workload(4)
     n4 = max(16, n_tokens // 2)
     dt4 = run(lambda rows: O.moe_w4a8(w4.x, lay, w4.ids, w4.w, rows=rows), n4)
+    n44 = max(16, n_tokens // 4)
+    dt44 = run(lambda rows: O.moe_w4a4(w4.x, lay, w4.ids, w4.w, rows=rows), n44)
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tokens} tokens of the 8192-token prefill workload (all "
                       f"{len(np.unique(wl.ids[:n_tokens]))} experts they route to), float64 numpy oracle, "
@@ -467,6 +470,9 @@ def cpu_baseline(n_tokens):
             "w4a8_t32768": {"value": round(n4 / dt4, 3), "unit": "tokens/s", "cores": threads,
                             "sample": f"first {n4} tokens of the 32768-token W4A8 workload (int8 x and h per "
                                       f"row, float64 oracle), {dt4:.1f} s"},
+            "w4a4_t32768": {"value": round(n44 / dt44, 3), "unit": "tokens/s", "cores": threads,
+                            "sample": f"first {n44} tokens of the same workload with NVFP4 x and h per row "
+                                      f"(float64 oracle), {dt44:.1f} s"},
             "host": cpu_description()}
 
 
@@ -521,6 +527,10 @@ def main():
             w4i = bench_prefill(layers, 4, "w4a8", max(3, args.steps // 8), 1, not args.no_stage_times)
             log(f"w4a8 int8 MFMA 32768: {w4i['ms']:.3f} ms/step, {w4i['tokens_per_s']:.0f} tok/s, "
                 f"stages {w4i['stages_ms']}")
+    w44 = None
+    if args.only in ("all", "w4a4"):
+        w44 = bench_prefill(layers, 4, "w4a4", max(4, args.steps // 4), 2, not args.no_stage_times)
+        log(f"w4a4 32768: {w44['ms']:.3f} ms/step, {w44['tokens_per_s']:.0f} tok/s, stages {w44['stages_ms']}")
     rt = None
     if args.only in ("all", "router"):
         rt = {f"t{T}_us": round(bench_router(T), 2) for T in (1, 4, 8192)}
@@ -640,6 +650,13 @@ def main():
                                             / PEAK_INT8_TOPS, 4),
             "frac_of_fp16_peak_step": round((w4i["gu_flops"] + w4i["dn_flops"]) / (w4i["ms"] * 1e-3) / 1e12
                                             / PEAK_FP16_TFLOPS, 4)}
+    if w44 is not None:
+        result["w4a4"] = {"workload": "32768 tokens, NVFP4 activations (x and h per row: E2M1 codes, E4M3 scale "
+                                      "per 16, fp32 row scale), fp16 matrix cores",
+                          "tokens/s": round(w44["tokens_per_s"], 1), "ms_per_step": round(w44["ms"], 4),
+                          "stage_ms": [round(v, 4) for v in w44["stages_ms"]],
+                          "frac_of_fp16_peak_step": round((w44["gu_flops"] + w44["dn_flops"]) / (w44["ms"] * 1e-3)
+                                                          / 1e12 / PEAK_FP16_TFLOPS, 4)}
     if rt is not None:
         result["router"] = {"workload": "logits of 512 experts (bf16 router matrix, hidden 2048) on bf16 activations, "
                                         "top-8, softmax over the selected logits; us per call in a hipGraph of 48 "
