@@ -67,7 +67,7 @@ def _problem(seed, T, E=8, H=512, I=256, k=4, down_fmt="nvfp4"):
     return layer_dev(lay), bf16_dev(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
 
 
-@pytest.mark.parametrize("act", ["bf16", "w4a8_f16", "w4a8"])
+@pytest.mark.parametrize("act", ["bf16", "w4a8_f16", "w4a8", "w4a4"])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shared", [False, True])
 def test_prefill_writes_only_its_output_and_workspace(act, out_dtype, shared):
@@ -141,6 +141,15 @@ def test_router_route_quant_dequant_linear_write_only_their_outputs():
         assert lib.nvfp4_quant_rows_i8(xin.data_ptr(), dt, T, H, q.t.data_ptr(), sc.t.data_ptr(), s) == 0
         torch.cuda.synchronize()
         assert q.intact() and sc.intact() and unchanged(b, xin)
+    # NVFP4 row quantizer (bf16 and fp32 inputs)
+    for xin, dt in ((x, 1), (x.float(), 0)):
+        c, sb, g = guarded_like((T, H // 2), torch.uint8), guarded_like((T, H // 16), torch.uint8), \
+            guarded_like((T,), torch.float32)
+        b = snapshot(xin)
+        assert lib.nvfp4_quant_rows_nvfp4(xin.data_ptr(), dt, T, H, c.t.data_ptr(), sb.t.data_ptr(), g.t.data_ptr(),
+                                          s) == 0
+        torch.cuda.synchronize()
+        assert c.intact() and sb.intact() and g.intact() and unchanged(b, xin)
     # dequant and the single-expert linear
     lay = W.draw_layer(87, E=2, H=256, I=128)
     p = nv.Proj.from_numpy(lay.gate, DEV)
