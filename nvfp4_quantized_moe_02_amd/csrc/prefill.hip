@@ -10,7 +10,10 @@
 // K loop.
 //
 // A (activations, fp16): loaded two K-blocks (of 64 inputs) ahead into registers and
-// stored to a 2-stage LDS ring at the top of the iteration that uses it.
+// stored to a 2-stage LDS ring at the top of the iteration that uses it. The gate/up GEMM
+// on fp16 activations (the prefill's default) instead loads A, the B codes and the scale
+// bytes straight into LDS (global_load_lds_dwordx4, 4 A stages, explicit vmcnt waits before
+// each K-block's barrier): no staging registers and no LDS store instructions.
 // Each LDS row holds 64 inputs (8 slots of 16 bytes); chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7). gfx950's LDS serves a 128-bit read 16 lanes (256 bytes, all 64
 // banks) per cycle, and the 16 rows of such a lane group then cover every bank once: the
@@ -54,6 +57,37 @@ constexpr int BM = kTileM;
 constexpr int KBLK = 64;                        // inputs per K-block
 constexpr int NSTAGE = 2;                       // LDS stages of A
 constexpr int STAGE_BYTES = BM * KBLK * 2;      // 16 KiB per stage
+
+// Direct-to-LDS staging for the gate/up GEMM on fp16 activations (the one mode whose A
+// needs no conversion): A and B go from memory straight into their swizzled LDS slots with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS window + 16 * lane,
+// so the XOR swizzle is applied to the source chunk a lane loads), with four A stages.
+#ifndef NVFP4_GATEUP_DLDS
+#define NVFP4_GATEUP_DLDS 1
+#endif
+template <bool GATEUP, int AM, int KQ, bool Q8>
+constexpr bool direct_lds() {
+  return NVFP4_GATEUP_DLDS && GATEUP && AM == 0 && KQ == 4 && !Q8;
+}
+constexpr int NSTAGE_DL = 4;  // A stages with direct-to-LDS loads: K-block kb in stage kb & 3
+
+typedef __attribute__((address_space(3))) char* lds_ptr_t;
+// 16 bytes per lane from gsrc into the wave's LDS window at ldst (wave-uniform) + 16 * lane.
+// Written as asm: the compiler, seeing the builtin's LDS write, waits for it to land
+// (vmcnt(0)) before every later LDS read, which would serialize the prefetch. The
+// instruction writes no register (the data goes to LDS), and its waits are explicit here:
+// wait_vm before the barrier that publishes the stage, wait_vm<0> before the block ends.
+__device__ __forceinline__ void load_lds16(const void* gsrc, char* ldst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)ldst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m) : "memory", "m0");
+}
+// wait until at most N vector memory operations of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ uint32_t word_of(const uint4& c, int s) {
   return s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
@@ -150,6 +184,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
                                           const uint8_t* s_hd, int seg_shift, float* s_red,
                                           int32_t* __restrict__ hexp_out, int NB) {
   constexpr bool HOUT32 = GATEUP && AM != A_F16;
+  constexpr bool DL = direct_lds<GATEUP, AM, KQ, Q8>();
   // A_F4 raw chunk: x = the 8 codes, y = the K-block's 4 scale bytes
   typedef typename std::conditional<AM == A_F16, uint4, uint2>::type ARaw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -175,6 +210,16 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   }
   const int aslot = ((achunk ^ ((arow >> 1) & 7)) << 4);
   const int ashift = 8 * (achunk >> 1);  // A_F4: the chunk's scale byte in the K-block's word
+  // DL: lane L of wave w fills slot L & 7 of row 8w + L/8 (+ RPR*i), so it loads the chunk
+  // that the swizzle puts there: chunk (L & 7) ^ key(row)
+  const char* adl[NA];
+  if constexpr (DL) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int row = arow + RPR * i;
+      adl[i] = reinterpret_cast<const char*>(A) + (size_t)s_src[row] * K * 2 + ((achunk ^ ((row >> 1) & 7)) << 4);
+    }
+  }
 
   // B codes: the block's NCB weight rows, GK K-blocks (GK*32 bytes of each row) per
   // group. Thread t stages chunks j*(WPB*64) + t of the group tile, i.e. chunk t % CPR of
@@ -185,7 +230,7 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   constexpr int GKB = Q8 ? 1 : GK;  // K-blocks per B group
   typedef BTile<WPB, Q8 ? 2 : GK> BT;
   const size_t rowbytes = Q8 ? K : K / 2;
-  char* btiles = lds + NSTAGE * STAGE_BYTES;
+  char* btiles = lds + (DL ? NSTAGE_DL : NSTAGE) * STAGE_BYTES;
   const int brow = tid / BT::CPR, bch = tid % BT::CPR;
   const int ngb = nkb / GKB;
   auto load_bg = [&](int g, int j) -> uint4 {
@@ -196,6 +241,21 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     const uint8_t* base = (GATEUP && j * BT::RPT >= BT::NCB / 2) ? b1row + (size_t)(row - BT::NCB / 2) * rowbytes
                                                                  : b0row + (size_t)row * rowbytes;
     return *reinterpret_cast<const uint4*>(base + gc * BT::ROWB + bch * 16);
+  };
+  // DL: group g's staging round j straight into tile t: lane L of wave w fills slot L % CPR
+  // of tile row j*RPT + 16w + L/CPR (the thread's brow), loading the chunk the swizzle
+  // puts there
+  auto load_bg_dl = [&](int g, int j, char* tile) {
+    const int gc = g < ngb ? g : ngb - 1;
+    const int row = j * BT::RPT + brow;
+    const uint8_t* base = (GATEUP && j * BT::RPT >= BT::NCB / 2) ? b1row + (size_t)(row - BT::NCB / 2) * rowbytes
+                                                                 : b0row + (size_t)row * rowbytes;
+    const int ch = bch ^ ((row >> BT::SHIFT) & (BT::CPR - 1));
+    load_lds16(base + gc * BT::ROWB + ch * 16, tile + (j * BT::RPT + (tid >> 6) * (64 / BT::CPR)) * BT::ROWB);
+  };
+  auto load_a_dl = [&](int kb, int i) {
+    const int kc = kb < nkb ? kb : nkb - 1;
+    load_lds16(adl[i] + kc * KBLK * 2, lds + (kb & (NSTAGE_DL - 1)) * STAGE_BYTES + (RPR * i + 8 * (tid >> 6)) * 128);
   };
   // tile row of this lane's fragment in column block cb
   const int frow0 = GATEUP ? wave * 32 + l32 : wave * 64 + l32;
@@ -208,6 +268,26 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   auto load_s = [&](int j, int cb) -> SRaw {
     const int jc = j < ngrp ? j : ngrp - 1;
     return *reinterpret_cast<const SRaw*>(bs[cb] + jc * (4 * KQ));
+  };
+  // DL: a scale group's bytes (16 per weight row: KQ = 4 K-blocks) straight into scale tile
+  // (group & 1), thread t filling tile row t (the gate rows, then the up rows); every lane
+  // then reads its two columns' 16 bytes from there. Scale loads into registers would make
+  // the compiler, which cannot see the asm loads, drain every load (vmcnt(0)) before using
+  // them.
+  char* stiles = btiles + 2 * BT::BYTES;
+  const uint8_t* sdl = nullptr;
+  if constexpr (DL) {
+    const size_t srow0 = (size_t)tc.nb * (WPB * 32);
+    sdl = tid < BT::NCB / 2 ? w0.scale_row(tc.e, srow0 + tid) : w1.scale_row(tc.e, srow0 + tid - BT::NCB / 2);
+  }
+  auto load_s_dl = [&](int j) {
+    const int jc = j < ngrp ? j : ngrp - 1;
+    load_lds16(sdl + jc * (4 * KQ), stiles + (j & 1) * (BT::NCB * 16) + (tid >> 6) * 1024);
+  };
+  auto read_s_dl = [&](int j, SRaw* q) {
+    const char* t = stiles + (j & 1) * (BT::NCB * 16);
+    q[0] = *reinterpret_cast<const SRaw*>(t + (wave * 32 + l32) * 16);
+    q[1] = *reinterpret_cast<const SRaw*>(t + (BT::NCB / 2 + wave * 32 + l32) * 16);
   };
   const uint32_t psel = half ? 0x07060302u : 0x05040100u;
   // compact word c holds, for K-blocks 2c and 2c+1 of the group, this lane's two bytes each
@@ -265,16 +345,35 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   // back-edge while loads are in flight makes the compiler drain every load there).
   ARaw aq[2][NA];
   uint4 bg[BT::CH];
-  SRaw sq[2] = {load_s(0, 0), load_s(0, 1)};
-  __builtin_amdgcn_sched_barrier(0);
+  SRaw sq[2];
+  if constexpr (DL) {
+    // scale group 0, then the order of the loop's own issue (B group, then A): B(0) and
+    // A(0), then A(1); the first group's scales are read once A(0) has landed
+    load_s_dl(0);
 #pragma unroll
-  for (int j = 0; j < BT::CH; ++j) bg[j] = load_bg(0, j);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < BT::CH; ++j) load_bg_dl(0, j, btiles);
 #pragma unroll
-  for (int d = 0; d < 2; ++d) {
+    for (int d = 0; d < 2; ++d) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) aq[d][i] = load_a(d, i);
+      for (int i = 0; i < NA; ++i) load_a_dl(d, i);
+    }
     __builtin_amdgcn_sched_barrier(0);
+    wait_vm<NA>();
+    __syncthreads();
+    read_s_dl(0, sq);
+  } else {
+    sq[0] = load_s(0, 0);
+    sq[1] = load_s(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < BT::CH; ++j) bg[j] = load_bg(0, j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) aq[d][i] = load_a(d, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   uint32_t sc0[KQ / 2], sc1[KQ / 2];
   compact(sq[0], sc0);
@@ -283,20 +382,35 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
   auto kstep = [&](auto qpos, int kb) {
     constexpr int Q = decltype(qpos)::value;  // position in the scale group
     constexpr int R = Q & 1;                  // LDS stage / register ring slot
-    char* st = lds + R * STAGE_BYTES;
+    char* st = lds + (DL ? Q : R) * STAGE_BYTES;
+    if constexpr (DL) {
+      // This wave's direct loads of A(kb) (and, at a group start, of the B group) are
+      // complete once no more than the loads issued after them are outstanding: those of
+      // the previous K-block (A(kb+1); its B group when it started one) and the scale load
+      // issued between positions 1 and 2 of a scale group. Loads complete in order.
+      constexpr int kAfter = NA + (((Q + 3) % 4) % GKB == 0 ? BT::CH : 0) + (Q == 2 ? 1 : 0);
+      wait_vm<kAfter>();
+    } else {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = a_fp16(aq[R][i], kb, i);
-    // At a group start the staged B group goes to tile (group & 1): that tile was last
-    // read in the group before the previous one, which every wave finished before passing
-    // the previous group's first barrier.
-    if constexpr (Q % GKB == 0) {
-      char* bt = btiles + ((kb / GKB) & 1) * BT::BYTES;
+      for (int i = 0; i < NA; ++i)
+        *reinterpret_cast<uint4*>(st + (arow + RPR * i) * 128 + aslot) = a_fp16(aq[R][i], kb, i);
+      // At a group start the staged B group goes to tile (group & 1): that tile was last
+      // read in the group before the previous one, which every wave finished before passing
+      // the previous group's first barrier.
+      if constexpr (Q % GKB == 0) {
+        char* bt = btiles + ((kb / GKB) & 1) * BT::BYTES;
 #pragma unroll
-      for (int j = 0; j < BT::CH; ++j) *reinterpret_cast<uint4*>(bt + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
+        for (int j = 0; j < BT::CH; ++j) *reinterpret_cast<uint4*>(bt + BT::slot(j * BT::RPT + brow, bch)) = bg[j];
+      }
     }
     // A(kb) (and the B group) visible to all waves. Stage R was last read in iteration
-    // kb-2, and every wave finished those reads before passing the barrier of iteration kb-1.
+    // kb-2, and every wave finished those reads before passing the barrier of iteration
+    // kb-1 (DL: the stage and tile the loads issued below fill were last read in K-block
+    // kb-2 and in the previous group, both finished before this barrier).
     __syncthreads();
+    // DL: the next scale group's bytes (loaded before position 2, so landed before this
+    // barrier at position 3) into registers, compacted at the group's end
+    if constexpr (DL && Q == 3) read_s_dl(kb / KQ + 1, sq);
     const char* btile = btiles + ((kb / GKB) & 1) * BT::BYTES;
     // The next B group (at a group start) and A(kb+2) are loaded spread over the MFMAs of
     // this K-block: a burst of loads from every wave right after the barrier queues in the
@@ -307,8 +421,13 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
 #pragma unroll
       for (int g = 0; g < NLD; ++g) {
         if (g * nf / NLD == idx) {
-          if (g < NBL) bg[g < NBL ? g : 0] = load_bg(kb / GKB + 1, g < NBL ? g : 0);
-          else aq[R][g - NBL] = load_a(kb + 2, g - NBL);
+          if constexpr (DL) {
+            if (g < NBL) load_bg_dl(kb / GKB + 1, g < NBL ? g : 0, btiles + ((kb / GKB + 1) & 1) * BT::BYTES);
+            else load_a_dl(kb + 2, g - NBL);
+          } else {
+            if (g < NBL) bg[g < NBL ? g : 0] = load_bg(kb / GKB + 1, g < NBL ? g : 0);
+            else aq[R][g - NBL] = load_a(kb + 2, g - NBL);
+          }
         }
       }
     };
@@ -388,8 +507,12 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     if constexpr (KQ == 4) {
       kstep(std::integral_constant<int, 0>{}, kb);
       kstep(std::integral_constant<int, 1>{}, kb + 1);
-      sq[0] = load_s(j + 1, 0);
-      sq[1] = load_s(j + 1, 1);
+      if constexpr (DL) {
+        load_s_dl(j + 1);
+      } else {
+        sq[0] = load_s(j + 1, 0);
+        sq[1] = load_s(j + 1, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       kstep(std::integral_constant<int, 2>{}, kb + 2);
       kstep(std::integral_constant<int, 3>{}, kb + 3);
@@ -403,6 +526,9 @@ __device__ __forceinline__ void gemm_tile(const TileCtx& tc, const void* __restr
     compact(sq[0], sc0);
     compact(sq[1], sc1);
   }
+  // DL: the loads issued past the last K-block (refetches, never read) land before the
+  // block can end and its LDS be handed to another block
+  if constexpr (DL) wait_vm<0>();
 
   if constexpr (GATEUP) {
     // The weights are the first MFMA operand, so element v of acc[rb][cb] is intermediate
@@ -531,7 +657,9 @@ __global__ __launch_bounds__(WPB * 64, 8 / WPB) void moe_gemm_f16_kernel(
     WeightArgs w0, WeightArgs w1, const float* __restrict__ route_w, void* __restrict__ out, int ldo,
     int32_t* __restrict__ hexp_out) {
   // A stages and the B tile; the down epilogue reuses them (32 rows x WPB*64 fp32)
-  constexpr int kMain = NSTAGE * STAGE_BYTES + 2 * BTile<WPB, Q8 ? 2 : GK>::BYTES;
+  constexpr bool kDl = direct_lds<GATEUP, AM, KQ, Q8>();
+  constexpr int kMain = (kDl ? NSTAGE_DL : NSTAGE) * STAGE_BYTES + 2 * BTile<WPB, Q8 ? 2 : GK>::BYTES +
+                        (kDl ? 2 * WPB * 64 * 16 : 0);  // + the two scale tiles
   constexpr int kEpi = GATEUP ? 0 : 32 * WPB * 64 * 4;
   constexpr int kLds = kMain > kEpi ? kMain : kEpi;
   constexpr bool kHd = !GATEUP && AM == A_F16;    // down rescales A per gate/up block
