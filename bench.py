@@ -82,18 +82,33 @@ def replicate(layer, n):
 
 
 def stage_times(calls, steps, nstages):
-    """Mean ms per stage over `steps` calls, from events on the launch stream."""
+    """Mean ms per launch of each stage: stage s of `steps` calls (rotating over the layer
+    copies) captured back to back in a hipGraph, replayed once untimed and once between two
+    events on the launch stream (the decode legs time their stages the same way). Every
+    call shares the workspace, activations and routing, so after one full call stage s of
+    any call finds its inputs there. An event pair around each eager staged call would also
+    time the host's launch latency and the events' own synchronisation between kernels."""
     import torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nstages + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        c = calls[i % len(calls)]
-        for s in range(nstages):
-            ev[i][s].record()
-            c.stage(s)
-        ev[i][nstages].record()
-    torch.cuda.synchronize()
-    return [sum(ev[i][s].elapsed_time(ev[i][s + 1]) for i in range(steps)) / steps for s in range(nstages)]
+    out = []
+    calls[0].run()  # every stage's inputs in the workspace
+    for s in range(nstages):
+        torch.cuda.synchronize()
+        st = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(steps):
+                calls[i % len(calls)].stage(s)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        out.append(t0.elapsed_time(t1) / steps)
+        del g
+    return out
 
 
 def timed_steps(calls, steps, warmup):
@@ -161,8 +176,11 @@ def bench_prefill(layers, index, act, steps, warmup, stage_pass=True, eager=Fals
     else:
         ms = timed_steps(calls, steps, warmup)
     if stage_pass:
-        st = stage_times(calls, steps, 4)
+        # the eager loop first: the stage pass's timed launches are then the last of each
+        # kernel in a trace of this run (so a summary of the last `steps` dispatches per
+        # kernel holds exactly the launches whose event time this reports)
         ms_eager = eager_steps(calls, steps)
+        st = stage_times(calls, steps, 4)
     else:
         st, ms_eager = [float("nan")] * 4, float("nan")
     P = wl.T * 8
