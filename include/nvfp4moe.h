@@ -163,7 +163,8 @@ int nvfp4_quant_rows_i8(const void* x, int32_t x_dtype, int64_t rows, int32_t co
  *   scale byte of group b = the E4M3 value nearest to fp32(blockmax / fp32(6 * g[r])),
  *     ties to the even code, saturating at 448 (0x7E);
  *   code of x[r][c] = the E2M1 magnitude nearest to |fp32(x / fp32(s * g[r]))|, ties to the
- *     even code, saturating at 6, with the sign bit set for x < 0;
+ *     even code, saturating at 6, with the sign bit of x (so -0.0, and a negative value whose
+ *     magnitude rounds to zero, give the negative-zero code 8);
  * so x ~ code * scale * g. A zero row, or a block whose scale rounds to zero, gives zero
  * codes (and g = 0 for a zero row); a row holding a NaN gets g = NaN, else one holding an
  * infinity g = +inf, with zero codes and scales (so code * scale * g is NaN there).

@@ -252,9 +252,10 @@ hipError_t launch_quant_rows(const void* x, int x_dtype, int64_t rows, int cols,
 // 2688 = 6 * 448), per 16 inputs an E4M3 scale s = the value nearest to blockmax / (6 g)
 // (fp32 product and division) with ties to the even code, saturating at 448, and per input
 // the E2M1 code nearest to v / (s g) (fp32 product and division), ties to the even code,
-// saturating at 6, with the sign bit for v < 0. Zero rows give g = 0 and zero codes and
-// scales; a zero or underflowed block scale gives zero codes; a row holding a NaN gets
-// g = NaN, else one holding an infinity g = +inf, with zero codes and scales.
+// saturating at 6, with the sign bit of v (so -0.0 gives the negative-zero code). Zero
+// rows give g = 0 and zero codes and scales; a zero or underflowed block scale gives zero
+// codes; a row holding a NaN gets g = NaN, else one holding an infinity g = +inf, with zero
+// codes and scales.
 
 // E4M3 ("FN") code of the value nearest to t (0 <= t, finite), ties to the even code,
 // t >= 448 -> 448. Subnormals are multiples of 2^-9 (codes 0..7, code 8 = 2^-6); a normal t
@@ -268,12 +269,19 @@ __device__ __forceinline__ uint32_t e4m3_rne(float t) {
   return (uint32_t)((e + 7) * 8) + (uint32_t)rintf((x - 1.0f) * 8.0f);
 }
 
-// E2M1 magnitude code (0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to a >= 0, ties to the
-// even code (the midpoints 0.25, 1.25, 2.5 and 5 round down, 0.75, 1.75 and 3.5 up),
-// saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_rne(float a) {
-  return a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-       : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+// 8 values -> 8 E2M1 codes, two per byte (the even value in the low nibble): each quotient
+// v / den (IEEE fp32 division) goes through the fp32 -> E2M1 conversion with scale 1, which
+// rounds to the nearest code with ties to the even one (the midpoints 0.25, 1.25, 2.5 and 5
+// round down, 0.75, 1.75 and 3.5 up), saturates at 6 and keeps the sign bit (checked on the
+// device against that rule at every midpoint and its neighbours, exact codes, saturating,
+// tiny, denormal and signed-zero inputs).
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* v, float den) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] / den, v[1] / den, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] / den, v[3] / den, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] / den, v[5] / den, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] / den, v[7] / den, 1.0f, 3);
+  return w;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -340,11 +348,8 @@ __global__ __launch_bounds__(256) void quant_rows_nvfp4_kernel(const void* __res
       sc = e4m3_rne(bm / d6);
       const float den = e4m3_value(sc) * gr;
       if (den > 0.f) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t c = e2m1_rne(fabsf(v[j] / den)) | (v[j] < 0.f ? 8u : 0u);
-          w[j >> 3] |= c << (4 * (j & 7));
-        }
+        w[0] = pack8_e2m1(v, den);
+        w[1] = pack8_e2m1(v + 8, den);
       }
     }
     reinterpret_cast<uint2*>(codes + r * (cols / 2))[gi] = make_uint2(w[0], w[1]);

@@ -430,7 +430,8 @@ def w4a8_down_from_codes(qh: np.ndarray, sh: np.ndarray, pairs: np.ndarray, laye
 # the reading taken (r9): per row an FP32 scale g = fp32(absmax / 2688) (2688 = 6 * 448, so
 # the largest block scale is 448), per 16 inputs an E4M3 scale s = E4M3_RNE(fp32(blockmax /
 # fp32(6 g))) (saturating at 448), and per input the E2M1 code nearest to fp32(v / fp32(s g))
-# with ties to the even code (saturating at 6), its sign bit set for v < 0. A zero row has
+# with ties to the even code (saturating at 6), its sign bit the sign bit of v (so -0.0 and
+# negative values that round to zero give the negative-zero code). A zero row has
 # g = 0 and all codes and scales 0; a zero or underflowed block scale gives zero codes. A row
 # holding a NaN gets g = NaN, else one holding an infinity g = +inf, with zero codes and
 # scales, so the dequantized row (code * s * g) is NaN and propagates.
@@ -477,7 +478,7 @@ def quant_rows_nvfp4(v32: np.ndarray):
         coded = live[:, None] & (den > 0)
         q = (v.reshape(R, G, GROUP) / np.where(coded, den, np.float32(1))[:, :, None]).astype(np.float32)
         mag = _rne_table(np.abs(q).astype(np.float64), E2M1_POS).astype(np.uint8)
-        nib = np.where(coded[:, :, None], mag | np.where(v.reshape(R, G, GROUP) < 0, 8, 0).astype(np.uint8), 0)
+        nib = np.where(coded[:, :, None], mag | np.where(np.signbit(v.reshape(R, G, GROUP)), 8, 0).astype(np.uint8), 0)
     return pack_codes(nib.reshape(R, K).astype(np.uint8)), si, g
 
 

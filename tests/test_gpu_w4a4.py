@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 def _quant_case_rows():
     """fp32 rows: seeded normals over a wide range of row magnitudes, rows with zero, tiny
     (subnormal block scales) and saturating blocks, exact ties of both roundings, a zero
-    row, and NaN / +inf / -inf rows."""
+    row, signed zeros, and NaN / +inf / -inf rows."""
     rng = np.random.default_rng(77)
     K = 256
     rows = [(rng.standard_normal(K) * np.exp2(rng.integers(-60, 60))).astype(np.float32) for _ in range(24)]
@@ -39,6 +39,10 @@ def _quant_case_rows():
     t[33:33 + len(mids)] = mids * np.float32(1.25)
     rows.append(t)
     rows.append(np.zeros(K, np.float32))
+    z = rng.standard_normal(K).astype(np.float32)
+    z[::7] = np.float32(-0.0)  # signed zeros: the code keeps the sign bit
+    z[1::7] = np.float32(-1e-12)  # negative values whose magnitude rounds to zero
+    rows.append(z)
     for bad in (np.nan, np.inf, -np.inf):
         b = rng.standard_normal(K).astype(np.float32)
         b[37] = bad

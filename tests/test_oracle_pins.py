@@ -834,10 +834,12 @@ def test_quant_nvfp4_bruteforce():
     """Random rows (with zeros, ties, tiny and saturating values): every scale byte is the
     E4M3 value nearest to fp32(blockmax / fp32(6 g)) with ties to even, and every code the
     E2M1 magnitude nearest to fp32(v / fp32(s g)) with ties to even (saturating at 6), found
-    by exact rational brute force; the sign bit follows v < 0."""
+    by exact rational brute force; the sign bit is that of v (-0.0 included)."""
     rng = np.random.default_rng(13)
     x = (rng.standard_normal((6, 64)) * np.exp2(rng.integers(-30, 30, size=(6, 1)))).astype(np.float32)
     x[1, 16:32] = 0                       # a zero group
+    x[0, 3] = np.float32(-0.0)            # signed zeros inside coded groups
+    x[5, 40] = np.float32(-0.0)
     x[2, :] *= np.float32(1e-38)          # tiny values: scales underflow E4M3
     x[3, 5] = x[3].max() * 1.001 if x[3].max() > 0 else 1.0
     x[4, 0:16] = np.float32(0.25) * np.sign(x[4, 0:16] + 1e-30)  # ties on the E2M1 grid
@@ -864,7 +866,17 @@ def test_quant_nvfp4_bruteforce():
                     continue
                 q = np.float32(blk[k] / den)
                 assert (c & 7) == _nearest_even(abs(q), e2), (r, b, k, q)
-                assert (c >> 3) == (1 if blk[k] < 0 else 0)
+                assert (c >> 3) == (1 if np.signbit(blk[k]) else 0)
+
+
+def test_quant_nvfp4_signed_zero():
+    """The code's sign bit is the input's: in a row of max 1.0 (g = 1/2688, scale 448, s g =
+    1/6), 1.0 -> 6 (code 7), -0.0 -> code 8, +0.0 -> code 0, -1e-9 -> code 8 (magnitude 0)."""
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0], x[0, 1], x[0, 2], x[0, 3] = 1.0, -0.0, 0.0, -1e-9
+    codes, scales, g = O.quant_rows_nvfp4(x)
+    assert scales[0, 0] == 0x7E and g[0] == np.float32(1.0) / np.float32(2688.0)
+    assert list(O.unpack_codes(codes)[0, :4]) == [7, 8, 0, 8]
 
 
 def test_quant_nvfp4_zero_and_nonfinite_rows():
