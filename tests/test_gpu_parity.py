@@ -133,6 +133,31 @@ def test_route_bit_exact(case):
 
 
 # ------------------------------------------------------------------ int8 rows
+def test_quant_rows_near_ties_bit_exact():
+    """Quotients on, and one or two ulps either side of, every .5 point between -127 and 127,
+    under row scales with exact (s = 1, 2) and inexact reciprocals (s = fp32(absmax / 127) for
+    seeded absmax), on the vectorised kernel (cols % 8 == 0): codes and scales equal the
+    oracle's bit for bit."""
+    rng = np.random.default_rng(7)
+    halves = np.arange(-127, 127, dtype=np.float64) + 0.5
+    rows = []
+    for amax in [127.0, 254.0] + list(rng.uniform(0.01, 1000.0, size=14)):
+        s32 = np.float32(np.float32(amax) / np.float32(127.0))
+        base = (halves * np.float64(s32)).astype(np.float32)  # quotients at or next to ties
+        for ulps in (-2, -1, 0, 1, 2):
+            v = base.copy()
+            for _ in range(abs(ulps)):
+                v = np.nextafter(v, np.float32(np.inf) if ulps > 0 else np.float32(-np.inf)).astype(np.float32)
+            v = np.clip(v, -np.float32(amax), np.float32(amax))
+            row = np.concatenate([[np.float32(amax)], v, rng.standard_normal(7).astype(np.float32)])
+            rows.append(row[:256].astype(np.float32))
+    x = np.stack([np.pad(r, (0, 256 - len(r))) for r in rows]).astype(np.float32)
+    q, s = nv.quant_rows_i8(torch.from_numpy(x).to(DEV))
+    rq, rs = O.quant_rows_i8(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
 def test_quant_rows_bit_exact():
     xb = W.draw_activations(W.config_seed(4), 512)
     q, s = nv.quant_rows_i8(bf16_dev(xb))
