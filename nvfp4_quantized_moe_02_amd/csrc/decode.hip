@@ -13,8 +13,9 @@
 //            copies h into LDS once; each wave covers all 8 rows (8 lanes per row) for
 //            the unique experts w, w+8, ..., sums its experts' pairs in a fixed order, and
 //            the 8 waves' partials are added in wave order, so the result is
-//            deterministic. Each wave issues the loads of its first down weights before
-//            phase 1, so that traffic overlaps phase 1 and the wait.
+//            deterministic. Each wave issues the loads of its first down weights as soon
+//            as its block has arrived at the barrier, so that traffic overlaps the wait
+//            and the h copy while phase 1 has the memory system to itself.
 //
 // The same device code also runs as two ordinary launches (phase 1, then phase 2) for
 // the staged entry point and for shapes whose grid cannot be co-resident or whose h does
@@ -462,7 +463,7 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
 // size was, and stale flags (at most the previous epoch) never release a wait. Readers
 // then load h with agent-coherent loads. Returns false (and sets bit 0 of hdr[1]) if the
 // wait exceeds the spin limit, so every wave exits.
-__device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
+__device__ void barrier_arrive(const DecodeArgs& a, DecodeSmem& sm) {
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -471,16 +472,21 @@ __device__ bool grid_barrier(const DecodeArgs& a, DecodeSmem& sm) {
     sm.ok = 1;
   }
   __syncthreads();
-  const unsigned long long target = sm.epoch + 1;
   if (sm.last) {
+    const unsigned long long target = sm.epoch + 1;
     for (unsigned b = threadIdx.x; b < gridDim.x; b += kDecThreads)
       __hip_atomic_store(a.flags + (size_t)b * 16, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
       __hip_atomic_store(a.barrier, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.epoch, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    return true;
   }
+}
+
+// The wait half of the barrier (the last arriver does not wait).
+__device__ bool barrier_wait(const DecodeArgs& a, DecodeSmem& sm) {
+  if (sm.last) return true;
+  const unsigned long long target = sm.epoch + 1;
   if (threadIdx.x == 0) {
     const unsigned long long* f = a.flags + (size_t)blockIdx.x * 16;
     int n = 0;
@@ -515,10 +521,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a) {
   const int j0 = a.T == 1 ? (int)blockIdx.x * kDecWaves + wave : wave * (int)gridDim.x + (int)blockIdx.x;
   if (MODE != 1) phase1_issue<CHG, X>(a, sm, j0, p1);
   DownRows<CHD, Q8> d;
-  if (MODE != 0) down_load<CHD, Q8, X>(a, sm, 0, row, l8, d);  // in flight during phase 1 and the wait
+  if (MODE == 1) down_load<CHD, Q8, X>(a, sm, 0, row, l8, d);
   if (MODE != 1) phase1<CHG, X>(a, sm, p1);
   if (MODE == 0) return;
-  if (MODE == 2 && !grid_barrier(a, sm)) {
+  // The fused form issues its first down-weight loads once it has arrived at the grid
+  // barrier: they then overlap the wait instead of sharing the memory system with the
+  // gate/up loads of phase 1.
+  if (MODE == 2) barrier_arrive(a, sm);
+  if (MODE == 2) down_load<CHD, Q8, X>(a, sm, 0, row, l8, d);
+  if (MODE == 2 && !barrier_wait(a, sm)) {
     // the wait gave up: this block's output rows are written as NaN, never left stale
     if (tid < kRowsPerBlock * a.T) {
       const int r = blockIdx.x * kRowsPerBlock + (tid & 7), t = tid >> 3;
