@@ -461,8 +461,8 @@ __device__ __forceinline__ void down_accum(const DecodeArgs& a, const DecodeSmem
 // stores epoch + 1 as the next call's epoch. A block waits until its flag reaches
 // epoch + 1. So every call starts with a zero counter whatever the previous call's grid
 // size was, and stale flags (at most the previous epoch) never release a wait. Readers
-// then load h with agent-coherent loads. Returns false (and sets bit 0 of hdr[1]) if the
-// wait exceeds the spin limit, so every wave exits.
+// then load h with agent-coherent loads. The arrival and the wait are two calls, so a block
+// can issue loads in between.
 __device__ void barrier_arrive(const DecodeArgs& a, DecodeSmem& sm) {
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
@@ -483,7 +483,8 @@ __device__ void barrier_arrive(const DecodeArgs& a, DecodeSmem& sm) {
   }
 }
 
-// The wait half of the barrier (the last arriver does not wait).
+// The wait half of the barrier (the last arriver does not wait). Returns false (and sets
+// bit 0 of hdr[1]) if the wait exceeds the spin limit, so every wave exits.
 __device__ bool barrier_wait(const DecodeArgs& a, DecodeSmem& sm) {
   if (sm.last) return true;
   const unsigned long long target = sm.epoch + 1;
