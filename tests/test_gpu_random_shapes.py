@@ -1,0 +1,84 @@
+"""Seeded random shapes within the documented limits, against the float64 oracle: the
+prefill (bf16 activations, every launch variant the shape selects: 8 or 4 waves, scale
+groups of 4 or 2 K-blocks) and the decode (one or two launches, every chunk-count variant up
+to H = 2048, I = 1024), with Zipf routing plus duplicate and dropped ids. Each case prints
+its shape and error, so a failure names the case."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_quantized_moe_02_amd as nv
+import oracle as O
+import workloads as W
+from gpu_util import DEV, TOL, bf16_dev, bf16_out_to_f64, layer_dev, max_row_rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _routing(rng, seed, T, E, k):
+    """Zipf routing over E experts (k <= E distinct per token), then a few duplicates and
+    ids outside [0, E), which the method drops."""
+    kk = min(k, E)
+    ids = np.full((T, k), -1, dtype=np.int32)
+    ids[:, :kk] = W.draw_routing_zipf(seed, T, E, kk)
+    for t in range(T):
+        if kk < k:
+            ids[t, kk:] = ids[t, 0]               # duplicates fill the slots past E
+        if rng.random() < 0.05:
+            ids[t, int(rng.integers(0, k))] = int(rng.choice([-1, E, E + 7]))
+    w = rng.random((T, k)).astype(np.float32)
+    return ids, w
+
+
+def _prefill_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    H = int(rng.choice([256, 512, 768, 1024]))
+    I = 128 * int(rng.integers(1, 7))            # 128 .. 768
+    E = int(rng.integers(1, 40))
+    k = int(rng.integers(1, 9))
+    T = int(rng.integers(1, 420))
+    return rng, H, I, E, k, T
+
+
+def _decode_case(seed):
+    rng = np.random.default_rng(9000 + seed)
+    H = 32 * int(rng.integers(1, 65))            # 32 .. 2048
+    I = 32 * int(rng.integers(1, 33))            # 32 .. 1024
+    E = int(rng.integers(1, 80))
+    T = int(rng.integers(1, 9))
+    k = int(rng.integers(1, min(8, 64 // T) + 1))
+    return rng, H, I, E, k, T
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_shape(seed):
+    rng, H, I, E, k, T = _prefill_case(seed)
+    print(f"prefill seed={seed} T={T} E={E} H={H} I={I} k={k}", flush=True)
+    lay = W.draw_layer(500 + seed, E=E, H=H, I=I)
+    xb = W.draw_activations(500 + seed, T, H)
+    ids, w = _routing(rng, 500 + seed, T, E, k)
+    ref = O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w)
+    dl = layer_dev(lay)
+    x, ti, tw = bf16_dev(xb), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    y32 = nv.moe_prefill(x, dl, ti, tw, out_dtype=torch.float32)
+    yb = nv.moe_prefill(x, dl, ti, tw, out_dtype=torch.bfloat16)
+    e32 = max_row_rel_l2(y32.cpu().numpy().astype(np.float64), ref)
+    eb = max_row_rel_l2(bf16_out_to_f64(yb), ref)
+    print(f"   max row rel L2: fp32 out {e32:.3e}, bf16 out {eb:.3e}")
+    assert e32 < 1e-3  # the fp16 h rounding alone
+    assert eb < TOL
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random_shape(seed):
+    rng, H, I, E, k, T = _decode_case(seed)
+    print(f"decode seed={seed} T={T} E={E} H={H} I={I} k={k}", flush=True)
+    lay = W.draw_layer(600 + seed, E=E, H=H, I=I)
+    xb = W.draw_activations(600 + seed, T, H)
+    ids, w = _routing(rng, 600 + seed, T, E, k)
+    ref = O.moe_grouped(O.bf16_to_f64(xb), lay, ids, w)
+    dl = layer_dev(lay)
+    y = nv.moe_decode(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+    err = max_row_rel_l2(y.cpu().numpy().astype(np.float64), ref)
+    print(f"   max row rel L2 {err:.3e}")
+    assert err < 1e-5  # FP32 arithmetic throughout
