@@ -82,3 +82,27 @@ def test_decode_random_shape(seed):
     err = max_row_rel_l2(y.cpu().numpy().astype(np.float64), ref)
     print(f"   max row rel L2 {err:.3e}")
     assert err < 1e-5  # FP32 arithmetic throughout
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("act", ["w4a8_f16", "w4a8", "w4a4"])
+def test_quantized_prefill_random_shape(act, seed):
+    """The W4A8 (fp16 and int8 matrix cores) and W4A4 paths on random shapes, with their
+    strict checks (the staged activation codes bit-exact, h, the requantized codes and the
+    oracle's down step on the GPU's codes) on every token row; distinct experts per token."""
+    from gpu_util import w4a4_strict, w4a8_strict
+    rng, H, I, E, k, T = _prefill_case(20 + seed)
+    k = min(k, E)
+    print(f"{act} seed={seed} T={T} E={E} H={H} I={I} k={k}", flush=True)
+    lay = W.draw_layer(700 + seed, E=E, H=H, I=I)
+    xb = W.draw_activations(700 + seed, T, H, outlier_frac=0.001)
+    ids = W.draw_routing_zipf(700 + seed, T, E, k)
+    w = W.draw_router_weights(700 + seed, T, k)
+    dl = layer_dev(lay)
+    ws = torch.zeros(nv.prefill_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device=DEV)
+    y = nv.moe_prefill(bf16_dev(xb), dl, torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), act=act,
+                       out_dtype=torch.float32, ws=ws)
+    got = y.cpu().numpy().astype(np.float64)
+    strict = w4a4_strict if act == "w4a4" else w4a8_strict
+    stats = strict(xb, lay, ids, w, np.arange(T), ws, got, act=act)
+    print(f"   {stats}")
