@@ -106,3 +106,36 @@ def test_quantized_prefill_random_shape(act, seed):
     strict = w4a4_strict if act == "w4a4" else w4a8_strict
     stats = strict(xb, lay, ids, w, np.arange(T), ws, got, act=act)
     print(f"   {stats}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("variant", ["shared", "q8_down", "shared_q8_down"])
+def test_layer_variants_random_shape(variant, seed):
+    """The layer's shared expert and the Q8_0 down projection (and both), prefill and
+    decode, on random shapes against the oracle."""
+    down_fmt = "q8_0" if "q8" in variant else "nvfp4"
+    with_shared = variant.startswith("shared")
+    rng, H, I, E, k, T = _prefill_case(40 + seed)
+    _, Hd, Id, Ed, kd, Td = _decode_case(40 + seed)
+    kd = min(kd, 64 // Td - 1) if with_shared else kd  # the shared slot counts as one more pair
+    print(f"{variant} seed={seed} prefill T={T} E={E} H={H} I={I} k={k}; decode T={Td} E={Ed} H={Hd} I={Id} "
+          f"k={kd}", flush=True)
+    for (tt, ee, hh, ii, kk, base) in ((T, E, H, I, k, 800), (Td, Ed, Hd, Id, kd, 900)):
+        s = base + seed
+        lay = W.draw_layer(s, E=ee, H=hh, I=ii, down_fmt=down_fmt)
+        sh = W.draw_shared_expert(s, H=hh, I=ii, down_fmt=down_fmt) if with_shared else None
+        xb = W.draw_activations(s, tt, hh)
+        ids, w = _routing(np.random.default_rng(s), s, tt, ee, kk)
+        x64 = O.bf16_to_f64(xb)
+        ref = O.moe_with_shared(x64, lay, sh, ids, w) if with_shared else O.moe_grouped(x64, lay, ids, w)
+        args = (bf16_dev(xb), layer_dev(lay), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV))
+        shd = layer_dev(sh) if with_shared else None
+        if base == 800:
+            y = nv.moe_prefill(*args, out_dtype=torch.float32, shared=shd)
+            bound = 1e-3  # the fp16 h (and a Q8_0 weight's one fp16 rounding)
+        else:
+            y = nv.moe_decode(*args, shared=shd)
+            bound = 1e-5
+        err = max_row_rel_l2(y.cpu().numpy().astype(np.float64), ref)
+        print(f"   {'prefill' if base == 800 else 'decode'}: max row rel L2 {err:.3e}")
+        assert err < bound
