@@ -1,8 +1,9 @@
 """Seeded random shapes within the documented limits, against the float64 oracle: the
 prefill (bf16 activations, every launch variant the shape selects: 8 or 4 waves, scale
 groups of 4 or 2 K-blocks) and the decode (one or two launches, every chunk-count variant up
-to H = 2048, I = 1024), with Zipf routing plus duplicate and dropped ids. Each case prints
-its shape and error, so a failure names the case."""
+to H = 2048, I = 1024), with Zipf routing plus duplicate and dropped ids; the W4A8 and W4A4
+paths, the shared expert, the Q8_0 down projection and the router the same way. Each case
+prints its shape and error, so a failure names the case."""
 import numpy as np
 import pytest
 import torch
@@ -139,3 +140,27 @@ def test_layer_variants_random_shape(variant, seed):
         err = max_row_rel_l2(y.cpu().numpy().astype(np.float64), ref)
         print(f"   {'prefill' if base == 800 else 'decode'}: max row rel L2 {err:.3e}")
         assert err < bound
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_router_random_shape(seed):
+    """The router (logits, top-k, softmax) on random shapes within its limits (H a multiple
+    of 64, E a multiple of 32 up to 2048, k up to 64), bf16 and fp32 activations, with the
+    checks of the router tests (logits within the fp32 accumulation bound, the selection and
+    weights exact from those logits, the ids against the oracle's away from near-ties)."""
+    from test_gpu_router import _run
+    rng = np.random.default_rng(11000 + seed)
+    H = 64 * int(rng.integers(1, 33))
+    E = 32 * int(rng.integers(1, 65))
+    k = int(rng.integers(1, min(64, E) + 1))
+    T = int(rng.integers(1, 600))
+    fp32 = bool(seed % 2)
+    print(f"router seed={seed} T={T} E={E} H={H} k={k} x {'fp32' if fp32 else 'bf16'}", flush=True)
+    wr = W.draw_router(1100 + seed, E=E, H=H)
+    if fp32:
+        x = (rng.standard_normal((T, H)) * np.exp(rng.uniform(-2, 2, (T, 1)))).astype(np.float32)
+        ntie = _run(torch.from_numpy(x).to(DEV), x.astype(np.float64), wr, k)
+    else:
+        xb = W.draw_activations(1100 + seed, T, H)
+        ntie = _run(bf16_dev(xb), O.bf16_to_f64(xb), wr, k)
+    print(f"   {ntie} tokens with a near-tie at the k-th expert")
